@@ -1,0 +1,313 @@
+"""Bench: achieved HBM GB/s of the block-quantised products on one MI355X.
+
+`value` is the decode-FFN step of a 27B-like layer at batch 1 (fused gate/up
+Q4_0 5120 -> 2 x 17408 with SiLU, then down Q4_0 17408 -> 5120 accumulated
+into the residual): algorithmic bytes per step x steps / time.  The other
+workloads (decode GEMV 2048 x 2048, verify GEMVs at 4 and 8 columns, the
+16-column prefill GEMMs, the LM head + argmax, the MoE FFN at 1 and 16
+tokens) are timed the same way and reported under "kernels".
+
+Inputs are seeded synthetic tensors at the pages' model shapes, resident in
+HBM before timing.  Every timed loop cycles a pool of byte-identical,
+address-distinct weight copies of >= 1 GiB (larger than the 256 MB
+Infinity Cache), is captured in a HIP graph (no host launch gaps) and is
+timed with events on the stream the kernels run on.
+
+Algorithmic bytes: packed weights (qs + f16 scales) + activations read +
+outputs written (+ outputs read when accumulating) + router weights.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+POOL_BYTES = 1 << 30
+
+
+def qbytes(qtype, rows, cols):
+    return rows * cols // 32 * (18 if qtype == 2 else 34)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Bench:
+    def __init__(self, torch, qg, dev):
+        self.torch, self.qg, self.dev = torch, qg, dev
+
+    def up(self, a):
+        return self.torch.from_numpy(np.ascontiguousarray(a)).to(self.dev)
+
+    def matrix(self, qtype, rows, cols, seed, sigma):
+        raw = __import__("synth").gen_weights(qtype, rows, cols, sigma, np.random.default_rng(seed))
+        return self.qg.qg_repack(qtype, self.up(raw.reshape(-1)), rows, cols), raw
+
+    def pool(self, w, per_copy_bytes):
+        """Byte-identical, address-distinct copies totalling >= 1 GiB."""
+        n = max(2, -(-POOL_BYTES // per_copy_bytes))
+        out = [w]
+        for _ in range(n - 1):
+            out.append(self.qg.QMatrix(w.qtype, w.rows, w.cols, w.n_mat, w.qs.clone(), w.d.clone()))
+        return out
+
+    def graph_time(self, fns, iters):
+        """Capture `iters` calls (cycling fns) in one HIP graph; return the
+        mean time per call in seconds over one timed replay."""
+        torch = self.torch
+        for f in fns[:2]:
+            f()                                   # eager warm-up (workspaces, code objects)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(iters):
+                    fns[i % len(fns)]()
+        torch.cuda.current_stream().wait_stream(s)
+        g.replay()                                # warm replay
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / iters, g
+
+
+def kernel_entry(bytes_per_call, t, extra=None):
+    gbs = bytes_per_call / t / 1e9
+    d = {"us": round(t * 1e6, 3), "bytes": int(bytes_per_call), "GB_s": round(gbs, 1),
+         "frac_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    if extra:
+        d.update(extra)
+    return d
+
+
+def run_ffn(B, steps, warmup):
+    """The decode-FFN step: returns (bytes/step, step time, gate/up time, down time)."""
+    torch, qg = B.torch, B.qg
+    Q4 = qg.Q4_0
+    N, K = 17408, 5120
+    wg, graw = B.matrix(Q4, N, K, seed=21, sigma=0.02)
+    wu, uraw = B.matrix(Q4, N, K, seed=22, sigma=0.02)
+    wd, draw = B.matrix(Q4, K, N, seed=23, sigma=0.02)
+    set_bytes = 3 * qbytes(Q4, N, K)
+    n = max(2, -(-POOL_BYTES // set_bytes))
+    pg, pu, pd = B.pool(wg, set_bytes)[:n], B.pool(wu, set_bytes)[:n], B.pool(wd, set_bytes)[:n]
+    import synth
+    x = B.up(synth.gen_x(K, 1, cfg_id=2).T)
+    y = B.up(synth.rng(2, 90).standard_normal((1, K)).astype(np.float32))
+    h = torch.empty((1, N), dtype=torch.float32, device=B.dev)
+    gu_bytes = 2 * qbytes(Q4, N, K) + 4 * K + 4 * N
+    dn_bytes = qbytes(Q4, K, N) + 4 * N + 8 * K
+    step_bytes = gu_bytes + dn_bytes
+
+    def step(i):
+        qg.gateup_silu(pg[i], pu[i], x, h)
+        qg.qgemv(pd[i], h, y, accumulate=True)
+
+    steps_fns = [lambda i=i: step(i) for i in range(n)]
+    # W warm-up steps, then exactly K timed steps, barrier + sync on both sides
+    if warmup > 0:
+        _, gw = B.graph_time(steps_fns, warmup)
+    t_step, _ = B.graph_time(steps_fns, steps)
+    t_gu, _ = B.graph_time([lambda i=i: qg.gateup_silu(pg[i], pu[i], x, h) for i in range(n)], 4 * n)
+    t_dn, _ = B.graph_time([lambda i=i: qg.qgemv(pd[i], h, y, accumulate=True) for i in range(n)], 4 * n)
+    raws = (graw, uraw, draw)
+    del pg, pu, pd
+    return step_bytes, t_step, gu_bytes, t_gu, dn_bytes, t_dn, raws
+
+
+def run_extras(B, kernels):
+    torch, qg = B.torch, B.qg
+    import synth
+    Q4, Q8 = qg.Q4_0, qg.Q8_0
+
+    # decode GEMV, 2048 x 2048 Q4_0 (a parity-size matrix; launch-bound)
+    w, _ = B.matrix(Q4, 2048, 2048, seed=11, sigma=0.02)
+    p = B.pool(w, qbytes(Q4, 2048, 2048))
+    x = B.up(synth.gen_x(2048, 1, cfg_id=1).T)
+    y = torch.empty((1, 2048), device=B.dev)
+    t, _ = B.graph_time([lambda m=m: qg.qgemv(m, x, y) for m in p], 2 * len(p))
+    kernels["gemv_q4_0_2048x2048_1col"] = kernel_entry(qbytes(Q4, 2048, 2048) + 8192 * 2, t)
+    del p
+    log("  gemv 2048 done")
+
+    # verify GEMVs at 4 and 8 columns
+    for qtype, N, K, name in ((Q8, 5120, 5120, "q8_0_5120x5120"), (Q4, 17408, 5120, "q4_0_5120to17408")):
+        w, _ = B.matrix(qtype, N, K, seed=31, sigma=0.005 if qtype == Q8 else 0.02)
+        p = B.pool(w, qbytes(qtype, N, K))
+        for nc in (4, 8):
+            x = B.up(synth.gen_x(K, nc, cfg_id=3).T)
+            y = torch.empty((nc, N), device=B.dev)
+            t, _ = B.graph_time([lambda m=m: qg.qgemv(m, x, y) for m in p], 2 * len(p))
+            kernels[f"verify_{name}_{nc}col"] = kernel_entry(qbytes(qtype, N, K) + 4 * nc * (N + K), t,
+                                                             {"tokens_per_s": round(nc / t, 1)})
+        del p
+    log("  verify done")
+
+    # 16-column prefill GEMMs
+    for qtype in (Q4, Q8):
+        for N, K in ((17408, 5120), (5120, 17408)):
+            w, _ = B.matrix(qtype, N, K, seed=41, sigma=0.005 if qtype == Q8 else 0.02)
+            p = B.pool(w, qbytes(qtype, N, K))
+            x = B.up(synth.gen_x(K, 16, cfg_id=4).T)
+            y = torch.empty((16, N), device=B.dev)
+            t, _ = B.graph_time([lambda m=m: qg.qgemm16(m, x, y) for m in p], 2 * len(p))
+            nm = f"gemm16_{'q4_0' if qtype == Q4 else 'q8_0'}_{K}to{N}"
+            kernels[nm] = kernel_entry(qbytes(qtype, N, K) + 64 * (N + K), t,
+                                       {"tokens_per_s": round(16 / t, 1)})
+            del p
+    log("  gemm16 done")
+
+    # LM head + argmax, Q8_0 248,320 x 5120
+    N, K = 248320, 5120
+    w, _ = B.matrix(Q8, N, K, seed=51, sigma=0.005)
+    p = [w, qg.QMatrix(w.qtype, w.rows, w.cols, 1, w.qs.clone(), w.d.clone())]
+    x = B.up(synth.gen_x(K, 1, cfg_id=4)[:, 0])
+    oi = torch.empty(1, dtype=torch.int32, device=B.dev)
+    ov = torch.empty(1, dtype=torch.float32, device=B.dev)
+    t, _ = B.graph_time([lambda m=m: qg.lmhead_argmax(m, x, None, oi, ov) for m in p], 20)
+    kernels["lmhead_argmax_q8_0_5120to248320"] = kernel_entry(qbytes(Q8, N, K) + 4 * K + 8, t)
+    del p, w
+    log("  lmhead done")
+
+    # MoE FFN, 256 experts (8 active) + shared, hidden 2048, ffn 512
+    E, H, F, k = 256, 2048, 512, 8
+    g = np.random.default_rng(61)
+    def stack(rows, cols):
+        raw = np.stack([synth.gen_weights(Q4, rows, cols, 0.02, g) for _ in range(E)])
+        return qg.qg_repack(Q4, B.up(raw.reshape(-1)), rows, cols, E)
+    gate, upm, down = stack(F, H), stack(F, H), stack(H, F)
+    sh = [B.matrix(Q4, r, c, seed=62 + i, sigma=0.02)[0] for i, (r, c) in enumerate(((F, H), (F, H), (H, F)))]
+    router = B.up(synth.gen_f32((E, H), 0.02, g))
+    layer_bytes = 3 * E * qbytes(Q4, F, H)
+    copies = max(2, -(-POOL_BYTES // layer_bytes))
+    cl = lambda m: qg.QMatrix(m.qtype, m.rows, m.cols, m.n_mat, m.qs.clone(), m.d.clone())
+    moes = []
+    for c in range(copies):
+        gg, uu, dd = (gate, upm, down) if c == 0 else (cl(gate), cl(upm), cl(down))
+        moes.append(qg.MoE(hidden=H, ffn=F, n_expert=E, top_k=k, router=router, gate=gg, up=uu,
+                           down=dd, sh_gate=sh[0], sh_up=sh[1], sh_down=sh[2]))
+    eb = qbytes(Q4, F, H) * 3
+    for T in (1, 16):
+        X = B.up(synth.gen_x(H, T, cfg_id=5).T)
+        Y = torch.zeros((T, H), device=B.dev)
+        tidx = torch.empty((T, k), dtype=torch.int32, device=B.dev)
+        qg.moe_ffn(moes[0], X, Y, tidx)
+        torch.cuda.synchronize()
+        U = len(np.unique(tidx.cpu().numpy()))
+        nbytes = 4 * E * H + eb * (U + 1) + 4 * H * T + 8 * H * T
+        t, _ = B.graph_time([lambda m=m: qg.moe_ffn(m, X, Y) for m in moes], 4 * copies)
+        kernels[f"moe_ffn_{T}tok"] = kernel_entry(nbytes, t, {"distinct_experts": U,
+                                                             "tokens_per_s": round(T / t, 1)})
+    del moes, gate, upm, down
+    log("  moe done")
+
+
+def read_ceiling(B):
+    """Plain device copy of 1 GiB (read + write) timed the same way."""
+    torch = B.torch
+    a = torch.empty(POOL_BYTES // 4, dtype=torch.float32, device=B.dev).normal_()
+    b = torch.empty_like(a)
+    t, _ = B.graph_time([lambda: b.copy_(a)], 10)
+    return 2 * POOL_BYTES / t / 1e9
+
+
+def cpu_baseline(raws):
+    """The oracle, as it stands, on one full decode-FFN step (2 repetitions)."""
+    import synth
+    from oracle import ops
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        threads = 1
+    graw, uraw, draw = raws
+    x = synth.gen_x(5120, 1, cfg_id=2)[:, 0]
+    y_in = synth.rng(2, 90).standard_normal(5120).astype(np.float32)
+    reps = 2
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        h, _, _, _ = ops.gateup_silu(2, graw, uraw, x)
+        ops.gemv(2, draw, h.astype(np.float32), y_in=y_in)
+    dt = (time.perf_counter() - t0) / reps
+    nbytes = 3 * qbytes(2, 17408, 5120) + 4 * 5120 + 4 * 17408 + 4 * 17408 + 8 * 5120
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"one full decode-FFN step (gate/up 17408x5120 + down 5120x17408, Q4_0, batch 1), "
+                      f"{reps} repetitions, {dt:.2f} s per step; f64 numpy, BLAS threads={threads}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--suite", choices=["all", "main"], default="all")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gemm_q4_q8_amd as qg
+    dev = torch.device("cuda:0")
+    B = Bench(torch, qg, dev)
+
+    log("bench: decode FFN step")
+    step_bytes, t_step, gu_bytes, t_gu, dn_bytes, t_dn, raws = run_ffn(B, args.steps, args.warmup)
+    value = step_bytes / t_step / 1e9
+    kernels = {
+        "gateup_silu_q4_0_5120to2x17408": kernel_entry(gu_bytes, t_gu),
+        "qgemv_q4_0_17408to5120_acc": kernel_entry(dn_bytes, t_dn),
+    }
+    ceiling = read_ceiling(B)
+    if args.suite == "all":
+        log("bench: other workloads")
+        run_extras(B, kernels)
+    achieved = gu_bytes / t_gu / 1e9
+    out = {
+        "metric": "Q4_0/Q8_0 GEMV+GEMM achieved HBM GB/s and % of MI355X peak",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q4_0 weights, f16 activation operands, f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": "27B-like decode FFN layer, batch 1: gate/up Q4_0 5120->2x17408 + SiLU, "
+                               "down Q4_0 17408->5120 y+=W.h",
+                   "bytes_per_step": int(step_bytes), "tokens_per_s": round(1.0 / t_step, 1),
+                   "frac_peak": round(value / PEAK_HBM_GBS, 4),
+                   "copy_ceiling_GB_s": round(ceiling, 1)},
+        "roofline": {"bound": "hbm", "kernel": "gateup_silu (Q4_0, 1 column)",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+        "kernels": kernels,
+    }
+    if not args.no_cpu:
+        log("bench: cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(raws)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

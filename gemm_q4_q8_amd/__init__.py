@@ -1,0 +1,281 @@
+"""Python binding of libqgemm (block-quantised Q4_0 / Q8_0 products, gfx950).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream.  The functions carry
+the C-ABI names declared in include/qgemm.h; `lib` is the raw ctypes handle.
+
+Importing fails loudly when the built library is missing: there is no
+fallback.  Build it with `python -m gemm_q4_q8_amd.build`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqgemm.so")
+
+Q4_0 = 2
+Q8_0 = 8
+BLOCK_BYTES = {Q4_0: 18, Q8_0: 34}
+STATUS = {0: "QG_OK", -1: "QG_EINVAL", -2: "QG_ESHAPE", -3: "QG_EALIGN",
+          -4: "QG_EUNSUPPORTED", -5: "QG_EWORKSPACE", -6: "QG_EHIP"}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built (python -m gemm_q4_q8_amd.build)")
+lib = ctypes.CDLL(LIB_PATH)
+
+_i32, _i64, _sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+
+
+class qg_moe(ctypes.Structure):
+    _fields_ = [
+        ("hidden", _i64), ("ffn", _i64),
+        ("n_expert", _i32), ("top_k", _i32), ("normalize_topk", _i32),
+        ("qtype", _i32),
+        ("router", _vp),
+        ("gate_qs", _vp), ("up_qs", _vp), ("down_qs", _vp),
+        ("gate_d", _vp), ("up_d", _vp), ("down_d", _vp),
+        ("sh_ffn", _i64),
+        ("sh_gate_qs", _vp), ("sh_up_qs", _vp), ("sh_down_qs", _vp),
+        ("sh_gate_d", _vp), ("sh_up_d", _vp), ("sh_down_d", _vp),
+    ]
+
+
+_SIGS = {
+    "qg_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "qg_packed_bytes": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64,
+                                       ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
+    "qg_repack": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "qg_gemv_ws_bytes": (_sz, [_i64, _i64]),
+    "qgemv_q4_0": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _i64, _i32, _vp, _i64, _i32,
+                                  _vp, _sz, _vp]),
+    "qgemv_q8_0": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _i64, _i32, _vp, _i64, _i32,
+                                  _vp, _sz, _vp]),
+    "qg_gemm16_ws_bytes": (_sz, [ctypes.c_int, _i64, _i64]),
+    "qgemm16": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i32,
+                               _vp, _sz, _vp]),
+    "qg_gateup_ws_bytes": (_sz, [_i64, _i64]),
+    "gateup_silu": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _i32,
+                                   _vp, _i64, _vp, _sz, _vp]),
+    "qg_lmhead_ws_bytes": (_sz, [_i64, _i64]),
+    "lmhead_argmax": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp,
+                                     _vp, _sz, _vp]),
+    "qg_moe_ws_bytes": (_sz, [ctypes.POINTER(qg_moe), _i32]),
+    "moe_ffn": (ctypes.c_int, [ctypes.POINTER(qg_moe), _vp, _i64, _i32, _vp, _i64, _vp, _vp,
+                               _vp, _sz, _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+class QGError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({lib.qg_strerror(status).decode()})")
+        self.status = status
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise QGError(status, what)
+
+
+# ---------------------------------------------------------------- torch glue
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+_WS = {}
+
+
+def workspace(nbytes: int, device, key: str = "default"):
+    """A zero-filled device workspace (cached per device and key).  The
+    library leaves it zero-filled after every completed call."""
+    torch = _torch()
+    dev = torch.device(device)
+    k = (dev.index, key)
+    ws = _WS.get(k)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
+        _WS[k] = ws
+    return ws
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+@dataclass
+class QMatrix:
+    """A repacked matrix (or a stack of n_mat matrices) on the GPU."""
+    qtype: int
+    rows: int
+    cols: int
+    n_mat: int
+    qs: object
+    d: object
+
+
+def packed_bytes(qtype: int, rows: int, cols: int, n_mat: int = 1):
+    qb, db = _sz(), _sz()
+    _check(lib.qg_packed_bytes(qtype, n_mat, rows, cols, ctypes.byref(qb), ctypes.byref(db)),
+           "qg_packed_bytes")
+    return qb.value, db.value
+
+
+def qg_repack(qtype: int, blocks, rows: int, cols: int, n_mat: int = 1) -> QMatrix:
+    """blocks: uint8 tensor on the GPU holding n_mat*rows*cols/32 GGUF blocks."""
+    torch = _torch()
+    _check_dev(blocks)
+    qb, db = packed_bytes(qtype, rows, cols, n_mat)
+    qs = torch.empty(qb, dtype=torch.uint8, device=blocks.device)
+    d = torch.empty(db, dtype=torch.uint8, device=blocks.device)
+    _check(lib.qg_repack(qtype, n_mat, rows, cols, blocks.data_ptr(), qs.data_ptr(),
+                         d.data_ptr(), _stream(blocks.device)), "qg_repack")
+    return QMatrix(qtype, rows, cols, n_mat, qs, d)
+
+
+def _ld(t) -> int:
+    """Leading dimension of a column-major [len, ncols] matrix stored as a
+    row-major torch tensor of shape [ncols, len] (column j = t[j])."""
+    return t.stride(0) if t.dim() == 2 else t.shape[-1]
+
+
+def qgemv(w: QMatrix, X, Y=None, accumulate: bool = False):
+    """Y[j] = (acc ? Y[j] : 0) + W X[j]; X: [ncols, cols] f32 (ncols 1..8)."""
+    torch = _torch()
+    _check_dev(X)
+    X2 = X if X.dim() == 2 else X.view(1, -1)
+    ncols = X2.shape[0]
+    if Y is None:
+        Y = torch.empty((ncols, w.rows), dtype=torch.float32, device=X.device)
+    Y2 = Y if Y.dim() == 2 else Y.view(1, -1)
+    ws_b = lib.qg_gemv_ws_bytes(w.rows, w.cols)
+    ws = workspace(ws_b, X.device)
+    fn = lib.qgemv_q4_0 if w.qtype == Q4_0 else lib.qgemv_q8_0
+    _check(fn(w.qs.data_ptr(), w.d.data_ptr(), w.rows, w.cols, X2.data_ptr(), _ld(X2), ncols,
+              Y2.data_ptr(), _ld(Y2), int(accumulate), ws.data_ptr(), ws.numel(),
+              _stream(X.device)), "qgemv")
+    return Y
+
+
+def qgemv_q4_0(w: QMatrix, X, Y=None, accumulate: bool = False):
+    assert w.qtype == Q4_0
+    return qgemv(w, X, Y, accumulate)
+
+
+def qgemv_q8_0(w: QMatrix, X, Y=None, accumulate: bool = False):
+    assert w.qtype == Q8_0
+    return qgemv(w, X, Y, accumulate)
+
+
+def qgemm16(w: QMatrix, X, Y=None, accumulate: bool = False):
+    """Y = (acc ? Y : 0) + W X; X: [16, cols] f32, Y: [16, rows]."""
+    torch = _torch()
+    _check_dev(X)
+    if X.shape[0] != 16:
+        raise ValueError("qgemm16 takes exactly 16 columns")
+    if Y is None:
+        Y = torch.empty((16, w.rows), dtype=torch.float32, device=X.device)
+    ws_b = lib.qg_gemm16_ws_bytes(w.qtype, w.rows, w.cols)
+    ws = workspace(ws_b, X.device)
+    _check(lib.qgemm16(w.qtype, w.qs.data_ptr(), w.d.data_ptr(), w.rows, w.cols, X.data_ptr(),
+                       _ld(X), Y.data_ptr(), _ld(Y), int(accumulate), ws.data_ptr(), ws.numel(),
+                       _stream(X.device)), "qgemm16")
+    return Y
+
+
+def gateup_silu(wg: QMatrix, wu: QMatrix, X, H=None):
+    """H[j] = silu(Wg X[j]) * (Wu X[j]); X: [ncols, cols] (ncols 1..8)."""
+    torch = _torch()
+    _check_dev(X)
+    X2 = X if X.dim() == 2 else X.view(1, -1)
+    ncols = X2.shape[0]
+    if H is None:
+        H = torch.empty((ncols, wg.rows), dtype=torch.float32, device=X.device)
+    H2 = H if H.dim() == 2 else H.view(1, -1)
+    ws = workspace(lib.qg_gateup_ws_bytes(wg.rows, wg.cols), X.device)
+    _check(lib.gateup_silu(wg.qtype, wg.qs.data_ptr(), wg.d.data_ptr(), wu.qs.data_ptr(),
+                           wu.d.data_ptr(), wg.rows, wg.cols, X2.data_ptr(), _ld(X2), ncols,
+                           H2.data_ptr(), _ld(H2), ws.data_ptr(), ws.numel(),
+                           _stream(X.device)), "gateup_silu")
+    return H
+
+
+def lmhead_argmax(w: QMatrix, x, n_rows: Optional[int] = None, out_idx=None, out_val=None):
+    """Returns (idx int32 [1], val f32 [1]) on the GPU (no host sync)."""
+    torch = _torch()
+    _check_dev(x)
+    if out_idx is None:
+        out_idx = torch.empty(1, dtype=torch.int32, device=x.device)
+    if out_val is None:
+        out_val = torch.empty(1, dtype=torch.float32, device=x.device)
+    ws = workspace(lib.qg_lmhead_ws_bytes(w.rows, w.cols), x.device, "lmhead")
+    _check(lib.lmhead_argmax(w.qtype, w.qs.data_ptr(), w.d.data_ptr(), w.rows, w.cols,
+                             w.rows if n_rows is None else n_rows, x.data_ptr(),
+                             out_idx.data_ptr(), out_val.data_ptr(), ws.data_ptr(), ws.numel(),
+                             _stream(x.device)), "lmhead_argmax")
+    return out_idx, out_val
+
+
+@dataclass
+class MoE:
+    """Role-stacked experts (gate / up / down stacks) plus optional shared expert."""
+    hidden: int
+    ffn: int
+    n_expert: int
+    top_k: int
+    router: object            # f32 [n_expert, hidden]
+    gate: QMatrix             # n_mat = n_expert, ffn x hidden
+    up: QMatrix
+    down: QMatrix             # n_mat = n_expert, hidden x ffn
+    sh_gate: Optional[QMatrix] = None
+    sh_up: Optional[QMatrix] = None
+    sh_down: Optional[QMatrix] = None
+    normalize_topk: bool = True
+
+    def struct(self) -> qg_moe:
+        s = qg_moe()
+        s.hidden, s.ffn = self.hidden, self.ffn
+        s.n_expert, s.top_k, s.normalize_topk = self.n_expert, self.top_k, int(self.normalize_topk)
+        s.qtype = self.gate.qtype
+        s.router = self.router.data_ptr()
+        s.gate_qs, s.up_qs, s.down_qs = (m.qs.data_ptr() for m in (self.gate, self.up, self.down))
+        s.gate_d, s.up_d, s.down_d = (m.d.data_ptr() for m in (self.gate, self.up, self.down))
+        if self.sh_gate is not None:
+            s.sh_ffn = self.sh_gate.rows
+            s.sh_gate_qs, s.sh_up_qs, s.sh_down_qs = (
+                m.qs.data_ptr() for m in (self.sh_gate, self.sh_up, self.sh_down))
+            s.sh_gate_d, s.sh_up_d, s.sh_down_d = (
+                m.d.data_ptr() for m in (self.sh_gate, self.sh_up, self.sh_down))
+        else:
+            s.sh_ffn = 0
+        return s
+
+
+def moe_ffn(moe: MoE, X, Y, topk_idx=None, topk_w=None):
+    """Y[t] += MoE(X[t]) for the ntok = X.shape[0] tokens (<= 16)."""
+    _check_dev(X, Y)
+    s = moe.struct()
+    ntok = X.shape[0]
+    ws = workspace(lib.qg_moe_ws_bytes(ctypes.byref(s), ntok), X.device, "moe")
+    _check(lib.moe_ffn(ctypes.byref(s), X.data_ptr(), _ld(X), ntok, Y.data_ptr(), _ld(Y),
+                       _ptr(topk_idx), _ptr(topk_w), ws.data_ptr(), ws.numel(),
+                       _stream(X.device)), "moe_ffn")
+    return Y

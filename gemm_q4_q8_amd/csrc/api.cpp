@@ -1,0 +1,297 @@
+// C-ABI entry points of libqgemm: argument checks (host only, before any HIP
+// call) and dispatch to the kernel launchers.  What each call computes is
+// stated, with its sources, in include/qgemm.h.
+#include <string.h>
+
+#include "internal.h"
+#include "qgemm.h"
+
+using namespace qg;
+
+namespace {
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+bool qtype_ok(int q) { return q == QG_Q4_0 || q == QG_Q8_0; }
+
+// Byte range [lo, hi) of a column-major f32 matrix.
+struct Range {
+  uintptr_t lo, hi;
+};
+Range span(const float *p, int64_t ld, int64_t len, int64_t ncols) {
+  Range r;
+  r.lo = (uintptr_t)p;
+  r.hi = (uintptr_t)(p + (ncols - 1) * ld + len);
+  return r;
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int check_matrix(const void *qs, const void *d, int64_t rows, int64_t cols) {
+  if (!qs || !d) return QG_EINVAL;
+  if (rows <= 0 || cols <= 0 || cols % 32) return QG_ESHAPE;
+  if (rows > (int64_t)1 << 31 || cols > (int64_t)1 << 24) return QG_EUNSUPPORTED;
+  if (!aligned(qs, 16) || !aligned(d, 8)) return QG_EALIGN;
+  return QG_OK;
+}
+
+int check_act(const float *X, int64_t ldx, int64_t len, int ncols) {
+  if (!X) return QG_EINVAL;
+  if (ldx < len) return QG_ESHAPE;
+  if (!aligned(X, 16) || ldx % 4) return QG_EALIGN;
+  (void)ncols;
+  return QG_OK;
+}
+
+int check_out(const float *Y, int64_t ldy, int64_t len) {
+  if (!Y) return QG_EINVAL;
+  if (ldy < len) return QG_ESHAPE;
+  if (!aligned(Y, 4)) return QG_EALIGN;
+  return QG_OK;
+}
+
+int qmv_common(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols, const float *X,
+               int64_t ldx, int ncols, float *Y, int64_t ldy, int accumulate, void *ws, size_t ws_bytes,
+               void *stream, bool gemm16) {
+  if (!qtype_ok(qtype)) return QG_EINVAL;
+  int st = check_matrix(qs, d, rows, cols);
+  if (st) return st;
+  if (!gemm16 && (ncols < 1 || ncols > 8)) return QG_ESHAPE;
+  if ((st = check_act(X, ldx, cols, ncols))) return st;
+  if ((st = check_out(Y, ldy, rows))) return st;
+  if (overlap(span(X, ldx, cols, ncols), span(Y, ldy, rows, ncols))) return QG_EINVAL;
+  const int S = gemm16 ? gemm16_splits(rows, cols) : gemv_splits(rows, cols);
+  if (!ws) return QG_EWORKSPACE;
+  if (ws_bytes < qmv_ws_bytes(rows, cols, S, 1, gemm16 ? 16 : 8, false)) return QG_EWORKSPACE;
+  if (!aligned(ws, 256)) return QG_EALIGN;
+  QmvCall c;
+  memset(&c, 0, sizeof(c));
+  c.qtype = qtype;
+  c.nmat = 1;
+  c.qs[0] = c.qs[1] = qs;
+  c.d[0] = c.d[1] = d;
+  c.rows = rows;
+  c.cols = cols;
+  c.n_rows = rows;
+  c.X = X;
+  c.ldx = ldx;
+  c.ncols = ncols;
+  c.Y = Y;
+  c.ldy = ldy;
+  c.epi = accumulate ? EPI_ACC : EPI_STORE;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  c.stream = (hipStream_t)stream;
+  return launch_qmv(c);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qg_strerror(int status) {
+  switch (status) {
+    case QG_OK: return "ok";
+    case QG_EINVAL: return "invalid argument (null pointer, bad type id, or output overlapping input)";
+    case QG_ESHAPE: return "invalid shape (cols % 32, non-positive size, ncols, n_rows or top_k out of range)";
+    case QG_EALIGN: return "misaligned pointer or leading dimension";
+    case QG_EUNSUPPORTED: return "request outside what this build supports";
+    case QG_EWORKSPACE: return "workspace missing or too small";
+    case QG_EHIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+int qg_packed_bytes(int qtype, int64_t n_mat, int64_t rows, int64_t cols, size_t *qs_bytes,
+                    size_t *d_bytes) {
+  if (!qtype_ok(qtype) || !qs_bytes || !d_bytes) return QG_EINVAL;
+  if (n_mat <= 0 || rows <= 0 || cols <= 0 || cols % 32) return QG_ESHAPE;
+  const int64_t NT = (rows + 15) / 16, KT = (cols / 32 + 3) / 4;
+  const int64_t tiles = n_mat * NT * KT;
+  *qs_bytes = (size_t)tiles * (qtype == QG_Q4_0 ? 1024 : 2048);
+  *d_bytes = (size_t)tiles * 128;
+  return QG_OK;
+}
+
+int qg_repack(int qtype, int64_t n_mat, int64_t rows, int64_t cols, const void *blocks, void *qs,
+              void *d, void *stream) {
+  size_t qb, db;
+  int st = qg_packed_bytes(qtype, n_mat, rows, cols, &qb, &db);
+  if (st) return st;
+  if (!blocks || !qs || !d) return QG_EINVAL;
+  if (!aligned(blocks, 2) || !aligned(qs, 16) || !aligned(d, 8)) return QG_EALIGN;
+  const size_t in_bytes = (size_t)n_mat * rows * (cols / 32) * (qtype == QG_Q4_0 ? 18 : 34);
+  const Range in{(uintptr_t)blocks, (uintptr_t)blocks + in_bytes};
+  const Range oq{(uintptr_t)qs, (uintptr_t)qs + qb};
+  const Range od{(uintptr_t)d, (uintptr_t)d + db};
+  if (overlap(in, oq) || overlap(in, od) || overlap(oq, od)) return QG_EINVAL;
+  return launch_repack(qtype, n_mat, rows, cols, blocks, qs, d, (hipStream_t)stream);
+}
+
+size_t qg_gemv_ws_bytes(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0 || cols % 32) return 0;
+  return qmv_ws_bytes(rows, cols, gemv_splits(rows, cols), 1, 8, false);
+}
+
+size_t qg_gateup_ws_bytes(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0 || cols % 32) return 0;
+  return qmv_ws_bytes(rows, cols, gemv_splits(rows, cols), 2, 8, false);
+}
+
+size_t qg_gemm16_ws_bytes(int qtype, int64_t rows, int64_t cols) {
+  if (!qtype_ok(qtype) || rows <= 0 || cols <= 0 || cols % 32) return 0;
+  return qmv_ws_bytes(rows, cols, gemm16_splits(rows, cols), 1, 16, false);
+}
+
+size_t qg_lmhead_ws_bytes(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0 || cols % 32) return 0;
+  return qmv_ws_bytes(rows, cols, gemv_splits(rows, cols), 1, 1, true);
+}
+
+int qgemv_q4_0(const void *qs, const void *d, int64_t rows, int64_t cols, const float *X, int64_t ldx,
+               int32_t ncols, float *Y, int64_t ldy, int32_t accumulate, void *ws, size_t ws_bytes,
+               void *stream) {
+  return qmv_common(QG_Q4_0, qs, d, rows, cols, X, ldx, ncols, Y, ldy, accumulate, ws, ws_bytes, stream,
+                    false);
+}
+
+int qgemv_q8_0(const void *qs, const void *d, int64_t rows, int64_t cols, const float *X, int64_t ldx,
+               int32_t ncols, float *Y, int64_t ldy, int32_t accumulate, void *ws, size_t ws_bytes,
+               void *stream) {
+  return qmv_common(QG_Q8_0, qs, d, rows, cols, X, ldx, ncols, Y, ldy, accumulate, ws, ws_bytes, stream,
+                    false);
+}
+
+int qgemm16(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols, const float *X,
+            int64_t ldx, float *Y, int64_t ldy, int32_t accumulate, void *ws, size_t ws_bytes,
+            void *stream) {
+  return qmv_common(qtype, qs, d, rows, cols, X, ldx, 16, Y, ldy, accumulate, ws, ws_bytes, stream, true);
+}
+
+int gateup_silu(int qtype, const void *g_qs, const void *g_d, const void *u_qs, const void *u_d,
+                int64_t rows, int64_t cols, const float *X, int64_t ldx, int32_t ncols, float *H,
+                int64_t ldh, void *ws, size_t ws_bytes, void *stream) {
+  if (!qtype_ok(qtype)) return QG_EINVAL;
+  int st = check_matrix(g_qs, g_d, rows, cols);
+  if (st) return st;
+  if ((st = check_matrix(u_qs, u_d, rows, cols))) return st;
+  if (ncols < 1 || ncols > 8) return QG_ESHAPE;
+  if ((st = check_act(X, ldx, cols, ncols))) return st;
+  if ((st = check_out(H, ldh, rows))) return st;
+  if (overlap(span(X, ldx, cols, ncols), span(H, ldh, rows, ncols))) return QG_EINVAL;
+  if (!ws || ws_bytes < qg_gateup_ws_bytes(rows, cols)) return QG_EWORKSPACE;
+  if (!aligned(ws, 256)) return QG_EALIGN;
+  QmvCall c;
+  memset(&c, 0, sizeof(c));
+  c.qtype = qtype;
+  c.nmat = 2;
+  c.qs[0] = g_qs;
+  c.qs[1] = u_qs;
+  c.d[0] = g_d;
+  c.d[1] = u_d;
+  c.rows = rows;
+  c.cols = cols;
+  c.n_rows = rows;
+  c.X = X;
+  c.ldx = ldx;
+  c.ncols = ncols;
+  c.Y = H;
+  c.ldy = ldh;
+  c.epi = EPI_SILU;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  c.stream = (hipStream_t)stream;
+  return launch_qmv(c);
+}
+
+int lmhead_argmax(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols, int64_t n_rows,
+                  const float *x, int32_t *out_idx, float *out_val, void *ws, size_t ws_bytes,
+                  void *stream) {
+  if (!qtype_ok(qtype)) return QG_EINVAL;
+  int st = check_matrix(qs, d, rows, cols);
+  if (st) return st;
+  if (n_rows < 1 || n_rows > rows) return QG_ESHAPE;
+  if ((st = check_act(x, cols, cols, 1))) return st;
+  if (!out_idx) return QG_EINVAL;
+  if (!aligned(out_idx, 4) || (out_val && !aligned(out_val, 4))) return QG_EALIGN;
+  if (!ws || ws_bytes < qg_lmhead_ws_bytes(rows, cols)) return QG_EWORKSPACE;
+  if (!aligned(ws, 256)) return QG_EALIGN;
+  QmvCall c;
+  memset(&c, 0, sizeof(c));
+  c.qtype = qtype;
+  c.nmat = 1;
+  c.qs[0] = c.qs[1] = qs;
+  c.d[0] = c.d[1] = d;
+  c.rows = rows;
+  c.cols = cols;
+  c.n_rows = n_rows;
+  c.X = x;
+  c.ldx = cols;
+  c.ncols = 1;
+  c.Y = nullptr;
+  c.ldy = 0;
+  c.epi = EPI_ARGMAX;
+  c.out_idx = out_idx;
+  c.out_val = out_val;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  c.stream = (hipStream_t)stream;
+  return launch_qmv(c);
+}
+
+static int check_moe(const qg_moe *m, int32_t ntok) {
+  if (!m) return QG_EINVAL;
+  if (!qtype_ok(m->qtype)) return QG_EINVAL;
+  if (ntok < 1 || ntok > 16) return QG_ESHAPE;
+  if (m->n_expert < 1 || m->n_expert > 1024) return QG_ESHAPE;
+  if (m->top_k < 1 || m->top_k > 8 || m->top_k > m->n_expert) return QG_ESHAPE;
+  if (m->hidden <= 0 || m->hidden % 128 || m->hidden > 16384) return QG_ESHAPE;
+  if (m->ffn <= 0 || m->ffn % 128 || m->ffn > 16384) return QG_ESHAPE;
+  if (m->sh_ffn < 0 || m->sh_ffn % 128 || m->sh_ffn > 16384) return QG_ESHAPE;
+  if (!m->router || !m->gate_qs || !m->up_qs || !m->down_qs || !m->gate_d || !m->up_d || !m->down_d)
+    return QG_EINVAL;
+  if (!aligned(m->router, 16)) return QG_EALIGN;
+  const void *q[3] = {m->gate_qs, m->up_qs, m->down_qs};
+  const void *d[3] = {m->gate_d, m->up_d, m->down_d};
+  for (int i = 0; i < 3; ++i)
+    if (!aligned(q[i], 16) || !aligned(d[i], 8)) return QG_EALIGN;
+  if (m->sh_ffn > 0) {
+    const void *sq[3] = {m->sh_gate_qs, m->sh_up_qs, m->sh_down_qs};
+    const void *sd[3] = {m->sh_gate_d, m->sh_up_d, m->sh_down_d};
+    for (int i = 0; i < 3; ++i) {
+      if (!sq[i] || !sd[i]) return QG_EINVAL;
+      if (!aligned(sq[i], 16) || !aligned(sd[i], 8)) return QG_EALIGN;
+    }
+  }
+  return QG_OK;
+}
+
+size_t qg_moe_ws_bytes(const qg_moe *m, int32_t ntok) {
+  if (check_moe(m, ntok) != QG_OK) return 0;
+  return moe_ws_bytes(m, ntok);
+}
+
+int moe_ffn(const qg_moe *m, const float *X, int64_t ldx, int32_t ntok, float *Y, int64_t ldy,
+            int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_moe(m, ntok);
+  if (st) return st;
+  if ((st = check_act(X, ldx, m->hidden, ntok))) return st;
+  if ((st = check_out(Y, ldy, m->hidden))) return st;
+  if (overlap(span(X, ldx, m->hidden, ntok), span(Y, ldy, m->hidden, ntok))) return QG_EINVAL;
+  if ((topk_idx && !aligned(topk_idx, 4)) || (topk_w && !aligned(topk_w, 4))) return QG_EALIGN;
+  if (!ws || ws_bytes < moe_ws_bytes(m, ntok)) return QG_EWORKSPACE;
+  if (!aligned(ws, 256)) return QG_EALIGN;
+  MoeCall c;
+  c.m = m;
+  c.X = X;
+  c.ldx = ldx;
+  c.ntok = ntok;
+  c.Y = Y;
+  c.ldy = ldy;
+  c.topk_idx = topk_idx;
+  c.topk_w = topk_w;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  c.stream = (hipStream_t)stream;
+  return launch_moe(c);
+}
+
+}  // extern "C"

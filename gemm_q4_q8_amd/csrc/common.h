@@ -1,0 +1,127 @@
+// Device helpers shared by the gfx950 kernels of libqgemm.
+//
+// Weight decoding follows the GGUF block definition ("Engine and kernels",
+// What it runs: 32 weights plus one f16 scale per block) in the tiled layout
+// declared in include/qgemm.h.  Weights become exact f16 values in registers
+// ("Reading weights": dequantise in registers, full-precision weights never
+// exist in memory); activations enter as f16; every sum is f32 ("Correctness
+// and portability": no f16 accumulation).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qg {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
+constexpr int Q4 = 2;
+constexpr int Q8 = 8;
+constexpr int TILE_ROWS = 16;
+constexpr int TILE_BLOCKS = 4;
+constexpr int TILE_COLS = 128;
+constexpr int TILE_D_BYTES = 128;
+template <int QT> struct QTraits;
+template <> struct QTraits<Q4> { static constexpr int tile_bytes = 1024; static constexpr int block_bytes = 18; };
+template <> struct QTraits<Q8> { static constexpr int tile_bytes = 2048; static constexpr int block_bytes = 34; };
+
+__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
+
+// Q4_0: one u32 word of the tiled layout = 8 nibbles of one block slice.
+// OR-ing a nibble into the mantissa of f16 1024.0 (0x6400) gives 1024 + n
+// exactly; subtracting 1032 leaves n - 8 exactly (integers below 2048 are
+// exact in f16).  Pair u holds columns (2u, 2u + 1) of the slice.
+__device__ __forceinline__ void unpack_q4(uint32_t w, h2 out[4]) {
+  const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+  out[0] = as_h2((w & 0x000F000Fu) | 0x64006400u) - bias;
+  out[1] = as_h2(((w >> 4) & 0x000F000Fu) | 0x64006400u) - bias;
+  out[2] = as_h2(((w >> 8) & 0x000F000Fu) | 0x64006400u) - bias;
+  out[3] = as_h2(((w >> 12) & 0x000F000Fu) | 0x64006400u) - bias;
+}
+
+// Q8_0: two u32 words = 8 biased bytes (q + 128) of one block slice.  A byte
+// permute puts each byte under a 0x64 high byte (1024 + b, exact), then
+// subtracting 1152 = 1024 + 128 leaves q exactly.
+__device__ __forceinline__ void unpack_q8(uint32_t w0, uint32_t w1, h2 out[4]) {
+  const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  out[0] = as_h2(__builtin_amdgcn_perm(0x64646464u, w0, 0x05010400u)) - bias;
+  out[1] = as_h2(__builtin_amdgcn_perm(0x64646464u, w0, 0x05030402u)) - bias;
+  out[2] = as_h2(__builtin_amdgcn_perm(0x64646464u, w1, 0x05010400u)) - bias;
+  out[3] = as_h2(__builtin_amdgcn_perm(0x64646464u, w1, 0x05030402u)) - bias;
+}
+
+// The f16 scale number j (0..3) of a lane's 8-byte scale word.
+__device__ __forceinline__ float scale_of(u2 dw, int j) {
+  uint32_t w = (j < 2) ? dw[0] : dw[1];
+  uint16_t b = (j & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xFFFF);
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+
+__device__ __forceinline__ h8 cvt8(const float4 lo, const float4 hi) {
+  h8 r;
+  r[0] = (_Float16)lo.x; r[1] = (_Float16)lo.y; r[2] = (_Float16)lo.z; r[3] = (_Float16)lo.w;
+  r[4] = (_Float16)hi.x; r[5] = (_Float16)hi.y; r[6] = (_Float16)hi.z; r[7] = (_Float16)hi.w;
+  return r;
+}
+
+__device__ __forceinline__ h2 lo_pair(h8 v, int u) {
+  h2 r;
+  r[0] = v[2 * u];
+  r[1] = v[2 * u + 1];
+  return r;
+}
+
+// Agent-scope relaxed accesses for data exchanged between workgroups (the
+// L2 caches of the eight XCDs are not coherent with each other).
+__device__ __forceinline__ void st_agent(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent_u32(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_agent_u32(const uint32_t *p) {
+  return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// "Last one in" for a group of `target` workgroups sharing a counter: every
+// workgroup publishes its stores, then increments; the workgroup that sees
+// target - 1 is last, resets the counter to zero for the next call, and
+// acquires everything the others published.  `flag` is an LDS word.
+__device__ __forceinline__ bool arrive_last(uint32_t *cnt, uint32_t target, uint32_t *flag) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t old = atomicAdd(cnt, 1u);
+    uint32_t last = (old == target - 1) ? 1u : 0u;
+    if (last) atomicExch(cnt, 0u);
+    *flag = last;
+  }
+  __syncthreads();
+  bool last = *flag != 0;
+  if (last) __threadfence();
+  return last;
+}
+
+// Order for argmax / top-k: larger value first, then lower index; a NaN
+// ranks below every number.
+__device__ __forceinline__ bool ranks_before(float va, int32_t ia, float vb, int32_t ib) {
+  bool na = va != va, nb = vb != vb;
+  if (na || nb) return nb && (!na || ia < ib);
+  return va > vb || (va == vb && ia < ib);
+}
+
+// blockIdx -> work unit, so that each XCD (workgroups are dealt to the eight
+// XCDs round-robin) takes a contiguous range of units.
+__device__ __forceinline__ int64_t xcd_unit(int64_t per_xcd) {
+  int64_t b = blockIdx.x;
+  return (b & 7) * per_xcd + (b >> 3);
+}
+
+}  // namespace qg

@@ -1,0 +1,62 @@
+// Host-side interfaces between the C-ABI layer (api.cpp) and the kernel
+// launchers (*.hip).  Not installed; not part of the ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "qgemm.h"
+
+namespace qg {
+
+enum Epi { EPI_STORE = 0, EPI_ACC = 1, EPI_SILU = 2, EPI_ARGMAX = 3 };
+
+// One launch of the tiled product kernel.
+struct QmvCall {
+  int qtype;
+  int nmat;                 // 1, or 2 for gate/up
+  const void *qs[2];
+  const void *d[2];
+  int64_t rows, cols;       // logical matrix size
+  int64_t n_rows;           // rows actually produced (argmax: prefix), else rows
+  const float *X;
+  int64_t ldx;
+  int ncols;                // 1..8 (dot path) or 16 (matrix-core path)
+  float *Y;
+  int64_t ldy;
+  int epi;
+  int32_t *out_idx;         // argmax
+  float *out_val;
+  void *ws;
+  size_t ws_bytes;
+  hipStream_t stream;
+};
+
+// Split-K factor: a function of the matrix shape only, so that every column
+// count gives the same per-row reduction order.
+int gemv_splits(int64_t rows, int64_t cols);
+int gemm16_splits(int64_t rows, int64_t cols);
+
+size_t qmv_ws_bytes(int64_t rows, int64_t cols, int splits, int nmat, int ncols_max, bool argmax);
+
+int launch_qmv(const QmvCall &c);  // returns 0 or a QG_ status
+int launch_repack(int qtype, int64_t n_mat, int64_t rows, int64_t cols, const void *blocks,
+                  void *qs, void *d, hipStream_t stream);
+
+struct MoeCall {
+  const qg_moe *m;
+  const float *X;
+  int64_t ldx;
+  int ntok;
+  float *Y;
+  int64_t ldy;
+  int32_t *topk_idx;
+  float *topk_w;
+  void *ws;
+  size_t ws_bytes;
+  hipStream_t stream;
+};
+size_t moe_ws_bytes(const qg_moe *m, int ntok);
+int launch_moe(const MoeCall &c);
+
+}  // namespace qg

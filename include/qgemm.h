@@ -1,0 +1,215 @@
+/*
+ * qgemm.h - block-quantised (GGUF Q4_0 / Q8_0) weight x activation products
+ * for AMD MI355X (gfx950).  Plain C ABI: no C++ or framework types cross it.
+ *
+ * Sources for what each call computes (the pages this library follows):
+ *   [ENG]  "Engine and kernels" (Pooled engine page): "What it runs" (GGUF
+ *          Q4_0 / Q8_0 blocks of 32 weights + one f16 scale), "Kernel
+ *          families" (cooperative GEMV, batched GEMV twins, fused gate/up with
+ *          SiLU, 16-column prefill GEMM, MoE, GPU sampling), "What each trick
+ *          bought" (Reading weights: dequantise in registers, f16 scales,
+ *          load-time repack into separate weight and scale arrays; Fewer
+ *          passes: y += W.x into the residual, GPU argmax with lowest-index
+ *          ties; Batching and prefill: split-K pinned per shape; Speculation:
+ *          drafts over a prefix of the vocabulary rows), "Correctness and
+ *          portability" (no f16 accumulation).
+ *   [ARCH] "Architecture" (Pooled architecture page): "One token, end to end"
+ *          (LM head over all vocabulary rows, greedy sampling on the GPU),
+ *          "Prefill" (16 columns per pass), "Memory and caching" (Q4_0 / Q8_0
+ *          repacked on the way into separate nibble and scale arrays).
+ *   [MOE]  "A 235B model in a browser window": experts stacked by role (all
+ *          gate matrices in one tensor, all up in a second, all down in a
+ *          third), each expert a gated FFN of three matrices.
+ *
+ * Conventions for every call:
+ *   - A matrix W has `rows` outputs and `cols` inputs; cols % 32 == 0.
+ *     Row r of the GGUF tensor is cols/32 consecutive blocks.
+ *   - Activations are f32 column-major: column j of X starts at X + j*ldx.
+ *     X, Y and H must be 16-byte aligned and ldx, ldy, ldh multiples of 4
+ *     (whole 16-byte vectors); ldx >= cols, ldy >= rows.
+ *   - Arithmetic: weights are dequantised exactly in registers; activations
+ *     enter the products rounded to f16 (round to nearest even, relative
+ *     error <= 2^-11); every sum and the scale multiply are f32.  Nothing is
+ *     accumulated in f16.  Results are bitwise reproducible run to run: all
+ *     reductions (split-K included) have a fixed order per shape.
+ *   - Pointers named qs, d, X, Y, H, x, out_*, ws, blocks are DEVICE
+ *     pointers; `stream` is a hipStream_t passed as void* (NULL = the null
+ *     stream).  Calls are asynchronous on that stream; a device fault shows
+ *     up at the caller's next synchronisation.  All argument checks run on
+ *     the host before any HIP call, so every error code below can be
+ *     produced without a GPU.  Nothing throws across the ABI.
+ *   - Memory is owned by the caller.  The library allocates nothing.
+ *   - Workspace (`ws`, `ws_bytes`): device memory sized by the matching
+ *     *_ws_bytes query.  It must be zero-filled before its first use; every
+ *     call that completes leaves it zero-filled again (its counters reset
+ *     themselves).  One workspace must not be used by two calls that may
+ *     overlap in time (different streams): they would race.
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* GGUF tensor type ids, so a GGUF reader can pass them through. */
+enum { QG_Q4_0 = 2, QG_Q8_0 = 8 };
+
+enum {
+  QG_OK = 0,
+  QG_EINVAL = -1,       /* null pointer, bad enum, overlap of output and input */
+  QG_ESHAPE = -2,       /* sizes: cols % 32, non-positive sizes, ncols, n_rows, top_k */
+  QG_EALIGN = -3,       /* pointer or leading dimension alignment */
+  QG_EUNSUPPORTED = -4, /* valid request this build does not serve */
+  QG_EWORKSPACE = -5,   /* ws NULL or smaller than the query says */
+  QG_EHIP = -6          /* a HIP launch reported an error */
+};
+
+/* Text for a status code (static storage). */
+const char *qg_strerror(int status);
+
+/* ------------------------------------------------------------------------
+ * Load-time repack  [ARCH Memory and caching; ENG Reading weights]
+ *
+ * Rewrites GGUF blocks into two streams the kernels read as contiguous
+ * 1 KiB stripes: a weight stream `qs` and an f16 scale stream `d`.  It is a
+ * layout change only (a bijection; the bytes are the same weights).
+ *
+ * Tiled layout (n_mat matrices of rows x cols, each padded independently):
+ *   tile = 16 rows x 4 blocks (128 columns); NT = ceil(rows/16),
+ *   KT = ceil(cols/128); tile (rt, kt) has index t = rt*KT + kt and matrix m
+ *   starts at m*NT*KT tiles.  Positions beyond rows / cols hold zero weights
+ *   and a zero scale.
+ *   Q4_0 qs: 1024 B per tile.  16-byte chunk c = 16*s + r (s = 8-column slice
+ *     0..3, r = row 0..15 in the tile) holds 4 little-endian u32 words; word
+ *     j covers block 4*kt + j, row 16*rt + r, columns 8*s + i (i = 0..7) of
+ *     that block.  The unsigned nibble (weight + 8) of column i = 2u is at
+ *     bits 4u..4u+3, that of column i = 2u + 1 at bits 16+4u..19+4u.
+ *   Q8_0 qs: 2048 B per tile, two 1024-B halves h = 0, 1.  In half h, chunk
+ *     c = 16*s + r holds 8 bytes of block 4*kt + 2h, then 8 bytes of block
+ *     4*kt + 2h + 1; byte i is (weight of column 8*s + i) + 128.
+ *   d: 128 B per tile; the f16 scale of row 16*rt + r, block 4*kt + j is at
+ *     byte 8*r + 2*j.
+ * ------------------------------------------------------------------------ */
+
+/* Sizes of the two packed streams (host only, no HIP call). */
+int qg_packed_bytes(int qtype, int64_t n_mat, int64_t rows, int64_t cols,
+                    size_t *qs_bytes, size_t *d_bytes);
+
+/* blocks: n_mat*rows*(cols/32) GGUF blocks (18 B or 34 B each), 2-byte
+ * aligned.  qs 16-byte aligned, d 8-byte aligned, sized by qg_packed_bytes.
+ * Outputs must not overlap the input. */
+int qg_repack(int qtype, int64_t n_mat, int64_t rows, int64_t cols,
+              const void *blocks, void *qs, void *d, void *stream);
+
+/* ------------------------------------------------------------------------
+ * GEMV / batched GEMV  [ENG Kernel families: cooperative GEMV (decode),
+ * batched GEMV twins (speculative verify); Fewer passes: y += W.x]
+ *
+ *   Y[:, j] = (accumulate ? Y[:, j] : 0) + W X[:, j],  j < ncols, ncols 1..8.
+ * With accumulate the product is summed first and added to Y once.  Column j
+ * of an ncols-wide call is bitwise equal to a 1-column call on X[:, j] (the
+ * per-row reduction order depends only on rows and cols).
+ * qs / d: the packed streams of one matrix (qg_repack with n_mat = 1).
+ * Y must not overlap X.
+ * ------------------------------------------------------------------------ */
+size_t qg_gemv_ws_bytes(int64_t rows, int64_t cols);
+
+int qgemv_q4_0(const void *qs, const void *d, int64_t rows, int64_t cols,
+               const float *X, int64_t ldx, int32_t ncols, float *Y, int64_t ldy,
+               int32_t accumulate, void *ws, size_t ws_bytes, void *stream);
+
+int qgemv_q8_0(const void *qs, const void *d, int64_t rows, int64_t cols,
+               const float *X, int64_t ldx, int32_t ncols, float *Y, int64_t ldy,
+               int32_t accumulate, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * 16-column prefill GEMM  [ENG Kernel families: prefill GEMM; Batching and
+ * prefill: row-stationary GEMM at 16 columns, split-K pinned per shape;
+ * ARCH Prefill: each weight block read once for all 16 columns]
+ *
+ *   Y = (accumulate ? Y : 0) + W X,  X cols x 16, Y rows x 16.
+ * Runs on the matrix cores (f16 operands after exact dequantisation, f32
+ * accumulate; the block scale is applied in f32 to each block's product).
+ * ------------------------------------------------------------------------ */
+size_t qg_gemm16_ws_bytes(int qtype, int64_t rows, int64_t cols);
+
+int qgemm16(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols,
+            const float *X, int64_t ldx, float *Y, int64_t ldy, int32_t accumulate,
+            void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Fused gate/up + SiLU  [ENG Kernel families: fused gate/up, both FFN
+ * projections in one sweep, SiLU applied before writing]
+ *
+ *   H[:, j] = silu(Wg X[:, j]) * (Wu X[:, j]),  silu(g) = g / (1 + e^-g),
+ *   ncols 1..8.  Wg and Wu have the same rows x cols.  H rows x ncols.
+ * ------------------------------------------------------------------------ */
+size_t qg_gateup_ws_bytes(int64_t rows, int64_t cols);
+
+int gateup_silu(int qtype, const void *g_qs, const void *g_d, const void *u_qs,
+                const void *u_d, int64_t rows, int64_t cols, const float *X,
+                int64_t ldx, int32_t ncols, float *H, int64_t ldh,
+                void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * LM head + greedy argmax  [ARCH One token, end to end: head over the whole
+ * vocabulary, greedy sampling on the GPU; ENG Fewer passes: GPU argmax,
+ * lowest-index tie-breaking; ENG Speculation: drafts over a row prefix]
+ *
+ *   *out_idx = the lowest r < n_rows maximising (W x)[r];  *out_val = that
+ *   maximum (out_val may be NULL).  Only rows < n_rows are read (up to the
+ *   16-row tile holding row n_rows - 1).  -0 equals +0; inputs are finite
+ *   (a NaN logit ranks below every number).  The logits never reach memory.
+ * ------------------------------------------------------------------------ */
+size_t qg_lmhead_ws_bytes(int64_t rows, int64_t cols);
+
+int lmhead_argmax(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols,
+                  int64_t n_rows, const float *x, int32_t *out_idx, float *out_val,
+                  void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * MoE FFN  [ENG What it runs: 256 experts, 8 active per token, plus a shared
+ * expert; Kernel families: router, top-k, expert gate/up and down, weighted
+ * combine, all on the GPU, no readback; MOE: experts stacked by role]
+ *
+ * Per token t (column t of X, hidden rows):
+ *   l = R x_t (f32 router, n_expert x hidden, row-major, 16-byte aligned);
+ *   sel = the top_k experts by (l descending, index ascending);
+ *   p = softmax(l[sel]) if normalize_topk, else softmax(l)[sel];
+ *   Y[:, t] += sum_k p_k Down_e(silu(Gate_e x_t) * Up_e x_t)     (e = sel_k)
+ *            + SharedDown(silu(SharedGate x_t) * SharedUp x_t)   (if sh_ffn > 0)
+ * The expert sum is formed in f32 in k order, the shared expert added last,
+ * then the total is added to Y once.  Gate and up stacks: qg_repack with
+ * n_mat = n_expert, rows = ffn, cols = hidden; down stack: n_mat = n_expert,
+ * rows = hidden, cols = ffn; the shared matrices: n_mat = 1, ffn -> sh_ffn.
+ * Each selected expert's weights are read once for all tokens routed to it.
+ * topk_idx / topk_w (ntok x top_k, row-major, may be NULL) receive sel and p.
+ * Limits: ntok 1..16 per call, top_k 1..8, n_expert 1..1024,
+ * hidden and ffn multiples of 128 and at most 16384.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int64_t hidden, ffn;
+  int32_t n_expert, top_k, normalize_topk;
+  int32_t qtype;
+  const float *router;
+  const void *gate_qs, *up_qs, *down_qs;
+  const void *gate_d, *up_d, *down_d;
+  int64_t sh_ffn; /* 0 = no shared expert */
+  const void *sh_gate_qs, *sh_up_qs, *sh_down_qs;
+  const void *sh_gate_d, *sh_up_d, *sh_down_d;
+} qg_moe;
+
+size_t qg_moe_ws_bytes(const qg_moe *m, int32_t ntok);
+
+int moe_ffn(const qg_moe *m, const float *X, int64_t ldx, int32_t ntok, float *Y,
+            int64_t ldy, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+            void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QGEMM_H */

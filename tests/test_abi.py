@@ -1,0 +1,157 @@
+"""C-ABI checks that need no GPU: every declared symbol is exported, the
+size queries, and every argument check (each returns before any HIP call)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gemm_q4_q8_amd as qg
+from oracle import quant
+from tests.conftest import ROOT
+
+L = qg.lib
+OK, EINVAL, ESHAPE, EALIGN, EUNSUP, EWS = 0, -1, -2, -3, -4, -5
+FAKE = 1 << 40          # an aligned, never-dereferenced "device" address
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "qgemm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char)\s*\*?\s*(\w+)\s*\(", src, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert {"qgemv_q4_0", "qgemv_q8_0", "qgemm16", "gateup_silu", "moe_ffn",
+            "lmhead_argmax", "qg_repack", "qg_packed_bytes"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_strerror():
+    for s in (0, -1, -2, -3, -4, -5, -6, 7):
+        assert isinstance(L.qg_strerror(s), bytes) and L.qg_strerror(s)
+
+
+@pytest.mark.parametrize("qtype", [qg.Q4_0, qg.Q8_0])
+@pytest.mark.parametrize("n_mat,rows,cols", [(1, 2048, 2048), (1, 20, 160), (3, 512, 2048), (1, 248320, 5120)])
+def test_packed_bytes_match_layout_definition(qtype, n_mat, rows, cols):
+    assert qg.packed_bytes(qtype, rows, cols, n_mat) == quant.packed_bytes(qtype, n_mat, rows, cols)
+
+
+def test_packed_bytes_exact_sizes_for_whole_tiles():
+    # 17408 x 5120 Q4_0: 44,564,480 weight bytes + 5,570,560 scale bytes (18 B per 32 weights)
+    assert qg.packed_bytes(qg.Q4_0, 17408, 5120) == (44564480, 5570560)
+    assert sum(qg.packed_bytes(qg.Q8_0, 248320, 5120)) == 248320 * 5120 // 32 * 34
+
+
+def test_packed_bytes_rejects():
+    qb, db = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.qg_packed_bytes(3, 1, 16, 32, ctypes.byref(qb), ctypes.byref(db)) == EINVAL
+    assert L.qg_packed_bytes(2, 1, 16, 33, ctypes.byref(qb), ctypes.byref(db)) == ESHAPE
+    assert L.qg_packed_bytes(2, 0, 16, 32, ctypes.byref(qb), ctypes.byref(db)) == ESHAPE
+    assert L.qg_packed_bytes(2, 1, 16, 32, None, ctypes.byref(db)) == EINVAL
+
+
+def test_ws_queries():
+    assert L.qg_gemv_ws_bytes(5120, 17408) > 0
+    assert L.qg_gemv_ws_bytes(5120, 17) == 0
+    assert L.qg_gemm16_ws_bytes(2, 5120, 17408) > L.qg_gemv_ws_bytes(5120, 17408)
+    assert L.qg_gateup_ws_bytes(17408, 5120) >= L.qg_gemv_ws_bytes(17408, 5120)
+    assert L.qg_lmhead_ws_bytes(248320, 5120) > 0
+
+
+def _gemv(**kw):
+    a = dict(qs=FAKE, d=FAKE, rows=64, cols=128, X=FAKE + (1 << 20), ldx=128, ncols=1,
+             Y=FAKE + (2 << 20), ldy=64, acc=0, ws=FAKE + (3 << 20), wsb=1 << 20, stream=None)
+    a.update(kw)
+    return L.qgemv_q4_0(a["qs"], a["d"], a["rows"], a["cols"], a["X"], a["ldx"], a["ncols"],
+                        a["Y"], a["ldy"], a["acc"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_gemv_argument_checks():
+    assert _gemv(qs=None) == EINVAL
+    assert _gemv(d=None) == EINVAL
+    assert _gemv(X=None) == EINVAL
+    assert _gemv(Y=None) == EINVAL
+    assert _gemv(cols=100) == ESHAPE
+    assert _gemv(rows=0) == ESHAPE
+    assert _gemv(ncols=0) == ESHAPE
+    assert _gemv(ncols=9) == ESHAPE
+    assert _gemv(ldx=64) == ESHAPE
+    assert _gemv(ldy=10) == ESHAPE
+    assert _gemv(qs=FAKE + 8) == EALIGN
+    assert _gemv(d=FAKE + 4) == EALIGN
+    assert _gemv(X=FAKE + (1 << 20) + 4) == EALIGN
+    assert _gemv(ldx=130) == EALIGN
+    assert _gemv(Y=FAKE + (2 << 20) + 2) == EALIGN
+    assert _gemv(ws=None) == EWS
+    assert _gemv(wsb=16) == EWS
+    assert _gemv(ws=FAKE + (3 << 20) + 16) == EALIGN
+    # output overlapping the input
+    assert _gemv(Y=FAKE + (1 << 20) + 64) == EINVAL
+
+
+def test_gemm16_and_gateup_checks():
+    ws = FAKE + (3 << 20)
+    X, Y = FAKE + (1 << 20), FAKE + (2 << 20)
+    assert L.qgemm16(5, FAKE, FAKE, 64, 128, X, 128, Y, 64, 0, ws, 1 << 24, None) == EINVAL
+    assert L.qgemm16(2, FAKE, FAKE, 64, 100, X, 128, Y, 64, 0, ws, 1 << 24, None) == ESHAPE
+    assert L.qgemm16(2, FAKE, FAKE, 64, 128, X, 128, Y, 64, 0, ws, 8, None) == EWS
+    assert L.gateup_silu(2, FAKE, FAKE, None, FAKE, 64, 128, X, 128, 1, Y, 64, ws, 1 << 20, None) == EINVAL
+    assert L.gateup_silu(2, FAKE, FAKE, FAKE, FAKE, 64, 128, X, 128, 9, Y, 64, ws, 1 << 20, None) == ESHAPE
+    assert L.gateup_silu(2, FAKE, FAKE, FAKE, FAKE, 64, 128, X, 128, 1, X, 64, ws, 1 << 20, None) == EINVAL
+
+
+def test_lmhead_checks():
+    ws = FAKE + (3 << 20)
+    x, o = FAKE + (1 << 20), FAKE + (2 << 20)
+    assert L.lmhead_argmax(2, FAKE, FAKE, 64, 128, 0, x, o, None, ws, 1 << 20, None) == ESHAPE
+    assert L.lmhead_argmax(2, FAKE, FAKE, 64, 128, 65, x, o, None, ws, 1 << 20, None) == ESHAPE
+    assert L.lmhead_argmax(2, FAKE, FAKE, 64, 128, 64, x, None, None, ws, 1 << 20, None) == EINVAL
+    assert L.lmhead_argmax(2, FAKE, FAKE, 64, 128, 64, x, o + 2, None, ws, 1 << 20, None) == EALIGN
+    assert L.lmhead_argmax(2, FAKE, FAKE, 64, 128, 64, x, o, None, ws, 4, None) == EWS
+
+
+def test_repack_checks():
+    src, qs, d = FAKE, FAKE + (1 << 30), FAKE + (2 << 30)
+    assert L.qg_repack(2, 1, 16, 128, None, qs, d, None) == EINVAL
+    assert L.qg_repack(2, 1, 16, 128, src + 1, qs, d, None) == EALIGN
+    assert L.qg_repack(2, 1, 16, 128, src, qs + 4, d, None) == EALIGN
+    assert L.qg_repack(2, 1, 16, 100, src, qs, d, None) == ESHAPE
+    assert L.qg_repack(2, 1, 16, 128, src, src + 64, d, None) == EINVAL   # overlaps input
+
+
+def _moe(**kw):
+    m = qg.qg_moe()
+    m.hidden, m.ffn, m.n_expert, m.top_k, m.normalize_topk, m.qtype = 256, 128, 16, 4, 1, 2
+    m.router = FAKE
+    for f in ("gate_qs", "up_qs", "down_qs", "gate_d", "up_d", "down_d"):
+        setattr(m, f, FAKE + (1 << 24))
+    m.sh_ffn = 0
+    for k, v in kw.items():
+        setattr(m, k, v)
+    return m
+
+
+def test_moe_checks():
+    X, Y, ws = FAKE + (1 << 28), FAKE + (2 << 28), FAKE + (3 << 28)
+
+    def call(m, ntok=1, wsb=1 << 26):
+        return L.moe_ffn(ctypes.byref(m), X, 256, ntok, Y, 256, None, None, ws, wsb, None)
+
+    assert L.qg_moe_ws_bytes(ctypes.byref(_moe()), 16) > 0
+    assert call(_moe(), ntok=0) == ESHAPE
+    assert call(_moe(), ntok=17) == ESHAPE
+    assert call(_moe(top_k=9)) == ESHAPE
+    assert call(_moe(top_k=17, n_expert=16)) == ESHAPE
+    assert call(_moe(n_expert=4, top_k=5)) == ESHAPE
+    assert call(_moe(hidden=200)) == ESHAPE
+    assert call(_moe(ffn=96)) == ESHAPE
+    assert call(_moe(qtype=3)) == EINVAL
+    assert call(_moe(router=None)) == EINVAL
+    assert call(_moe(router=FAKE + 4)) == EALIGN
+    assert call(_moe(sh_ffn=128)) == EINVAL          # shared expert pointers missing
+    assert call(_moe(), wsb=8) == EWS

@@ -1,0 +1,317 @@
+"""GPU parity: the HIP path (through the C-ABI) against the f64 oracle.
+
+Float outputs must satisfy |gpu - ref| <= 2e-3 * sum|w x| + 1e-5 (derived
+bounds for SiLU-gated and MoE outputs, see oracle.ops); indices bit-exact
+whenever the oracle certifies them; byte outputs (the repack) bit-exact.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import ops, quant
+
+pytestmark = pytest.mark.gpu
+
+Q4, Q8 = synth.Q4_0, synth.Q8_0
+SIG = {Q4: 0.02, Q8: 0.005}
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need an MI355X")
+    import gemm_q4_q8_amd as qg
+    return torch, qg, torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def up(env, a):
+    torch, _, dev = env
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def make(env, qtype, rows, cols, seed, sigma=None, n_mat=1):
+    torch, qg, dev = env
+    g = np.random.default_rng(seed)
+    if n_mat == 1:
+        raw = synth.gen_weights(qtype, rows, cols, SIG[qtype] if sigma is None else sigma, g)
+    else:
+        raw = np.stack([synth.gen_weights(qtype, rows, cols, SIG[qtype] if sigma is None else sigma, g)
+                        for _ in range(n_mat)])
+    W = qg.qg_repack(qtype, up(env, raw.reshape(-1)), rows, cols, n_mat)
+    return raw, W
+
+
+def host(t):
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def assert_tol(got, ref, tol, what):
+    err = np.abs(got - ref)
+    ratio = float(np.max(err / tol)) if err.size else 0.0
+    say(f"  {what}: max err/tol = {ratio:.3g}")
+    assert np.all(err <= tol), f"{what}: {int(np.sum(err > tol))} elements out of tolerance, worst ratio {ratio}"
+
+
+# ------------------------------------------------------------------ repack
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("n_mat,rows,cols", [(1, 40, 416), (3, 20, 160), (1, 64, 2048)])
+def test_repack_bit_exact(env, qtype, n_mat, rows, cols):
+    torch, qg, dev = env
+    say(f"repack qtype={qtype} n_mat={n_mat} {rows}x{cols}")
+    raw, W = make(env, qtype, rows, cols, seed=1, n_mat=n_mat)
+    torch.cuda.synchronize()
+    qs_ref, d_ref = quant.repack_reference(qtype, raw)
+    assert np.array_equal(W.qs.cpu().numpy(), qs_ref)
+    assert np.array_equal(W.d.cpu().numpy(), d_ref)
+
+
+# -------------------------------------------------------------------- GEMV
+SMALL = [(40, 416), (16, 128), (64, 4096), (200, 2080), (2048, 2048)]
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("rows,cols", SMALL)
+@pytest.mark.parametrize("ncols", [1, 3, 8])
+@pytest.mark.parametrize("acc", [0, 1])
+def test_gemv_parity(env, qtype, rows, cols, ncols, acc):
+    torch, qg, dev = env
+    say(f"gemv qtype={qtype} {rows}x{cols} ncols={ncols} acc={acc}")
+    raw, W = make(env, qtype, rows, cols, seed=rows * 7 + cols)
+    X = synth.gen_x(cols, ncols, cfg_id=rows + cols)
+    y_in = synth.rng(9, rows).standard_normal((rows, ncols)).astype(np.float32)
+    Xd = up(env, X.T)
+    Yd = up(env, y_in.T) if acc else None
+    Yd = qg.qgemv(W, Xd, Yd, accumulate=bool(acc))
+    torch.cuda.synchronize()
+    ref, a = ops.gemv(qtype, raw, X, y_in=y_in if acc else None)
+    assert_tol(host(Yd).T, ref, ops.tol_dot(a, ref), "gemv")
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("rows,cols", [(40, 416), (64, 4096), (5120, 5120)])
+def test_batched_columns_bitwise_equal_single(env, qtype, rows, cols):
+    torch, qg, dev = env
+    say(f"bit-identity qtype={qtype} {rows}x{cols}")
+    _, W = make(env, qtype, rows, cols, seed=3)
+    X = up(env, synth.gen_x(cols, 8, cfg_id=33).T)
+    for n in range(1, 9):
+        Yn = qg.qgemv(W, X[:n].contiguous())
+        for j in range(n):
+            Y1 = qg.qgemv(W, X[j:j + 1].contiguous())
+            assert torch.equal(Yn[j], Y1[0]), (n, j)
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+def test_repeat_runs_bitwise_identical(env, qtype):
+    torch, qg, dev = env
+    _, W = make(env, qtype, 5120, 17408, seed=4)
+    X = up(env, synth.gen_x(17408, 4, cfg_id=44).T)
+    Y0 = qg.qgemv(W, X).clone()
+    for _ in range(3):
+        assert torch.equal(qg.qgemv(W, X), Y0)
+    Z0 = qg.qgemm16(W, up(env, synth.gen_x(17408, 16, cfg_id=45).T)).clone()
+    assert torch.equal(qg.qgemm16(W, up(env, synth.gen_x(17408, 16, cfg_id=45).T)), Z0)
+
+
+def test_degenerate_weights(env):
+    torch, qg, dev = env
+    say("degenerate weights")
+    rows, cols = 48, 256
+    nib = np.full((rows, cols // 32, 32), 8, np.uint8)
+    d = np.abs(np.random.default_rng(0).normal(0, 1, (rows, cols // 32))).astype(np.float16)
+    raw = synth.pack_q4_0(nib, d)
+    W = qg.qg_repack(Q4, up(env, raw.reshape(-1)), rows, cols)
+    X = up(env, synth.gen_x(cols, 2, cfg_id=5).T)
+    assert torch.count_nonzero(qg.qgemv(W, X)) == 0
+    nib = np.random.default_rng(1).integers(0, 16, (rows, cols // 32, 32)).astype(np.uint8)
+    raw = synth.pack_q4_0(nib, np.zeros((rows, cols // 32), np.float16))
+    W = qg.qg_repack(Q4, up(env, raw.reshape(-1)), rows, cols)
+    assert torch.count_nonzero(qg.qgemv(W, X)) == 0
+    assert torch.count_nonzero(qg.qgemm16(W, up(env, synth.gen_x(cols, 16, cfg_id=6).T))) == 0
+
+
+# ------------------------------------------------------------------ gemm16
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("rows,cols", [(40, 416), (64, 4096), (200, 2080), (16, 128)])
+@pytest.mark.parametrize("acc", [0, 1])
+def test_gemm16_parity(env, qtype, rows, cols, acc):
+    torch, qg, dev = env
+    say(f"gemm16 qtype={qtype} {rows}x{cols} acc={acc}")
+    raw, W = make(env, qtype, rows, cols, seed=rows + 11 * cols)
+    X = synth.gen_x(cols, 16, cfg_id=7)
+    y_in = synth.rng(8, rows).standard_normal((rows, 16)).astype(np.float32)
+    Yd = up(env, y_in.T) if acc else None
+    Yd = qg.qgemm16(W, up(env, X.T), Yd, accumulate=bool(acc))
+    torch.cuda.synchronize()
+    ref, a = ops.gemv(qtype, raw, X, y_in=y_in if acc else None)
+    assert_tol(host(Yd).T, ref, ops.tol_dot(a, ref), "gemm16")
+
+
+# ----------------------------------------------------------------- gate/up
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("rows,cols", [(40, 416), (64, 4096), (512, 2048)])
+@pytest.mark.parametrize("ncols", [1, 4, 8])
+def test_gateup_parity(env, qtype, rows, cols, ncols):
+    torch, qg, dev = env
+    say(f"gateup qtype={qtype} {rows}x{cols} ncols={ncols}")
+    graw, G = make(env, qtype, rows, cols, seed=21)
+    uraw, U = make(env, qtype, rows, cols, seed=22)
+    X = synth.gen_x(cols, ncols, cfg_id=23)
+    H = qg.gateup_silu(G, U, up(env, X.T))
+    torch.cuda.synchronize()
+    h, th, _, _ = ops.gateup_silu(qtype, graw, uraw, X)
+    assert_tol(host(H).T, h, th, "gateup")
+
+
+# ----------------------------------------------------------------- LM head
+def _lm_case(env, qtype, rows, cols, seed, plant=None):
+    torch, qg, dev = env
+    g = np.random.default_rng(seed)
+    raw = synth.gen_weights(qtype, rows, cols, SIG[qtype], g)
+    if plant:
+        for dst, src in plant:
+            raw[dst] = raw[src]
+    W = qg.qg_repack(qtype, up(env, raw.reshape(-1)), rows, cols)
+    return raw, W
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("rows,cols", [(40, 416), (1000, 512), (70000, 1024)])
+def test_lmhead_argmax_certified(env, qtype, rows, cols):
+    torch, qg, dev = env
+    say(f"lmhead qtype={qtype} {rows}x{cols}")
+    raw, W = _lm_case(env, qtype, rows, cols, seed=rows)
+    for s in range(20):
+        x = synth.gen_x(cols, 1, cfg_id=1000 + s)[:, 0]
+        ref, a = ops.gemv(qtype, raw, x)
+        if ops.argmax_certified(ref, a, cols + 64, ops.U16):
+            break
+    else:
+        pytest.fail("no certified seed")
+    idx, val = qg.lmhead_argmax(W, up(env, x))
+    torch.cuda.synchronize()
+    i = int(idx.item())
+    assert i == ops.argmax_first(ref)
+    assert abs(val.item() - ref[i]) <= ops.tol_dot(a[i])
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+def test_lmhead_planted_ties_and_prefix(env, qtype):
+    torch, qg, dev = env
+    rows, cols = 5000, 512
+    raw = synth.gen_weights(qtype, rows, cols, SIG[qtype], np.random.default_rng(5))
+    for s in range(20):
+        x = synth.gen_x(cols, 1, cfg_id=55 + s)[:, 0]
+        ref, a = ops.gemv(qtype, raw, x)
+        top = ops.argmax_first(ref)
+        if top not in (17, 4099, rows - 1) and ops.argmax_certified(ref, a, cols + 64, ops.U16):
+            break
+    else:
+        pytest.fail("no certified seed")
+    # identical rows give bitwise-identical logits: copies of the best row in
+    # other tiles and row groups, before and after it, and at the last row
+    plant = (17, 4099, rows - 1)
+    for where in plant:
+        raw[where] = raw[top]
+        ref[where], a[where] = ref[top], a[top]
+    W = qg.qg_repack(qtype, up(env, raw.reshape(-1)), rows, cols)
+    xd = up(env, x)
+    idx, val = qg.lmhead_argmax(W, xd)
+    assert int(idx.item()) == min(17, top)
+    # row prefixes (a draft head reads only rows < n_rows)
+    copies = np.array(sorted(set(plant + (top,))))
+    for n_rows in (1, 17, 18, 4099, 4100, rows - 1, rows):
+        want = ops.argmax_first(ref[:n_rows])
+        # bitwise-identical rows tie exactly on the GPU too; certify the rest
+        keep = np.ones(n_rows, bool)
+        if want in copies:
+            keep[copies[copies < n_rows]] = False
+            keep[want] = True
+        sub = np.flatnonzero(keep)
+        if not ops.argmax_certified(ref[sub], a[sub], cols + 64, ops.U16):
+            continue
+        idx, _ = qg.lmhead_argmax(W, xd, n_rows=n_rows)
+        assert int(idx.item()) == want, n_rows
+    # all rows identical -> index 0
+    raw[:] = raw[3]
+    W = qg.qg_repack(qtype, up(env, raw.reshape(-1)), rows, cols)
+    idx, _ = qg.lmhead_argmax(W, xd)
+    assert int(idx.item()) == 0
+
+
+# -------------------------------------------------------------------- MoE
+def _moe_build(env, E, H, F, k, seed, shared=True, normalize=True):
+    torch, qg, dev = env
+    g = np.random.default_rng(seed)
+    gate = np.stack([synth.gen_weights(Q4, F, H, 0.02, g) for _ in range(E)])
+    upw = np.stack([synth.gen_weights(Q4, F, H, 0.02, g) for _ in range(E)])
+    down = np.stack([synth.gen_weights(Q4, H, F, 0.02, g) for _ in range(E)])
+    router = synth.gen_f32((E, H), 0.02, g)
+    sh = None
+    if shared:
+        sh = tuple(synth.gen_weights(Q4, r, c, 0.02, g) for r, c in ((F, H), (F, H), (H, F)))
+    rep = lambda raw, r, c, n=1: qg.qg_repack(Q4, up(env, raw.reshape(-1)), r, c, n)
+    m = qg.MoE(hidden=H, ffn=F, n_expert=E, top_k=k, router=up(env, router),
+               gate=rep(gate, F, H, E), up=rep(upw, F, H, E), down=rep(down, H, F, E),
+               normalize_topk=normalize)
+    if shared:
+        m.sh_gate, m.sh_up, m.sh_down = rep(sh[0], F, H), rep(sh[1], F, H), rep(sh[2], H, F)
+    return m, (gate, upw, down, router, sh)
+
+
+def _moe_check(env, m, host_w, T, k, cfg, normalize=True, tries=40):
+    torch, qg, dev = env
+    gate, upw, down, router, sh = host_w
+    H = m.hidden
+    for s in range(tries):
+        X = synth.gen_x(H, T, cfg_id=cfg + 1000 * s)
+        res = ops.moe_ffn(X, router, Q4, gate, upw, down, top_k=k, normalize=normalize,
+                          sh_gate=None if sh is None else sh[0], sh_up=None if sh is None else sh[1],
+                          sh_down=None if sh is None else sh[2],
+                          y_in=synth.rng(cfg, 90).standard_normal((H, T)).astype(np.float32))
+        if ops.moe_routing_certified(res, k, H):
+            break
+    else:
+        pytest.fail("no certified routing seed")
+    y_in = synth.rng(cfg, 90).standard_normal((H, T)).astype(np.float32)
+    Y = up(env, y_in.T)
+    tidx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    qg.moe_ffn(m, up(env, X.T), Y, tidx, tw)
+    torch.cuda.synchronize()
+    assert np.array_equal(tidx.cpu().numpy(), res["idx"]), (tidx.cpu().numpy(), res["idx"])
+    assert np.all(np.abs(tw.cpu().numpy() - res["p"]) <= 1e-5)
+    assert_tol(host(Y).T, res["y"], res["tol"], f"moe T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 3, 16])
+@pytest.mark.parametrize("shared", [True, False])
+def test_moe_small(env, T, shared):
+    say(f"moe small T={T} shared={shared}")
+    m, hw = _moe_build(env, E=16, H=256, F=128, k=4, seed=60 + T, shared=shared)
+    _moe_check(env, m, hw, T, 4, cfg=70 + T)
+
+
+def test_moe_unnormalized(env):
+    m, hw = _moe_build(env, E=12, H=256, F=128, k=3, seed=80, normalize=False)
+    _moe_check(env, m, hw, 5, 3, cfg=81, normalize=False)
+
+
+def test_moe_repeat_bitwise(env):
+    torch, qg, dev = env
+    m, hw = _moe_build(env, E=16, H=256, F=128, k=4, seed=90)
+    X = up(env, synth.gen_x(256, 16, cfg_id=91).T)
+    Y0 = torch.zeros((16, 256), device=dev)
+    qg.moe_ffn(m, X, Y0)
+    for _ in range(3):
+        Y = torch.zeros((16, 256), device=dev)
+        qg.moe_ffn(m, X, Y)
+        assert torch.equal(Y, Y0)
