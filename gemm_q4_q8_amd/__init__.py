@@ -5,7 +5,7 @@ PyTorch supplies device memory and the current stream.  The functions carry
 the C-ABI names declared in include/qgemm.h; `lib` is the raw ctypes handle.
 
 Importing fails loudly when the built library is missing: there is no
-fallback.  Build it with `python -m gemm_q4_q8_amd.build`.
+fallback.  Build it with `python gemm_q4_q8_amd/build.py`.
 """
 from __future__ import annotations
 
@@ -24,7 +24,11 @@ STATUS = {0: "QG_OK", -1: "QG_EINVAL", -2: "QG_ESHAPE", -3: "QG_EALIGN",
           -4: "QG_EUNSUPPORTED", -5: "QG_EWORKSPACE", -6: "QG_EHIP"}
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built (python -m gemm_q4_q8_amd.build)")
+    raise ImportError(f"{LIB_PATH} is not built (python gemm_q4_q8_amd/build.py)")
+# torch ships its own HIP runtime.  Load it first so that the library binds to
+# the same runtime instance: streams and events are runtime objects, and a
+# second runtime in the process would not know torch's streams.
+import torch  # noqa: E402,F401
 lib = ctypes.CDLL(LIB_PATH)
 
 _i32, _i64, _sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
@@ -46,6 +50,7 @@ class qg_moe(ctypes.Structure):
 
 _SIGS = {
     "qg_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "qg_last_hip_error": (ctypes.c_char_p, []),
     "qg_packed_bytes": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64,
                                        ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
     "qg_repack": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
@@ -75,7 +80,10 @@ for _name, (_res, _args) in _SIGS.items():
 
 class QGError(RuntimeError):
     def __init__(self, status: int, what: str):
-        super().__init__(f"{what}: {STATUS.get(status, status)} ({lib.qg_strerror(status).decode()})")
+        msg = f"{what}: {STATUS.get(status, status)} ({lib.qg_strerror(status).decode()})"
+        if status == -6:
+            msg += f" [{lib.qg_last_hip_error().decode()}]"
+        super().__init__(msg)
         self.status = status
 
 
@@ -153,8 +161,13 @@ def qg_repack(qtype: int, blocks, rows: int, cols: int, n_mat: int = 1) -> QMatr
 
 def _ld(t) -> int:
     """Leading dimension of a column-major [len, ncols] matrix stored as a
-    row-major torch tensor of shape [ncols, len] (column j = t[j])."""
-    return t.stride(0) if t.dim() == 2 else t.shape[-1]
+    row-major torch tensor of shape [ncols, len] (column j = t[j]).  The stride
+    of a size-1 leading axis is meaningless, so a single column gets len."""
+    if t.dim() == 1:
+        return t.shape[0]
+    if t.stride(1) != 1:
+        raise ValueError("columns must be contiguous (stride 1 along the last axis)")
+    return t.shape[1] if t.shape[0] == 1 else t.stride(0)
 
 
 def qgemv(w: QMatrix, X, Y=None, accumulate: bool = False):

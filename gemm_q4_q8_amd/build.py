@@ -1,6 +1,6 @@
 """Build libqgemm.so (gfx950) in-tree with hipcc.
 
-    python -m gemm_q4_q8_amd.build        # or gemm_q4_q8_amd.build.build()
+    python gemm_q4_q8_amd/build.py        # run by path: the package import needs the library
 
 Every HIP translation unit is compiled with packed-FP32 instructions
 disabled; the host pass warns that it does not know that feature, which is

@@ -1,12 +1,20 @@
 // C-ABI entry points of libqgemm: argument checks (host only, before any HIP
 // call) and dispatch to the kernel launchers.  What each call computes is
 // stated, with its sources, in include/qgemm.h.
+#include <stdio.h>
 #include <string.h>
 
 #include "internal.h"
 #include "qgemm.h"
 
 using namespace qg;
+
+namespace qg {
+static thread_local char g_last_hip[256] = "no HIP error recorded";
+void record_hip_error(hipError_t e) {
+  snprintf(g_last_hip, sizeof(g_last_hip), "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+}
+}  // namespace qg
 
 namespace {
 
@@ -99,6 +107,8 @@ const char *qg_strerror(int status) {
   }
   return "unknown status";
 }
+
+const char *qg_last_hip_error(void) { return qg::g_last_hip; }
 
 int qg_packed_bytes(int qtype, int64_t n_mat, int64_t rows, int64_t cols, size_t *qs_bytes,
                     size_t *d_bytes) {

@@ -59,4 +59,16 @@ struct MoeCall {
 size_t moe_ws_bytes(const qg_moe *m, int ntok);
 int launch_moe(const MoeCall &c);
 
+// Launch bookkeeping: clear errors left by earlier calls of other code on
+// this thread, then turn the launch result into a status and remember the
+// HIP error text for qg_last_hip_error().
+void record_hip_error(hipError_t e);
+inline void clear_hip_error() { (void)hipGetLastError(); }
+inline int launch_status() {
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) return 0;
+  record_hip_error(e);
+  return -6;  // QG_EHIP
+}
+
 }  // namespace qg

@@ -391,8 +391,9 @@ template <int QT, int NCM>
 static int launch_moe_t(const MoeCall &c, MoeArgs &a) {
   const int ntc = NCM;
   const unsigned rgrid = (unsigned)((a.E + MW * EPW - 1) / (MW * EPW));
+  clear_hip_error();
   hipLaunchKernelGGL(moe_router_kernel<ntc>, dim3(rgrid), dim3(MTHR), 0, c.stream, a);
-  if (hipGetLastError() != hipSuccess) return QG_EHIP;
+  if (launch_status() != QG_OK) return QG_EHIP;
 
   const int T = a.T;
   size_t x_gu = (size_t)(a.H / 128) * 4 * T * 64;
@@ -409,8 +410,9 @@ static int launch_moe_t(const MoeCall &c, MoeArgs &a) {
     }
     if (lds_gu > 163840) return QG_EUNSUPPORTED;
   }
+  clear_hip_error();
   hipLaunchKernelGGL(kg, dim3(ggrid), dim3(MTHR), lds_gu, c.stream, a);
-  if (hipGetLastError() != hipSuccess) return QG_EHIP;
+  if (launch_status() != QG_OK) return QG_EHIP;
 
   size_t x_dn = (size_t)(a.Fmax / 128) * 4 * T * 64;
   size_t r_dn = (size_t)MW * 1 * RT_DN * 16 * T * 4;
@@ -426,8 +428,9 @@ static int launch_moe_t(const MoeCall &c, MoeArgs &a) {
     }
     if (lds_dn > 163840) return QG_EUNSUPPORTED;
   }
+  clear_hip_error();
   hipLaunchKernelGGL(kd, dim3(dgrid), dim3(MTHR), lds_dn, c.stream, a);
-  return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
+  return launch_status();
 }
 
 template <int QT>

@@ -445,8 +445,9 @@ static int launch_t(const QmvCall &c) {
     if (lds > 163840) return QG_EUNSUPPORTED;
   }
   const int64_t grid = a.per_xcd * 8;
+  clear_hip_error();
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NTHR), lds, c.stream, a);
-  return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
+  return launch_status();
 }
 
 template <int QT, int EPI>

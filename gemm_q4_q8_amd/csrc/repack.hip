@@ -120,11 +120,12 @@ int launch_repack(int qtype, int64_t n_mat, int64_t rows, int64_t cols, const vo
   const int64_t n = a.chunks > a.dslots ? a.chunks : a.dslots;
   const int64_t grid = (n + 255) / 256;
   if (grid > 0x7fffffff) return QG_EUNSUPPORTED;
+  clear_hip_error();
   if (qtype == QG_Q4_0)
     hipLaunchKernelGGL(repack_kernel<Q4>, dim3((unsigned)grid), dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL(repack_kernel<Q8>, dim3((unsigned)grid), dim3(256), 0, stream, a);
-  return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
+  return launch_status();
 }
 
 }  // namespace qg

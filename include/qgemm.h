@@ -25,8 +25,9 @@
  *   - A matrix W has `rows` outputs and `cols` inputs; cols % 32 == 0.
  *     Row r of the GGUF tensor is cols/32 consecutive blocks.
  *   - Activations are f32 column-major: column j of X starts at X + j*ldx.
- *     X, Y and H must be 16-byte aligned and ldx, ldy, ldh multiples of 4
- *     (whole 16-byte vectors); ldx >= cols, ldy >= rows.
+ *     X (and x) must be 16-byte aligned with ldx a multiple of 4 (columns are
+ *     read as whole 16-byte vectors); Y and H need 4-byte alignment only;
+ *     ldx >= cols, ldy >= rows.
  *   - Arithmetic: weights are dequantised exactly in registers; activations
  *     enter the products rounded to f16 (round to nearest even, relative
  *     error <= 2^-11); every sum and the scale multiply are f32.  Nothing is
@@ -40,7 +41,8 @@
  *     produced without a GPU.  Nothing throws across the ABI.
  *   - Memory is owned by the caller.  The library allocates nothing.
  *   - Workspace (`ws`, `ws_bytes`): device memory sized by the matching
- *     *_ws_bytes query.  It must be zero-filled before its first use; every
+ *     *_ws_bytes query, 256-byte aligned.  It must be zero-filled before its
+ *     first use; every
  *     call that completes leaves it zero-filled again (its counters reset
  *     themselves).  One workspace must not be used by two calls that may
  *     overlap in time (different streams): they would race.
@@ -70,6 +72,10 @@ enum {
 
 /* Text for a status code (static storage). */
 const char *qg_strerror(int status);
+
+/* Name and text of the last HIP error behind a QG_EHIP on the calling
+ * thread (thread-local storage, valid until the next failing call). */
+const char *qg_last_hip_error(void);
 
 /* ------------------------------------------------------------------------
  * Load-time repack  [ARCH Memory and caching; ENG Reading weights]
