@@ -90,22 +90,28 @@ __device__ __forceinline__ uint32_t ld_agent_u32(const uint32_t *p) {
   return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// "Last one in" for a group of `target` workgroups sharing a counter: every
-// workgroup publishes its stores, then increments; the workgroup that sees
-// target - 1 is last, resets the counter to zero for the next call, and
-// acquires everything the others published.  `flag` is an LDS word.
+// "Last one in" for a group of `target` workgroups sharing a counter.
+// Everything workgroups exchange goes through agent-scope atomic stores and
+// loads (st_agent / ld_agent above), which are coherent across the XCDs'
+// L2 caches by themselves.  So no cache-wide fence is needed (on gfx950 a
+// device-scope fence writes back and invalidates a whole L2): each thread
+// waits until its own stores are acknowledged, the workgroup increments the
+// counter with a relaxed agent-scope atomic, and the workgroup that sees
+// target - 1 is last.  It resets the counter to zero for the next call.  Its
+// later ld_agent loads are issued only after the counter returned.
+// `flag` is an LDS word.
 __device__ __forceinline__ bool arrive_last(uint32_t *cnt, uint32_t target, uint32_t *flag) {
-  __threadfence();
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t old = atomicAdd(cnt, 1u);
-    uint32_t last = (old == target - 1) ? 1u : 0u;
-    if (last) atomicExch(cnt, 0u);
+    const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t last = (old == target - 1) ? 1u : 0u;
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *flag = last;
   }
   __syncthreads();
-  bool last = *flag != 0;
-  if (last) __threadfence();
+  const bool last = *flag != 0;
+  __asm__ volatile("" ::: "memory");
   return last;
 }
 
