@@ -31,17 +31,36 @@ template <> struct QTraits<Q8> { static constexpr int tile_bytes = 2048; static 
 
 __device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 
-// Q4_0: one u32 word of the tiled layout = 8 nibbles of one block slice.
-// OR-ing a nibble into the mantissa of f16 1024.0 (0x6400) gives 1024 + n
-// exactly; subtracting 1032 leaves n - 8 exactly (integers below 2048 are
-// exact in f16).  Pair u holds columns (2u, 2u + 1) of the slice.
-__device__ __forceinline__ void unpack_q4(uint32_t w, h2 out[4]) {
-  const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
-  out[0] = as_h2((w & 0x000F000Fu) | 0x64006400u) - bias;
-  out[1] = as_h2(((w >> 4) & 0x000F000Fu) | 0x64006400u) - bias;
-  out[2] = as_h2(((w >> 8) & 0x000F000Fu) | 0x64006400u) - bias;
-  out[3] = as_h2(((w >> 12) & 0x000F000Fu) | 0x64006400u) - bias;
+// (w & mask) | bits in one VALU op.  gfx950 VOP3 encodings take no literal
+// constants and one scalar operand, so the mask rides in an SGPR and the OR
+// pattern in a VGPR (the compiler would otherwise split the op in two).
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t bits) {
+  uint32_t r;
+  __asm__("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(mask), "v"(bits));
+  return r;
 }
+
+// Q4_0: one u32 word of the tiled layout = 8 nibbles of one block slice;
+// pair u holds columns (2u, 2u + 1) at bits (4u, 16 + 4u).  A nibble n at
+// bits 0..3 of a 16-bit half, under the f16 pattern 0x6400 (1024.0, ulp 1),
+// reads as 1024 + n; a nibble at bits 4..7 under 0x5400 (64.0, ulp 1/16)
+// reads as 64 + n.  Both are exact, and subtracting 1032 or 72 leaves the
+// weight n - 8 exactly.  One shift by 8 brings pairs 2 and 3 into place.
+__device__ __forceinline__ void unpack_q4(uint32_t w, h2 out[4]) {
+  const h2 b_lo = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const h2 b_hi = {(_Float16)72.0f, (_Float16)72.0f};
+  const uint32_t w8 = w >> 8;
+  out[0] = as_h2(and_or(w, 0x000F000Fu, 0x64006400u)) - b_lo;
+  out[1] = as_h2(and_or(w, 0x00F000F0u, 0x54005400u)) - b_hi;
+  out[2] = as_h2(and_or(w8, 0x000F000Fu, 0x64006400u)) - b_lo;
+  out[3] = as_h2(and_or(w8, 0x00F000F0u, 0x54005400u)) - b_hi;
+}
+
+// Streaming loads of weights and scales: each byte is read once per call,
+// so they bypass cache allocation (nontemporal) and leave L2 to the
+// activations and partial sums.
+__device__ __forceinline__ u4 ld_stream(const uint8_t *p) { return __builtin_nontemporal_load((const u4 *)p); }
+__device__ __forceinline__ u2 ld_stream2(const uint8_t *p) { return __builtin_nontemporal_load((const u2 *)p); }
 
 // Q8_0: two u32 words = 8 biased bytes (q + 128) of one block slice.  A byte
 // permute puts each byte under a 0x64 high byte (1024 + b, exact), then

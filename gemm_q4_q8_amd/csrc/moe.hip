@@ -294,9 +294,9 @@ __global__ void __launch_bounds__(MTHR) moe_expert_kernel(MoeArgs a) {
       for (int t = 0; t < RT; ++t) {
         const int64_t tile = (rt_base + t) * KT + kt;
         const uint8_t *tp = (m ? q1 : q0) + tile * TB + lane * 16;
-        wq[m][t][0] = *(const u4 *)tp;
-        if constexpr (QW == 2) wq[m][t][QW - 1] = *(const u4 *)(tp + 1024);
-        wdd[m][t] = *(const u2 *)((m ? d1 : d0) + tile * TILE_D_BYTES + r * 8);
+        wq[m][t][0] = ld_stream(tp);
+        if constexpr (QW == 2) wq[m][t][QW - 1] = ld_stream(tp + 1024);
+        wdd[m][t] = ld_stream2((m ? d1 : d0) + tile * TILE_D_BYTES + r * 8);
       }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

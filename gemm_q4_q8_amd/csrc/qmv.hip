@@ -10,9 +10,10 @@
 //
 // How it maps to MI355X:
 //  * A workgroup of 4 waves owns RT row tiles (16 rows each) and a K range;
-//    the four waves take interleaved 128-column tile columns of that range.
-//    Each lane streams one 16-byte chunk per tile (a whole wave reads a
-//    contiguous 1 KiB stripe), so every HBM read is fully coalesced.
+//    each wave streams a contiguous quarter of that range, PF tile columns
+//    ahead, with nontemporal loads.  Each lane reads one 16-byte chunk per
+//    tile (a whole wave reads a contiguous 1 KiB stripe), so every HBM read
+//    is fully coalesced.
 //  * The K range of the activations is staged once in LDS as f16, laid out
 //    [block][column][32]; lanes of a row group read it with broadcast.
 //  * Dot path (1..8 columns): weights become exact f16 pairs (two ALU ops per
@@ -21,7 +22,8 @@
 //  * Matrix-core path (16 columns): one v_mfma_f32_16x16x32_f16 per block
 //    and row tile, A = activations (16 columns x 32), B = the block's
 //    weights; the block scale multiplies the 4 outputs each lane holds.
-//  * Reduction order is fixed: lane chunk order, a 2-step lane butterfly,
+//  * Reduction order is fixed: tile columns in order within a wave, a 2-step
+//    lane butterfly,
 //    waves in index order, then K splits in index order (the last-arriving
 //    workgroup sums all splits).  It depends on the shape only.
 #include "common.h"
@@ -32,6 +34,7 @@ namespace qg {
 
 constexpr int WK = 4;            // waves per workgroup (split of the K range)
 constexpr int NTHR = WK * 64;
+constexpr int PF = 2;            // tile columns in flight per wave
 
 struct QmvArgs {
   const uint8_t *qs0, *qs1, *d0, *d1;
@@ -57,9 +60,12 @@ struct QmvArgs {
   float *out_val;
 };
 
+// Row tiles per wave on the dot path: at most 16 accumulators per lane
+// ("Engine and kernels", verify twins keep 16 accumulators per thread), and
+// at most 4 tiles of weights in flight per tile column.
 template <int NC, int NMAT>
 constexpr int rt_dot() {
-  return (16 / (NC * NMAT)) < 1 ? 1 : ((16 / (NC * NMAT)) > 4 ? 4 : 16 / (NC * NMAT));
+  return (16 / (NC * NMAT)) < 1 ? 1 : ((16 / (NC * NMAT)) > 4 / NMAT ? 4 / NMAT : 16 / (NC * NMAT));
 }
 constexpr int RT_MFMA = 4;
 
@@ -99,7 +105,38 @@ __global__ void __launch_bounds__(NTHR) qmv_kernel(QmvArgs a) {
   float *red = (float *)smem;
   float *vals = (float *)(smem + red_offset<NC, NMAT, RT>(a.nkt_max));
 
-  // ---- 1. activations of this K range -> LDS, f16, [block][column][32]
+  const int r = lane & 15, sl = lane >> 4;
+  const int64_t rt_base = (int64_t)g * RT;
+
+  // ---- 1. start the weight stream: PF tile columns in flight per wave.
+  // Row tiles past the matrix (last row group) re-read the last row tile;
+  // their results are never written.
+  u4 wq[PF][NMAT][RT][QW];
+  u2 wd[PF][NMAT][RT];
+  auto load = [&](int slot, int kt) {
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+      const uint8_t *qsm = m ? a.qs1 : a.qs0;
+      const uint8_t *dsm = m ? a.d1 : a.d0;
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const int64_t trow = (rt_base + t < a.NT) ? rt_base + t : (int64_t)a.NT - 1;
+        const int64_t tile = trow * a.KT + kt;
+        const uint8_t *tp = qsm + tile * TB + lane * 16;
+        wq[slot][m][t][0] = ld_stream(tp);
+        if constexpr (QW == 2) wq[slot][m][t][QW - 1] = ld_stream(tp + 1024);
+        wd[slot][m][t] = ld_stream2(dsm + tile * TILE_D_BYTES + r * 8);
+      }
+    }
+  };
+  // wave wk streams the contiguous tile columns [wb, we) of the range
+  const int wb = kt0 + (int)((int64_t)nkt * wk / WK);
+  const int we = kt0 + (int)((int64_t)nkt * (wk + 1) / WK);
+#pragma unroll
+  for (int p = 0; p < PF; ++p)
+    if (wb + p < we) load(p, wb + p);
+
+  // ---- 2. activations of this K range -> LDS, f16, [block][column][32]
   {
     const int nvec = nkt * TILE_BLOCKS * NC * 4;
     for (int v = tid; v < nvec; v += NTHR) {
@@ -115,9 +152,7 @@ __global__ void __launch_bounds__(NTHR) qmv_kernel(QmvArgs a) {
   }
   __syncthreads();
 
-  // ---- 2. stream the weight tiles
-  const int r = lane & 15, sl = lane >> 4;
-  const int64_t rt_base = (int64_t)g * RT;
+  // ---- 3. stream the weight tiles
   float acc[NMAT][RT][NACC];
 #pragma unroll
   for (int m = 0; m < NMAT; ++m)
@@ -126,33 +161,7 @@ __global__ void __launch_bounds__(NTHR) qmv_kernel(QmvArgs a) {
 #pragma unroll
       for (int c = 0; c < NACC; ++c) acc[m][t][c] = 0.0f;
 
-  u4 cq[NMAT][RT][QW];
-  u2 cd[NMAT][RT];
-
-  auto load = [&](int kt, u4 (&q)[NMAT][RT][QW], u2 (&dd)[NMAT][RT]) {
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
-      const uint8_t *qsm = m ? a.qs1 : a.qs0;
-      const uint8_t *dsm = m ? a.d1 : a.d0;
-#pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        const int64_t trow = rt_base + t;
-        if (trow < a.NT) {
-          const int64_t tile = trow * a.KT + kt;
-          const uint8_t *tp = qsm + tile * TB + lane * 16;
-          q[m][t][0] = *(const u4 *)tp;
-          if constexpr (QW == 2) q[m][t][QW - 1] = *(const u4 *)(tp + 1024);
-          dd[m][t] = *(const u2 *)(dsm + tile * TILE_D_BYTES + r * 8);
-        } else {
-#pragma unroll
-          for (int h = 0; h < QW; ++h) q[m][t][h] = u4{0, 0, 0, 0};
-          dd[m][t] = u2{0, 0};
-        }
-      }
-    }
-  };
-
-  auto compute = [&](int kt, const u4 (&q)[NMAT][RT][QW], const u2 (&dd)[NMAT][RT]) {
+  auto compute = [&](int slot, int kt) {
     const int bl0 = (kt - kt0) * TILE_BLOCKS;
 #pragma unroll
     for (int j = 0; j < TILE_BLOCKS; ++j) {
@@ -161,11 +170,11 @@ __global__ void __launch_bounds__(NTHR) qmv_kernel(QmvArgs a) {
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
           h2 w[4];
-          if constexpr (QT == Q4) unpack_q4(q[0][t][0][j], w);
-          else unpack_q8(q[0][t][j >> 1][(j & 1) * 2], q[0][t][j >> 1][(j & 1) * 2 + 1], w);
+          if constexpr (QT == Q4) unpack_q4(wq[slot][0][t][0][j], w);
+          else unpack_q8(wq[slot][0][t][j >> 1][(j & 1) * 2], wq[slot][0][t][j >> 1][(j & 1) * 2 + 1], w);
           h8 B = {w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
           const f4 D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          const float dj = scale_of(dd[0][t], j);
+          const float dj = scale_of(wd[slot][0][t], j);
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[0][t][i] = __builtin_fmaf(dj, D[i], acc[0][t][i]);
         }
@@ -182,9 +191,9 @@ __global__ void __launch_bounds__(NTHR) qmv_kernel(QmvArgs a) {
 #pragma unroll
           for (int t = 0; t < RT; ++t) {
             h2 w[4];
-            if constexpr (QT == Q4) unpack_q4(q[m][t][0][j], w);
-            else unpack_q8(q[m][t][j >> 1][(j & 1) * 2], q[m][t][j >> 1][(j & 1) * 2 + 1], w);
-            const float dj = scale_of(dd[m][t], j);
+            if constexpr (QT == Q4) unpack_q4(wq[slot][m][t][0][j], w);
+            else unpack_q8(wq[slot][m][t][j >> 1][(j & 1) * 2], wq[slot][m][t][j >> 1][(j & 1) * 2 + 1], w);
+            const float dj = scale_of(wd[slot][m][t], j);
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
               float p = __builtin_amdgcn_fdot2(w[0], xv[c][0], 0.0f, false);
@@ -198,27 +207,18 @@ __global__ void __launch_bounds__(NTHR) qmv_kernel(QmvArgs a) {
     }
   };
 
-  int kt = kt0 + wk;
-  if (kt < kt1) load(kt, cq, cd);
-  for (; kt < kt1; kt += WK) {
-    u4 nq[NMAT][RT][QW];
-    u2 nd[NMAT][RT];
-    const int ktn = kt + WK;
-    if (ktn < kt1) load(ktn, nq, nd);
-    compute(kt, cq, cd);
-    if (ktn < kt1) {
+  for (int kt = wb; kt < we; kt += PF) {
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int t = 0; t < RT; ++t) {
-#pragma unroll
-          for (int h = 0; h < QW; ++h) cq[m][t][h] = nq[m][t][h];
-          cd[m][t] = nd[m][t];
-        }
+    for (int p = 0; p < PF; ++p) {
+      const int ktc = kt + p;
+      if (ktc < we) {
+        compute(p, ktc);
+        if (ktc + PF < we) load(p, ktc + PF);
+      }
     }
   }
 
-  // ---- 3. reduce inside the workgroup (fixed order)
+  // ---- 4. reduce inside the workgroup (fixed order)
   __syncthreads();  // every wave is done with the staged activations
   if constexpr (MFMA) {
 #pragma unroll
@@ -312,7 +312,7 @@ __global__ void __launch_bounds__(NTHR) qmv_kernel(QmvArgs a) {
   }
 
   if constexpr (EPI == EPI_ARGMAX) {
-    // ---- 4. argmax of this row group, then of all row groups
+    // ---- 5. argmax of this row group, then of all row groups
     __syncthreads();
     if (wk == 0) {
       float bv = __builtin_nanf("");
