@@ -66,9 +66,9 @@ int qmv_common(int qtype, const void *qs, const void *d, int64_t rows, int64_t c
   if ((st = check_act(X, ldx, cols, ncols))) return st;
   if ((st = check_out(Y, ldy, rows))) return st;
   if (overlap(span(X, ldx, cols, ncols), span(Y, ldy, rows, ncols))) return QG_EINVAL;
-  const int S = gemm16 ? gemm16_splits(rows, cols) : gemv_splits(rows, cols);
+  const int slots = gemm16 ? gemm16_splits(rows, cols) : gemv_segments(rows, cols);
   if (!ws) return QG_EWORKSPACE;
-  if (ws_bytes < qmv_ws_bytes(rows, cols, S, 1, gemm16 ? 16 : 8, false)) return QG_EWORKSPACE;
+  if (ws_bytes < qmv_ws_bytes(rows, cols, slots, 1, gemm16 ? 16 : 8, false)) return QG_EWORKSPACE;
   if (!aligned(ws, 256)) return QG_EALIGN;
   QmvCall c;
   memset(&c, 0, sizeof(c));
@@ -138,12 +138,12 @@ int qg_repack(int qtype, int64_t n_mat, int64_t rows, int64_t cols, const void *
 
 size_t qg_gemv_ws_bytes(int64_t rows, int64_t cols) {
   if (rows <= 0 || cols <= 0 || cols % 32) return 0;
-  return qmv_ws_bytes(rows, cols, gemv_splits(rows, cols), 1, 8, false);
+  return qmv_ws_bytes(rows, cols, gemv_segments(rows, cols), 1, 8, false);
 }
 
 size_t qg_gateup_ws_bytes(int64_t rows, int64_t cols) {
   if (rows <= 0 || cols <= 0 || cols % 32) return 0;
-  return qmv_ws_bytes(rows, cols, gemv_splits(rows, cols), 2, 8, false);
+  return qmv_ws_bytes(rows, cols, gemv_segments(rows, cols), 2, 8, false);
 }
 
 size_t qg_gemm16_ws_bytes(int qtype, int64_t rows, int64_t cols) {
@@ -153,7 +153,7 @@ size_t qg_gemm16_ws_bytes(int qtype, int64_t rows, int64_t cols) {
 
 size_t qg_lmhead_ws_bytes(int64_t rows, int64_t cols) {
   if (rows <= 0 || cols <= 0 || cols % 32) return 0;
-  return qmv_ws_bytes(rows, cols, gemv_splits(rows, cols), 1, 1, true);
+  return qmv_ws_bytes(rows, cols, gemv_segments(rows, cols), 1, 1, true);
 }
 
 int qgemv_q4_0(const void *qs, const void *d, int64_t rows, int64_t cols, const float *X, int64_t ldx,

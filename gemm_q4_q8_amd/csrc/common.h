@@ -46,14 +46,36 @@ __device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t b
 // reads as 1024 + n; a nibble at bits 4..7 under 0x5400 (64.0, ulp 1/16)
 // reads as 64 + n.  Both are exact, and subtracting 1032 or 72 leaves the
 // weight n - 8 exactly.  One shift by 8 brings pairs 2 and 3 into place.
-__device__ __forceinline__ void unpack_q4(uint32_t w, h2 out[4]) {
+// The two OR patterns live in VGPRs for the whole kernel: `Q4Magic` is made
+// once by an opaque move, so the compiler keeps it instead of re-creating
+// the constants before every use.
+struct Q4Magic {
+  uint32_t lo, hi;  // 0x64006400, 0x54005400
+};
+__device__ __forceinline__ Q4Magic q4_magic() {
+  Q4Magic m;
+  __asm__ volatile("v_mov_b32 %0, 0x64006400" : "=v"(m.lo));
+  __asm__ volatile("v_mov_b32 %0, 0x54005400" : "=v"(m.hi));
+  return m;
+}
+
+__device__ __forceinline__ void unpack_q4(uint32_t w, h2 out[4], Q4Magic mg) {
   const h2 b_lo = {(_Float16)1032.0f, (_Float16)1032.0f};
   const h2 b_hi = {(_Float16)72.0f, (_Float16)72.0f};
   const uint32_t w8 = w >> 8;
-  out[0] = as_h2(and_or(w, 0x000F000Fu, 0x64006400u)) - b_lo;
-  out[1] = as_h2(and_or(w, 0x00F000F0u, 0x54005400u)) - b_hi;
-  out[2] = as_h2(and_or(w8, 0x000F000Fu, 0x64006400u)) - b_lo;
-  out[3] = as_h2(and_or(w8, 0x00F000F0u, 0x54005400u)) - b_hi;
+  out[0] = as_h2(and_or(w, 0x000F000Fu, mg.lo)) - b_lo;
+  out[1] = as_h2(and_or(w, 0x00F000F0u, mg.hi)) - b_hi;
+  out[2] = as_h2(and_or(w8, 0x000F000Fu, mg.lo)) - b_lo;
+  out[3] = as_h2(and_or(w8, 0x00F000F0u, mg.hi)) - b_hi;
+}
+
+// The dot product of a weight pair and an activation pair, starting a new
+// sum (v_dot2_f32_f16 with an inline zero accumulator; the accumulating
+// v_dot2c form would need a register cleared first).
+__device__ __forceinline__ float dot2_first(h2 a, h2 b) {
+  float r;
+  __asm__("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 
 // Streaming loads of weights and scales: each byte is read once per call,

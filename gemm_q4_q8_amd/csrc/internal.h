@@ -32,12 +32,14 @@ struct QmvCall {
   hipStream_t stream;
 };
 
-// Split-K factor: a function of the matrix shape only, so that every column
-// count gives the same per-row reduction order.
-int gemv_splits(int64_t rows, int64_t cols);
+// K segments of the dot path: a function of the matrix shape only, so that
+// every column count gives the same per-row reduction order.
+int gemv_segments(int64_t rows, int64_t cols);
+// K splits of the 16-column matrix-core path.
 int gemm16_splits(int64_t rows, int64_t cols);
 
-size_t qmv_ws_bytes(int64_t rows, int64_t cols, int splits, int nmat, int ncols_max, bool argmax);
+// Workspace: counters, argmax candidates, and `slots` partial sums per output.
+size_t qmv_ws_bytes(int64_t rows, int64_t cols, int slots, int nmat, int ncols_max, bool argmax);
 
 int launch_qmv(const QmvCall &c);  // returns 0 or a QG_ status
 int launch_repack(int qtype, int64_t n_mat, int64_t rows, int64_t cols, const void *blocks,

@@ -285,6 +285,7 @@ __global__ void __launch_bounds__(MTHR) moe_expert_kernel(MoeArgs a) {
 #pragma unroll
       for (int c = 0; c < NCM; ++c) acc[m][t][c] = 0.0f;
 
+  const Q4Magic mg = q4_magic();
   for (int kt = wk; kt < KT; kt += MW) {
     u4 wq[NMAT][RT][QW];
     u2 wdd[NMAT][RT];
@@ -314,13 +315,13 @@ __global__ void __launch_bounds__(MTHR) moe_expert_kernel(MoeArgs a) {
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
           h2 w[4];
-          if constexpr (QT == Q4) unpack_q4(wq[m][t][0][j], w);
+          if constexpr (QT == Q4) unpack_q4(wq[m][t][0][j], w, mg);
           else unpack_q8(wq[m][t][j >> 1][(j & 1) * 2], wq[m][t][j >> 1][(j & 1) * 2 + 1], w);
           const float dj = scale_of(wdd[m][t], j);
 #pragma unroll
           for (int c = 0; c < NCM; ++c) {
             if (c < nc) {
-              float p = __builtin_amdgcn_fdot2(w[0], xv[c][0], 0.0f, false);
+              float p = dot2_first(w[0], xv[c][0]);
               p = __builtin_amdgcn_fdot2(w[1], xv[c][1], p, false);
               p = __builtin_amdgcn_fdot2(w[2], xv[c][2], p, false);
               p = __builtin_amdgcn_fdot2(w[3], xv[c][3], p, false);
@@ -401,14 +402,17 @@ static int launch_moe_t(const MoeCall &c, MoeArgs &a) {
   size_t lds_gu = x_gu > r_gu ? x_gu : r_gu;
   const unsigned ggrid = (unsigned)(a.sh_gu_units + (int64_t)a.Umax * a.gu_groups);
   auto kg = moe_expert_kernel<QT, NCM, 2, RT_GU>;
+  if (lds_gu > 163840 - 1024) return QG_EUNSUPPORTED;
   if (lds_gu > 65536) {
-    static bool granted = false;
-    if (!granted) {
-      if (hipFuncSetAttribute((const void *)kg, hipFuncAttributeMaxDynamicSharedMemorySize, 163840) != hipSuccess)
+    static size_t granted = 65536;
+    if (lds_gu > granted) {
+      const hipError_t e = hipFuncSetAttribute((const void *)kg, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_gu);
+      if (e != hipSuccess) {
+        record_hip_error(e);
         return QG_EHIP;
-      granted = true;
+      }
+      granted = lds_gu;
     }
-    if (lds_gu > 163840) return QG_EUNSUPPORTED;
   }
   clear_hip_error();
   hipLaunchKernelGGL(kg, dim3(ggrid), dim3(MTHR), lds_gu, c.stream, a);
@@ -419,14 +423,17 @@ static int launch_moe_t(const MoeCall &c, MoeArgs &a) {
   size_t lds_dn = x_dn > r_dn ? x_dn : r_dn;
   const unsigned dgrid = (unsigned)(a.sh_dn_units + (int64_t)a.Umax * a.dn_groups);
   auto kd = moe_expert_kernel<QT, NCM, 1, RT_DN>;
+  if (lds_dn > 163840 - 1024) return QG_EUNSUPPORTED;
   if (lds_dn > 65536) {
-    static bool granted = false;
-    if (!granted) {
-      if (hipFuncSetAttribute((const void *)kd, hipFuncAttributeMaxDynamicSharedMemorySize, 163840) != hipSuccess)
+    static size_t granted = 65536;
+    if (lds_dn > granted) {
+      const hipError_t e = hipFuncSetAttribute((const void *)kd, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dn);
+      if (e != hipSuccess) {
+        record_hip_error(e);
         return QG_EHIP;
-      granted = true;
+      }
+      granted = lds_dn;
     }
-    if (lds_dn > 163840) return QG_EUNSUPPORTED;
   }
   clear_hip_error();
   hipLaunchKernelGGL(kd, dim3(dgrid), dim3(MTHR), lds_dn, c.stream, a);
