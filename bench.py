@@ -225,6 +225,24 @@ def read_ceiling(B):
     return 2 * POOL_BYTES / t / 1e9
 
 
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gateup_silu_q4_0_decode_ffn_traffic.txt")
+    try:
+        fields = dict(l.split()[0:2] for l in open(path) if l.strip() and not l.startswith("#")
+                      and len(l.split()) == 2)
+    except OSError:
+        return None
+    h = hashlib.sha256()
+    for f in ("gemm_q4_q8_amd/csrc/qmv.hip", "gemm_q4_q8_amd/csrc/common.h"):
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if fields.get("kernel_source_hash") != h.hexdigest()[:16]:
+        return None
+    return int(float(fields["traffic_bytes_per_launch"]))
+
+
 def cpu_baseline(raws):
     """The oracle, as it stands, on one full decode-FFN step (2 repetitions)."""
     import synth
@@ -250,6 +268,32 @@ def cpu_baseline(raws):
                       f"{reps} repetitions, {dt:.2f} s per step; f64 numpy, BLAS threads={threads}"}
 
 
+def traffic_run(B):
+    """Fixed launches for hardware-counter runs (rocprofv3 --pmc FETCH_SIZE /
+    WRITE_SIZE): 5 element-wise copies of exactly 1 GiB (read 1 GiB, write
+    1 GiB) as the scale reference, then 16 fused gate/up launches of the
+    decode FFN shape over 8 address-distinct weight sets."""
+    torch, qg = B.torch, B.qg
+    a = torch.empty(POOL_BYTES // 4, dtype=torch.float32, device=B.dev).normal_()
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    del a, b
+    N, K = 17408, 5120
+    ws = [(B.matrix(2, N, K, seed=21 + i, sigma=0.02)[0], B.matrix(2, N, K, seed=41 + i, sigma=0.02)[0])
+          for i in range(8)]
+    import synth
+    x = B.up(synth.gen_x(K, 1, cfg_id=2).T)
+    h = torch.empty((1, N), dtype=torch.float32, device=B.dev)
+    torch.cuda.synchronize()
+    for i in range(16):
+        qg.gateup_silu(ws[i % 8][0], ws[i % 8][1], x, h)
+    torch.cuda.synchronize()
+    print("traffic run done", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -257,6 +301,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--suite", choices=["all", "main"], default="all")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--traffic", action="store_true",
+                    help="only the fixed launches used for HBM traffic counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -267,6 +313,9 @@ def main():
     import gemm_q4_q8_amd as qg
     dev = torch.device("cuda:0")
     B = Bench(torch, qg, dev)
+    if args.traffic:
+        traffic_run(B)
+        return
 
     log("bench: decode FFN step")
     step_bytes, t_step, gu_bytes, t_gu, dn_bytes, t_dn, raws = run_ffn(B, args.steps, args.warmup)
@@ -300,7 +349,8 @@ def main():
                    "copy_ceiling_GB_s": round(ceiling, 1)},
         "roofline": {"bound": "hbm", "kernel": "gateup_silu (Q4_0, 1 column)",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
+                     "bytes_per_launch": int(gu_bytes), "us_per_launch": round(t_gu * 1e6, 3)},
         "kernels": kernels,
     }
     if not args.no_cpu:
