@@ -111,8 +111,10 @@ _WS = {}
 
 
 def workspace(nbytes: int, device, key: str = "default"):
-    """A zero-filled device workspace (cached per device and key).  The
-    library leaves it zero-filled after every completed call."""
+    """A zero-filled device workspace (cached per device and key).  Its
+    leading counters are zero again after every completed call, so one
+    workspace serves any sequence of calls on one stream; a larger request
+    replaces it with a new zero-filled one."""
     torch = _torch()
     dev = torch.device(device)
     k = (dev.index, key)

@@ -39,6 +39,12 @@ int gemv_segments(int64_t rows, int64_t cols);
 int gemm16_splits(int64_t rows, int64_t cols);
 
 // Workspace: counters, argmax candidates, and `slots` partial sums per output.
+// Every workspace starts with WS_SYNC_WORDS counters shared by all entry
+// points.  They are zero between calls (each call's last workgroup resets
+// what it used), and no call ever writes anything else there, so one
+// workspace can serve calls of any shape in stream order.
+constexpr size_t WS_SYNC_WORDS = QG_WS_SYNC_BYTES / 4;
+
 size_t qmv_ws_bytes(int64_t rows, int64_t cols, int slots, int nmat, int ncols_max, bool argmax);
 
 int launch_qmv(const QmvCall &c);  // returns 0 or a QG_ status

@@ -62,9 +62,11 @@ static MoeLayout moe_layout(const qg_moe *m, int T) {
   const int64_t Fmax = m->sh_ffn > m->ffn ? m->sh_ffn : m->ffn;
   const int64_t umax = (int64_t)m->n_expert < (int64_t)T * m->top_k ? m->n_expert : (int64_t)T * m->top_k;
   const int64_t slots = (int64_t)T * m->top_k + T;
-  size_t o = 0;
-  L.rcnt = o; o += 256;
-  L.dcnt = o; o += a256((size_t)(m->hidden / 16) * 4);
+  // counters (in the shared counter words): the router's, then one per
+  // down-projection row group; data after them
+  L.rcnt = 0;
+  L.dcnt = 4;
+  size_t o = QG_WS_SYNC_BYTES;
   L.nused = o; o += 256;
   L.logits = o; o += a256((size_t)T * m->n_expert * 4);
   L.sel = o; o += a256((size_t)T * m->top_k * 4);

@@ -446,8 +446,7 @@ int gemm16_splits(int64_t rows, int64_t cols) {
 size_t qmv_ws_bytes(int64_t rows, int64_t cols, int slots, int nmat, int ncols_max, bool argmax) {
   const int64_t NT = cdiv(rows, 16);
   (void)cols;
-  size_t b = align256((size_t)NT * 4);              // split counters
-  b += 256;                                         // argmax counter
+  size_t b = QG_WS_SYNC_BYTES;                      // counters
   if (argmax) b += 2 * align256((size_t)NT * 4);    // candidates
   if (slots > 1) b += (size_t)slots * nmat * NT * 16 * ncols_max * 4;
   return b;
@@ -483,11 +482,12 @@ static int launch_t(const QmvCall &c, int Q, int S) {
   a.ncols = c.ncols;
   a.Y = c.Y;
   a.ldy = c.ldy;
+  // counters: word 0 for the argmax, words 1..G for the row groups
+  if (S > 1 && (size_t)a.G + 1 > WS_SYNC_WORDS) return QG_EUNSUPPORTED;
   uint8_t *ws = (uint8_t *)c.ws;
-  a.cnt = (uint32_t *)ws;
-  size_t off = align256((size_t)NT * 4);
-  a.gcnt = (uint32_t *)(ws + off);
-  off += 256;
+  a.gcnt = (uint32_t *)ws;
+  a.cnt = (uint32_t *)ws + 1;
+  size_t off = QG_WS_SYNC_BYTES;
   a.cand_v = nullptr;
   a.cand_i = nullptr;
   if (EPI == EPI_ARGMAX) {

@@ -41,11 +41,14 @@
  *     produced without a GPU.  Nothing throws across the ABI.
  *   - Memory is owned by the caller.  The library allocates nothing.
  *   - Workspace (`ws`, `ws_bytes`): device memory sized by the matching
- *     *_ws_bytes query, 256-byte aligned.  It must be zero-filled before its
- *     first use; every
- *     call that completes leaves it zero-filled again (its counters reset
- *     themselves).  One workspace must not be used by two calls that may
- *     overlap in time (different streams): they would race.
+ *     *_ws_bytes query, 256-byte aligned.  Its first QG_WS_SYNC_BYTES bytes
+ *     are counters through which workgroups of one call find the last of
+ *     them to finish: they must be zero before the first call, and every
+ *     call that completes leaves them zero again.  The rest is scratch that
+ *     each call writes before reading.  So one workspace (as large as the
+ *     largest query) may serve any sequence of calls, of any entry point and
+ *     shape, issued in order on one stream.  Two calls that may overlap in
+ *     time (different streams) must not share a workspace: they would race.
  */
 #ifndef QGEMM_H
 #define QGEMM_H
@@ -56,6 +59,9 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* Bytes of counters at the start of every workspace (see Conventions). */
+#define QG_WS_SYNC_BYTES 262144u
 
 /* GGUF tensor type ids, so a GGUF reader can pass them through. */
 enum { QG_Q4_0 = 2, QG_Q8_0 = 8 };

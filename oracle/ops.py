@@ -195,6 +195,24 @@ def topk_certified(logits: np.ndarray, a: np.ndarray, k: int, k_terms: int,
 # Readings: shared expert ungated (weight 1); the result accumulates into
 # the residual y like the FFN down projection.
 # --------------------------------------------------------------------------
+def router_logits(x: np.ndarray, router: np.ndarray):
+    """Router scores l = R x (f32 router weights, [E, H]) for x [H] or [H, T],
+    and a = |R| |x|, the scale of their rounding error."""
+    x = np.asarray(x, dtype=np.float64)
+    if x.ndim == 1:
+        x = x[:, None]
+    R = np.asarray(router, dtype=np.float64)
+    return R @ x, np.abs(R) @ np.abs(x)
+
+
+def routing_certified(logits: np.ndarray, la: np.ndarray, top_k: int, hidden: int,
+                      order: bool = False) -> np.ndarray:
+    """Per token: is the selected set (and, with order=True, its order) forced
+    by the error bound of an f32 router product of `hidden` terms?"""
+    return np.array([topk_certified(logits[:, t], la[:, t], top_k, hidden + 2, order=order)
+                     for t in range(logits.shape[1])])
+
+
 def moe_ffn(x: np.ndarray, router: np.ndarray, qtype: int,
             gate_raw: np.ndarray, up_raw: np.ndarray, down_raw: np.ndarray,
             top_k: int, normalize: bool = True,
@@ -210,10 +228,7 @@ def moe_ffn(x: np.ndarray, router: np.ndarray, qtype: int,
     if x.ndim == 1:
         x = x[:, None]
     H, T = x.shape
-    E = router.shape[0]
-    R = np.asarray(router, dtype=np.float64)
-    logits = R @ x                              # [E, T]
-    la = np.abs(R) @ np.abs(x)
+    logits, la = router_logits(x, router)       # [E, T]
     gam = (H + 2) * U32 / (1 - (H + 2) * U32)
     y = np.zeros((H, T)) if y_in is None else np.asarray(y_in, dtype=np.float64).reshape(H, T).copy()
     tol = np.full((H, T), ABS_TOL)
@@ -248,9 +263,7 @@ def moe_ffn(x: np.ndarray, router: np.ndarray, qtype: int,
 
 
 def moe_routing_certified(res: dict, top_k: int, hidden: int) -> bool:
-    lg, la = res["logits"], res["logit_a"]
-    return all(topk_certified(lg[:, t], la[:, t], top_k, hidden + 2)
-               for t in range(lg.shape[1]))
+    return bool(np.all(routing_certified(res["logits"], res["logit_a"], top_k, hidden)))
 
 
 def silu_slope_bound_holds() -> bool:
@@ -267,5 +280,5 @@ def gamma(k: int) -> float:
 __all__ = [
     "gemv", "tol_dot", "silu", "gateup_silu", "down_tol", "argmax_first",
     "argmax_certified", "topk_lowest_index", "softmax", "topk_certified",
-    "moe_ffn", "moe_routing_certified", "gamma",
+    "router_logits", "routing_certified", "moe_ffn", "moe_routing_certified", "gamma",
 ]

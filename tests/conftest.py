@@ -12,6 +12,16 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
 
 
+@pytest.fixture(scope="session")
+def env():
+    """(torch, the library binding, cuda:0) for the GPU tests."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need an MI355X")
+    import gemm_q4_q8_amd as qg
+    return torch, qg, torch.device("cuda:0")
+
+
 def golden(name: str) -> dict:
     """Parse a tests/golden key = value fixture ('#' starts a comment)."""
     out = {}

@@ -63,6 +63,17 @@ def test_ws_queries():
     assert L.qg_lmhead_ws_bytes(248320, 5120) > 0
 
 
+def test_ws_queries_cover_the_counter_prefix():
+    # every workspace starts with the shared counters the header declares
+    hdr = open(os.path.join(ROOT, "include", "qgemm.h")).read()
+    sync = int(re.search(r"#define QG_WS_SYNC_BYTES (\d+)u", hdr).group(1))
+    assert sync % 256 == 0
+    for q in (L.qg_gemv_ws_bytes(2048, 2048), L.qg_gemv_ws_bytes(16, 128),
+              L.qg_gemm16_ws_bytes(8, 5120, 17408), L.qg_gateup_ws_bytes(512, 2048),
+              L.qg_lmhead_ws_bytes(248320, 5120), L.qg_moe_ws_bytes(ctypes.byref(_moe()), 1)):
+        assert q >= sync
+
+
 def _gemv(**kw):
     a = dict(qs=FAKE, d=FAKE, rows=64, cols=128, X=FAKE + (1 << 20), ldx=128, ncols=1,
              Y=FAKE + (2 << 20), ldy=64, acc=0, ws=FAKE + (3 << 20), wsb=1 << 20, stream=None)

@@ -1,0 +1,156 @@
+"""GPU parity at the benchmarked sizes, in the launch configurations the bench
+times (the launch plan depends on the shape and the column count only).
+
+* decode FFN layer, batch 1: gate/up Q4_0 5120 -> 2 x 17408 with SiLU, then
+  down Q4_0 17408 -> 5120 accumulated into the residual, end to end;
+* speculative-verify GEMVs, 4 and 8 columns: Q8_0 5120 x 5120, Q4_0
+  5120 -> 17408;
+* 16-column prefill GEMMs, Q4_0 and Q8_0, 5120 -> 17408 and 17408 -> 5120;
+* LM head Q8_0 5120 -> 248,320 with argmax (and a 65,536-row draft prefix);
+* MoE FFN, 256 experts of 2048 -> 512 -> 2048 (top-8) + shared expert,
+  1 and 16 tokens.
+
+Every output element is checked against the f64 oracle (these sizes run in
+seconds on the host); indices bit-exact where the oracle certifies them.
+Weights and activations are drawn exactly as the bench draws them.
+"""
+import numpy as np
+import pytest
+
+import synth
+from gpu_helpers import assert_tol, check_routing, host, say, up
+from oracle import ops
+
+pytestmark = pytest.mark.gpu
+
+Q4, Q8 = synth.Q4_0, synth.Q8_0
+SIG = {Q4: 0.02, Q8: 0.005}
+
+
+def matrix(env, qtype, rows, cols, seed):
+    _, qg, _ = env
+    raw = synth.gen_weights(qtype, rows, cols, SIG[qtype], np.random.default_rng(seed))
+    return raw, qg.qg_repack(qtype, up(env, raw.reshape(-1)), rows, cols)
+
+
+def test_decode_ffn_layer(env):
+    torch, qg, dev = env
+    N, K = 17408, 5120
+    say(f"decode FFN gate/up {K}->2x{N}, down {N}->{K}, batch 1")
+    graw, G = matrix(env, Q4, N, K, 21)
+    uraw, U = matrix(env, Q4, N, K, 22)
+    draw, D = matrix(env, Q4, K, N, 23)
+    x = synth.gen_x(K, 1, cfg_id=synth.CFG_FFN)
+    y_in = synth.rng(synth.CFG_FFN, 90).standard_normal((K, 1)).astype(np.float32)
+    H = qg.gateup_silu(G, U, up(env, x.T))
+    Y = up(env, y_in.T)
+    qg.qgemv(D, H, Y, accumulate=True)
+    torch.cuda.synchronize()
+    h, th, _, _ = ops.gateup_silu(Q4, graw, uraw, x)
+    assert_tol(host(H).T, h, th, "h = silu(Wg x) * (Wu x)")
+    y, _ = ops.gemv(Q4, draw, h, y_in=y_in)
+    ty = ops.down_tol(Q4, draw, h, th) + 2 * ops.U32 * np.abs(y)
+    assert_tol(host(Y).T, y, ty, "y += Wd h")
+
+
+@pytest.mark.parametrize("qtype,N,K", [(Q8, 5120, 5120), (Q4, 17408, 5120)])
+@pytest.mark.parametrize("ncols", [4, 8])
+def test_verify_gemv(env, qtype, N, K, ncols):
+    torch, qg, dev = env
+    say(f"verify qtype={qtype} {K}->{N} ncols={ncols}")
+    raw, W = matrix(env, qtype, N, K, 31)
+    X = synth.gen_x(K, ncols, cfg_id=synth.CFG_VERIFY)
+    Xd = up(env, X.T)
+    Y = qg.qgemv(W, Xd)
+    torch.cuda.synchronize()
+    ref, a = ops.gemv(qtype, raw, X)
+    assert_tol(host(Y).T, ref, ops.tol_dot(a), "verify")
+    # column j of the batched product equals the 1-column product, bitwise
+    for j in range(ncols):
+        assert torch.equal(Y[j], qg.qgemv(W, Xd[j:j + 1].contiguous())[0]), j
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("N,K", [(17408, 5120), (5120, 17408)])
+def test_prefill_gemm16(env, qtype, N, K):
+    torch, qg, dev = env
+    say(f"gemm16 qtype={qtype} {K}->{N}")
+    raw, W = matrix(env, qtype, N, K, 41)
+    X = synth.gen_x(K, 16, cfg_id=synth.CFG_PREFILL)
+    Y = qg.qgemm16(W, up(env, X.T))
+    torch.cuda.synchronize()
+    ref, a = ops.gemv(qtype, raw, X)
+    assert_tol(host(Y).T, ref, ops.tol_dot(a), "gemm16")
+
+
+def test_lmhead_argmax_full_vocabulary(env):
+    torch, qg, dev = env
+    N, K = 248320, 5120
+    say(f"LM head Q8_0 {K}->{N}")
+    raw, W = matrix(env, Q8, N, K, 51)
+    X = synth.gen_x(K, 8, cfg_id=synth.CFG_PREFILL)   # column 0 is the bench's x
+    ref, a = ops.gemv(Q8, raw, X)
+    cols = [j for j in range(8) if ops.argmax_certified(ref[:, j], a[:, j], K + 64, ops.U16)]
+    say(f"  certified columns: {cols}")
+    assert cols, "no certified column"
+    checked_prefix = 0
+    for j in cols[:3]:
+        xd = up(env, X[:, j])
+        idx, val = qg.lmhead_argmax(W, xd)
+        torch.cuda.synchronize()
+        i = int(idx.item())
+        assert i == ops.argmax_first(ref[:, j]), (j, i)
+        assert abs(val.item() - ref[i, j]) <= ops.tol_dot(a[i, j])
+        n = 65536
+        if ops.argmax_certified(ref[:n, j], a[:n, j], K + 64, ops.U16):
+            idx, _ = qg.lmhead_argmax(W, xd, n_rows=n)
+            assert int(idx.item()) == ops.argmax_first(ref[:n, j]), (j, "prefix")
+            checked_prefix += 1
+    assert checked_prefix, "no certified draft prefix"
+
+
+@pytest.fixture(scope="module")
+def moe_full(env):
+    """The MoE layer exactly as the bench draws it."""
+    torch, qg, dev = env
+    E, H, F = 256, 2048, 512
+    g = np.random.default_rng(61)
+    stack = lambda r, c: np.stack([synth.gen_weights(Q4, r, c, 0.02, g) for _ in range(E)])
+    gate, upw, down = stack(F, H), stack(F, H), stack(H, F)
+    sh = [synth.gen_weights(Q4, r, c, 0.02, np.random.default_rng(62 + i))
+          for i, (r, c) in enumerate(((F, H), (F, H), (H, F)))]
+    router = synth.gen_f32((E, H), 0.02, g)
+    rep = lambda raw, r, c, n=1: qg.qg_repack(Q4, up(env, raw.reshape(-1)), r, c, n)
+    m = qg.MoE(hidden=H, ffn=F, n_expert=E, top_k=8, router=up(env, router),
+               gate=rep(gate, F, H, E), up=rep(upw, F, H, E), down=rep(down, H, F, E),
+               sh_gate=rep(sh[0], F, H), sh_up=rep(sh[1], F, H), sh_down=rep(sh[2], H, F))
+    return m, (gate, upw, down, router, sh)
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_moe_full_layer(env, moe_full, T):
+    torch, qg, dev = env
+    m, (gate, upw, down, router, sh) = moe_full
+    H, k = m.hidden, m.top_k
+    say(f"MoE 256 experts top-8 + shared, hidden 2048, ffn 512, T={T}")
+    # the bench's tokens first, then later seeds until the oracle certifies
+    # every token's selected set
+    for c in range(0, 64 * T, T):
+        X = synth.gen_x(H, T, cfg_id=synth.CFG_MOE, col0=c)
+        lg, la = ops.router_logits(X, router)
+        if np.all(ops.routing_certified(lg, la, k, H)):
+            break
+    else:
+        pytest.fail("no certified routing")
+    say(f"  tokens from column {c}")
+    y_in = synth.rng(synth.CFG_MOE, 90).standard_normal((H, T)).astype(np.float32)
+    Y = up(env, y_in.T)
+    tidx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    qg.moe_ffn(m, up(env, X.T), Y, tidx, tw)
+    torch.cuda.synchronize()
+    res = ops.moe_ffn(X, router, Q4, gate, upw, down, top_k=k,
+                      sh_gate=sh[0], sh_up=sh[1], sh_down=sh[2], y_in=y_in)
+    n_ord = check_routing(tidx.cpu().numpy(), tw.cpu().numpy(), res, k, H)
+    say(f"  routing: {T} tokens, order certified for {n_ord}")
+    assert_tol(host(Y).T, res["y"], res["tol"], f"moe T={T}")
