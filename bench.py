@@ -122,11 +122,13 @@ def run_ffn(B, steps, warmup):
     if warmup > 0:
         _, gw = B.graph_time(steps_fns, warmup)
     t_step, _ = B.graph_time(steps_fns, steps)
+    xv, yv, hv = x[0], y[0], h[0]
+    t_fused, _ = B.graph_time([lambda i=i: qg.ffn_fused(pg[i], pu[i], pd[i], xv, yv, hv) for i in range(n)], 4 * n)
     t_gu, _ = B.graph_time([lambda i=i: qg.gateup_silu(pg[i], pu[i], x, h) for i in range(n)], 4 * n)
     t_dn, _ = B.graph_time([lambda i=i: qg.qgemv(pd[i], h, y, accumulate=True) for i in range(n)], 4 * n)
     raws = (graw, uraw, draw)
     del pg, pu, pd
-    return step_bytes, t_step, gu_bytes, t_gu, dn_bytes, t_dn, raws
+    return step_bytes, t_step, gu_bytes, t_gu, dn_bytes, t_dn, raws, t_fused
 
 
 def run_extras(B, kernels):
@@ -318,11 +320,12 @@ def main():
         return
 
     log("bench: decode FFN step")
-    step_bytes, t_step, gu_bytes, t_gu, dn_bytes, t_dn, raws = run_ffn(B, args.steps, args.warmup)
+    step_bytes, t_step, gu_bytes, t_gu, dn_bytes, t_dn, raws, t_fused = run_ffn(B, args.steps, args.warmup)
     value = step_bytes / t_step / 1e9
     kernels = {
         "gateup_silu_q4_0_5120to2x17408": kernel_entry(gu_bytes, t_gu),
         "qgemv_q4_0_17408to5120_acc": kernel_entry(dn_bytes, t_dn),
+        "ffn_fused_q4_0_5120x17408": kernel_entry(step_bytes, t_fused),
     }
     ceiling = read_ceiling(B)
     if args.suite == "all":

@@ -63,6 +63,9 @@ _SIGS = {
     "qgemm16": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i32,
                                _vp, _sz, _vp]),
     "qg_gateup_ws_bytes": (_sz, [_i64, _i64]),
+    "qg_ffn_ws_bytes": (_sz, [_i64, _i64]),
+    "ffn_fused": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp,
+                                 _vp, _sz, _vp]),
     "gateup_silu": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _i32,
                                    _vp, _i64, _vp, _sz, _vp]),
     "qg_lmhead_ws_bytes": (_sz, [_i64, _i64]),
@@ -231,6 +234,29 @@ def gateup_silu(wg: QMatrix, wu: QMatrix, X, H=None):
                            H2.data_ptr(), _ld(H2), ws.data_ptr(), ws.numel(),
                            _stream(X.device)), "gateup_silu")
     return H
+
+
+def ffn_fused(wg: QMatrix, wu: QMatrix, wd: QMatrix, x, y, h=None):
+    """One token through a decode FFN: h = silu(Wg x) * (Wu x); y += Wd h.
+    Returns h.  Bitwise equal to gateup_silu + qgemv(accumulate=True)."""
+    torch = _torch()
+    _check_dev(x, y)
+    if not (wg.qtype == wu.qtype == wd.qtype):
+        raise ValueError("gate, up and down must share one quantisation type")
+    if h is None:
+        h = torch.empty(wg.rows, dtype=torch.float32, device=x.device)
+    ws = workspace(lib.qg_ffn_ws_bytes(wg.cols, wg.rows), x.device, "ffn")
+    _check(lib.ffn_fused(wg.qtype, wg.qs.data_ptr(), wg.d.data_ptr(), wu.qs.data_ptr(), wu.d.data_ptr(),
+                         wd.qs.data_ptr(), wd.d.data_ptr(), wg.cols, wg.rows, x.data_ptr(), h.data_ptr(),
+                         y.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x.device)), "ffn_fused")
+    return h
+
+
+def ffn_wait_error(device=None) -> int:
+    """The fused FFN's error word (nonzero: a wait gave up; see qgemm.h)."""
+    torch = _torch()
+    ws = _WS.get((torch.device(device or "cuda:0").index or 0, "ffn"))
+    return 0 if ws is None else int(ws[8:12].view(torch.int32).item())
 
 
 def lmhead_argmax(w: QMatrix, x, n_rows: Optional[int] = None, out_idx=None, out_val=None):

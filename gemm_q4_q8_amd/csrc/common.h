@@ -84,6 +84,22 @@ __device__ __forceinline__ float dot2_first(h2 a, h2 b) {
 __device__ __forceinline__ u4 ld_stream(const uint8_t *p) { return __builtin_nontemporal_load((const u4 *)p); }
 __device__ __forceinline__ u2 ld_stream2(const uint8_t *p) { return __builtin_nontemporal_load((const u2 *)p); }
 
+// Bounded streams: a raw buffer resource over [base, base + bytes).  A load
+// at an offset at or beyond `bytes` returns zeros and reads no memory (the
+// buffer range check of gfx9), so a prefetch loop can run past the end of
+// its range without a branch around its loads.  Offsets go in the VGPR
+// offset, which is what the range check covers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_range(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+// nontemporal (aux bit 1): streamed once, no cache allocation
+__device__ __forceinline__ u4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+}
+__device__ __forceinline__ u2 buf_ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2);
+}
+
 // Q8_0: two u32 words = 8 biased bytes (q + 128) of one block slice.  A byte
 // permute puts each byte under a 0x64 high byte (1024 + b, exact), then
 // subtracting 1152 = 1024 + 128 leaves q exactly.

@@ -1,0 +1,396 @@
+// One work unit of the dot path (1..8 activation columns): a K segment of
+// WKT * RT row tiles of one or two matrices (gate and up), used by the GEMV
+// kernels and by the fused FFN kernel.
+//
+// What is computed ("Engine and kernels", Kernel families): y = W x over
+// Q4_0 / Q8_0 blocks dequantised in registers with f32 sums, with the
+// epilogues of the kernel families (store, y += W x, SiLU(gate) * up, and
+// the per-row values an argmax needs).
+//
+// How (MI355X):
+//  * The workgroup stages the segment's activations once in LDS as f16,
+//    [block][column][32], read with broadcast by every wave.
+//  * One wave streams one row tile (of each matrix) across the segment, PF
+//    tile columns ahead; each 16-byte load of a wave reads a contiguous
+//    1 KiB stripe.  The stream is a bounded buffer range, so loads past the
+//    segment return zeros without touching memory and the loop has no
+//    branch around its loads.
+//  * Weights become exact f16 pairs and meet the activations in
+//    v_dot2_f32_f16; each block's partial is scaled by its f16 scale in f32.
+//  * Reduction order: tile columns in order within a wave, a 2-step lane
+//    butterfly, then the S segment partials in segment order (the last
+//    workgroup of the row group to finish adds them).  The order depends on
+//    the shape only, so each activation column of a batched call is bitwise
+//    equal to a 1-column call ("Architecture", Speculative decoding).
+//
+// Phases, for the fused FFN: a producer unit (gate/up) publishes the h rows
+// of its row group with coherent stores and then raises that group's ready
+// flag; a consumer unit (down) issues its first weight loads, waits until
+// the flags of its K segment are raised, and reads h with coherent loads.
+#pragma once
+#include "common.h"
+#include "internal.h"
+
+namespace qg {
+
+// Segment q of a K range of kt tile columns cut into n pieces.
+__host__ __device__ inline int seg_begin(int q, int kt, int n) { return (int)((int64_t)kt * q / n); }
+
+enum Phase { PH_PLAIN = 0, PH_PRODUCE = 1, PH_CONSUME = 2 };
+
+// Multiply form of the dot path: the matrix cores (true) or v_dot2 (false).
+#ifndef DOT_MF
+#define DOT_MF true
+#endif
+
+// Polls before a consumer gives up waiting (about 0.1 s); a correct launch
+// never gets near it, it only guarantees the kernel ends.
+constexpr int WAIT_POLLS = 1 << 20;
+
+struct DotArgs {
+  const uint8_t *qs0, *qs1, *d0, *d1;
+  int64_t rows;       // outputs produced (n_rows for the LM head)
+  int64_t cols;
+  int NT, KT;         // row tiles produced, tile columns of the matrix
+  int S;              // K segments
+  int G;              // row groups of WKT * RT row tiles
+  int64_t units;      // G * S workgroups
+  int64_t per_xcd;
+  const float *X;
+  int64_t ldx;
+  int ncols;
+  float *Y;
+  int64_t ldy;
+  float *part;        // segment partials [S][NMAT][NT*16][NC]
+  uint32_t *cnt;      // [G]
+  uint32_t *gcnt;     // argmax: one counter
+  float *cand_v;      // argmax: [G]
+  int32_t *cand_i;
+  int32_t *out_idx;
+  float *out_val;
+  uint32_t *ready;    // fused FFN: producer sets ready[g]; consumer waits on ready[kt]
+  uint32_t *err;      // fused FFN: set when a wait gave up
+};
+
+// Returns true when this workgroup emitted the outputs of row group g (its
+// only segment, or the last of its segments to finish).  For the argmax
+// epilogue, (bv, bi) then hold each lane's best (value, row).
+struct NoHook {
+  __device__ void operator()() const {}
+};
+
+// `staged` runs once the activations are in LDS and the first weight loads
+// are in flight (the fused FFN takes its next work unit there, so that
+// round trip overlaps the stream).
+template <int QT, int NC, int NMAT, int EPI, int RT, int PF, int WKT, int PH, bool MF = false,
+          class Hook = NoHook>
+__device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t *smem, uint32_t *flag,
+                                          float &bv, int32_t &bi, Hook staged = Hook()) {
+  constexpr int NTHR = WKT * 64;
+  constexpr int XC = NC;  // activation columns in the LDS layout
+  // accumulators per lane: dot form, one per column; matrix-core form, the
+  // 4 D values of lane (r, sl) are columns 4 sl + i
+  constexpr int NI = MF ? (NC < 4 ? NC : 4) : NC;
+  constexpr int TB = QTraits<QT>::tile_bytes;
+  constexpr int QW = (QT == Q4) ? 1 : 2;  // 16-byte loads per lane per tile
+  constexpr int XAUX = PH == PH_CONSUME ? 16 : 0;  // sc1: h comes from other XCDs
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wk = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kt0 = seg_begin(s, a.KT, a.S);
+  const int nkt = seg_begin(s + 1, a.KT, a.S) - kt0;
+  const int64_t rt_base = ((int64_t)g * WKT + wk) * RT;
+  const int r = lane & 15, sl = lane >> 4;
+  _Float16 *xs = (_Float16 *)smem;
+
+  // activations: a bounded range over the columns; a chunk outside the
+  // segment or the matrix reads zeros
+  const int nvec = nkt * TILE_BLOCKS * NC * 4;  // 8-value chunks of real columns
+  const __amdgpu_buffer_rsrc_t rx =
+      buf_range(a.X, (uint32_t)(((int64_t)(a.ncols - 1) * a.ldx + a.cols) * 4));
+  auto x_off = [&](int v) -> uint32_t {
+    const int qq = v & 3, c = (v >> 2) % NC, bl = (v >> 2) / NC;
+    const int64_t k = ((int64_t)kt0 * TILE_BLOCKS + bl) * 32 + qq * 8;
+    const bool ok = v < nvec && k < a.cols && c < a.ncols;
+    return ok ? (uint32_t)(((int64_t)c * a.ldx + k) * 4) : 0xFFFFFFC0u;  // past any range
+  };
+  auto x_ld = [&](int v, u4 &lo, u4 &hi) {
+    const uint32_t o = x_off(v);
+    lo = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, XAUX);
+    hi = __builtin_amdgcn_raw_buffer_load_b128(rx, o + 16u, 0, XAUX);
+  };
+  auto x_put = [&](int v, const u4 &lo, const u4 &hi) {
+    if (v < nvec) {
+      const int qq = v & 3, c = (v >> 2) % NC, bl = (v >> 2) / NC;
+      *(h8 *)(xs + ((size_t)bl * XC + c) * 32 + qq * 8) =
+          cvt8(__builtin_bit_cast(float4, lo), __builtin_bit_cast(float4, hi));
+    }
+  };
+
+  // one bounded range per (matrix, row tile) over this segment; row tiles
+  // past the matrix get an empty range
+  __amdgpu_buffer_rsrc_t rq[NMAT][RT], rd[NMAT][RT];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const bool in = rt_base + t < a.NT;
+      const int64_t tile = (in ? rt_base + t : 0) * a.KT + kt0;
+      rq[m][t] = buf_range((m ? a.qs1 : a.qs0) + tile * TB, in ? (uint32_t)nkt * TB : 0u);
+      rd[m][t] = buf_range((m ? a.d1 : a.d0) + tile * TILE_D_BYTES, in ? (uint32_t)nkt * TILE_D_BYTES : 0u);
+    }
+  u4 wq[PF][NMAT][RT][QW];
+  u2 wd[PF][NMAT][RT];
+  const uint32_t lane_off = (uint32_t)lane * 16u, d_off = (uint32_t)r * 8u;
+  auto load = [&](int slot, int rel) {  // rel: tile column within the segment
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const uint32_t qo = (uint32_t)rel * TB + lane_off;
+        wq[slot][m][t][0] = buf_ld16(rq[m][t], qo);
+        if constexpr (QW == 2) wq[slot][m][t][1] = buf_ld16(rq[m][t], qo + 1024u);
+        wd[slot][m][t] = buf_ld8(rd[m][t], (uint32_t)rel * TILE_D_BYTES + d_off);
+      }
+  };
+
+  // ---- 1. start the weight stream, and (first round) the activations
+  u4 xlo0, xhi0;
+  if constexpr (PH != PH_CONSUME) x_ld(tid, xlo0, xhi0);
+#pragma unroll
+  for (int p = 0; p < PF; ++p) load(p, p);
+
+  if constexpr (PH == PH_CONSUME) {
+    // the activations are h rows other workgroups produce: wait until the
+    // ready flags of this segment's tile columns are raised
+    if (wk == 0) {
+      for (int it = 0;; ++it) {
+        bool ok = true;
+        for (int j = lane; j < nkt; j += 64) ok = ok && ld_agent_u32(a.ready + kt0 + j) != 0u;
+        if (__all(ok)) break;
+        if (it >= WAIT_POLLS) {
+          if (lane == 0) st_agent_u32(a.err, 1u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
+    x_ld(tid, xlo0, xhi0);
+  }
+
+  // ---- 2. finish staging: f16 in LDS.  Further chunks (long segments, many
+  // columns) go in batches of XB whose loads are all issued before any is used.
+  x_put(tid, xlo0, xhi0);
+  {
+    constexpr int XB = 4;
+    for (int v0 = tid + NTHR; v0 < nvec; v0 += XB * NTHR) {
+      u4 lo[XB], hi[XB];
+#pragma unroll
+      for (int b = 0; b < XB; ++b) x_ld(v0 + b * NTHR, lo[b], hi[b]);
+#pragma unroll
+      for (int b = 0; b < XB; ++b) x_put(v0 + b * NTHR, lo[b], hi[b]);
+    }
+  }
+  __syncthreads();
+  staged();
+
+  // ---- 3. stream the weight tiles of the segment
+  float acc[NMAT][RT][NI];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int c = 0; c < NI; ++c) acc[m][t][c] = 0.0f;
+
+  const Q4Magic mg = q4_magic();
+  // matrix-core A operand: lane (r, sl) holds column r, k 8 sl .. 8 sl + 7.
+  // Lanes of columns past NC keep zeros: they never load (exec-masked), so
+  // the register set to zero here stays zero.
+  h8 A = {0, 0, 0, 0, 0, 0, 0, 0};
+  auto compute = [&](int slot, int rel) {
+    const int bl0 = rel * TILE_BLOCKS;
+    if constexpr (MF) {
+      // per block: D (16 columns x 16 rows) = X_blk^T W_blk^T on the matrix
+      // cores from the exact f16 weights, then each lane's 4 D values get
+      // the block scale of its row
+#pragma unroll
+      for (int j = 0; j < TILE_BLOCKS; ++j) {
+        if (NC == 16 || r < NC) A = *(const h8 *)(xs + ((size_t)(bl0 + j) * XC + r) * 32 + sl * 8);
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int t = 0; t < RT; ++t) {
+            h2 w[4];
+            if constexpr (QT == Q4) unpack_q4(wq[slot][m][t][0][j], w, mg);
+            else unpack_q8(wq[slot][m][t][j >> 1][(j & 1) * 2], wq[slot][m][t][j >> 1][(j & 1) * 2 + 1], w);
+            const h8 B = {w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
+            const f4 D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            // B stays in use past the MFMA, so its result cannot be given
+            // B's registers: the matrix core reads its A and B operands over
+            // several passes while it writes the result
+            __asm__ volatile("" ::"v"(B));
+            const float dj = scale_of(wd[slot][m][t], j);
+#pragma unroll
+            for (int i = 0; i < NI; ++i) acc[m][t][i] = __builtin_fmaf(dj, D[i], acc[m][t][i]);
+          }
+      }
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < TILE_BLOCKS; ++j) {
+      h2 xv[NC][4];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const h8 xx = *(const h8 *)(xs + ((size_t)(bl0 + j) * XC + c) * 32 + sl * 8);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) xv[c][p] = lo_pair(xx, p);
+      }
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          h2 w[4];
+          if constexpr (QT == Q4) unpack_q4(wq[slot][m][t][0][j], w, mg);
+          else unpack_q8(wq[slot][m][t][j >> 1][(j & 1) * 2], wq[slot][m][t][j >> 1][(j & 1) * 2 + 1], w);
+          const float dj = scale_of(wd[slot][m][t], j);
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            float p = dot2_first(w[0], xv[c][0]);
+            p = __builtin_amdgcn_fdot2(w[1], xv[c][1], p, false);
+            p = __builtin_amdgcn_fdot2(w[2], xv[c][2], p, false);
+            p = __builtin_amdgcn_fdot2(w[3], xv[c][3], p, false);
+            acc[m][t][c] = __builtin_fmaf(dj, p, acc[m][t][c]);
+          }
+        }
+    }
+  };
+
+  // PF tile columns in flight; loads past the segment read nothing
+  const int nseg = rt_base < a.NT ? nkt : 0;
+  for (int k = 0; k < nseg; k += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      if (k + p < nseg) compute(p, k + p);
+      load(p, k + p + PF);
+    }
+  }
+
+  // ---- 4. per-row sums.  Dot form: after the butterfly every lane of row r
+  // holds the same (bitwise) sum of the wave's segment, and lane (r, sl)
+  // handles the outputs o = t * NC + c with o % 4 == sl.  Matrix-core form:
+  // lane (r, sl) holds column 4 sl + i of row r.
+  if constexpr (!MF) {
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          float v = acc[m][t][c];
+          v += __shfl_xor(v, 16);
+          v += __shfl_xor(v, 32);
+          acc[m][t][c] = v;
+        }
+  }
+  // (t, i) -> the column this lane handles, or -1
+  auto col_of = [&](int t, int i) -> int {
+    if constexpr (MF) {
+      const int c = 4 * sl + i;
+      return c < NC ? c : -1;
+    } else {
+      return ((t * NC + i) & 3) == sl ? i : -1;
+    }
+  };
+
+  auto emit = [&](int t, int c, const float (&v)[NMAT]) {
+    const int64_t row = (rt_base + t) * 16 + r;
+    if (rt_base + t >= a.NT || row >= a.rows) return;
+    if constexpr (EPI == EPI_ARGMAX) {
+      if (ranks_before(v[0], (int32_t)row, bv, bi)) { bv = v[0]; bi = (int32_t)row; }
+    } else {
+      float *yp = a.Y + (int64_t)c * a.ldy + row;
+      float out;
+      if constexpr (EPI == EPI_STORE) {
+        out = v[0];
+      } else if constexpr (EPI == EPI_ACC) {
+        out = *yp + v[0];
+      } else {
+        const float gg = v[0];
+        const float sg = gg / (1.0f + expf(-gg));
+        out = sg * v[NMAT - 1];
+      }
+      if constexpr (PH == PH_PRODUCE) st_agent(yp, out);
+      else *yp = out;
+    }
+  };
+
+  bool emitted;
+  if (a.S == 1) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int c = col_of(t, i);
+        if (c >= 0) {
+          float v[NMAT];
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m) v[m] = acc[m][t][i];
+          emit(t, c, v);
+        }
+      }
+    emitted = true;
+  } else {
+    // publish the segment partials; the last workgroup of the row group
+    // adds them in segment order
+    const int64_t rows_pad = (int64_t)a.NT * 16;
+    auto slot_of = [&](int ss, int m, int64_t row, int c) {
+      return a.part + (((int64_t)ss * NMAT + m) * rows_pad + row) * NC + c;
+    };
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int c = col_of(t, i);
+        if (c >= 0 && rt_base + t < a.NT) {
+          const int64_t row = (rt_base + t) * 16 + r;
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m) st_agent(slot_of(s, m, row, c), acc[m][t][i]);
+        }
+      }
+    emitted = arrive_last(a.cnt + g, (uint32_t)a.S, flag);
+    if (emitted) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int c = col_of(t, i);
+          if (c >= 0 && rt_base + t < a.NT) {
+            const int64_t row = (rt_base + t) * 16 + r;
+            float v[NMAT];
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) {
+              float x = ld_agent(slot_of(0, m, row, c));
+              for (int ss = 1; ss < a.S; ++ss) x += ld_agent(slot_of(ss, m, row, c));
+              v[m] = x;
+            }
+            emit(t, c, v);
+          }
+        }
+    }
+  }
+
+  if constexpr (PH == PH_PRODUCE) {
+    // h rows of row group g are out: raise its flag once every wave's
+    // stores are acknowledged
+    if (emitted) {
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (tid == 0) st_agent_u32(a.ready + g, 1u);
+    }
+  }
+  return emitted;
+}
+
+}  // namespace qg

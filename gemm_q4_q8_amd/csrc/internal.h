@@ -32,9 +32,10 @@ struct QmvCall {
   hipStream_t stream;
 };
 
-// K segments of the dot path: a function of the matrix shape only, so that
-// every column count gives the same per-row reduction order.
-int gemv_segments(int64_t rows, int64_t cols);
+// K segments of the dot path: a function of the matrix shape (and of the
+// widest batch the entry point takes) only, so that every column count gives
+// the same per-row reduction order.
+int gemv_segments(int64_t rows, int64_t cols, int nmat, int ncols_max);
 // K splits of the 16-column matrix-core path.
 int gemm16_splits(int64_t rows, int64_t cols);
 
@@ -50,6 +51,20 @@ size_t qmv_ws_bytes(int64_t rows, int64_t cols, int slots, int nmat, int ncols_m
 int launch_qmv(const QmvCall &c);  // returns 0 or a QG_ status
 int launch_repack(int qtype, int64_t n_mat, int64_t rows, int64_t cols, const void *blocks,
                   void *qs, void *d, hipStream_t stream);
+
+// One fused decode FFN: h = SiLU(Wg x) * (Wu x); y += Wd h (one token).
+struct FfnCall {
+  int qtype;
+  const void *g_qs, *g_d, *u_qs, *u_d, *d_qs, *d_d;
+  int64_t hidden, ffn;
+  const float *x;
+  float *h, *y;
+  void *ws;
+  size_t ws_bytes;
+  hipStream_t stream;
+};
+size_t ffn_ws_bytes(int64_t hidden, int64_t ffn);
+int launch_ffn(const FfnCall &c);
 
 struct MoeCall {
   const qg_moe *m;

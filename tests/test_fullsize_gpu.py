@@ -2,7 +2,8 @@
 times (the launch plan depends on the shape and the column count only).
 
 * decode FFN layer, batch 1: gate/up Q4_0 5120 -> 2 x 17408 with SiLU, then
-  down Q4_0 17408 -> 5120 accumulated into the residual, end to end;
+  down Q4_0 17408 -> 5120 accumulated into the residual, end to end, as two
+  calls and as the fused single launch;
 * speculative-verify GEMVs, 4 and 8 columns: Q8_0 5120 x 5120, Q4_0
   5120 -> 17408;
 * 16-column prefill GEMMs, Q4_0 and Q8_0, 5120 -> 17408 and 17408 -> 5120;
@@ -51,6 +52,12 @@ def test_decode_ffn_layer(env):
     y, _ = ops.gemv(Q4, draw, h, y_in=y_in)
     ty = ops.down_tol(Q4, draw, h, th) + 2 * ops.U32 * np.abs(y)
     assert_tol(host(Y).T, y, ty, "y += Wd h")
+    # the fused single-launch form gives the same bits
+    yf = up(env, y_in[:, 0])
+    hf = qg.ffn_fused(G, U, D, up(env, x[:, 0]), yf)
+    torch.cuda.synchronize()
+    assert qg.ffn_wait_error() == 0
+    assert torch.equal(hf, H[0]) and torch.equal(yf, Y[0])
 
 
 @pytest.mark.parametrize("qtype,N,K", [(Q8, 5120, 5120), (Q4, 17408, 5120)])

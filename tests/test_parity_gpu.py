@@ -165,6 +165,39 @@ def test_gateup_parity(env, qtype, rows, cols, ncols):
     assert_tol(host(H).T, h, th, "gateup")
 
 
+# --------------------------------------------------------------- fused FFN
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("H,F", [(256, 384), (416, 224), (512, 2048), (2048, 1024)])
+def test_ffn_fused(env, qtype, H, F):
+    """One launch for gate/up + SiLU + down + residual: against the oracle,
+    bitwise against the two separate calls, and again on a second call (the
+    ready flags and the work queue reset themselves)."""
+    torch, qg, dev = env
+    say(f"ffn_fused qtype={qtype} hidden={H} ffn={F}")
+    graw, G = make(env, qtype, F, H, seed=H + F)
+    uraw, U = make(env, qtype, F, H, seed=H + F + 1)
+    draw, D = make(env, qtype, H, F, seed=H + F + 2)
+    x = synth.gen_x(H, 1, cfg_id=400 + H)[:, 0]
+    y_in = synth.rng(400, F).standard_normal(H).astype(np.float32)
+    y = up(env, y_in)
+    h = qg.ffn_fused(G, U, D, up(env, x), y)
+    torch.cuda.synchronize()
+    assert qg.ffn_wait_error() == 0
+    hr, th, _, _ = ops.gateup_silu(qtype, graw, uraw, x)
+    assert_tol(host(h), hr, th, "h")
+    yr, _ = ops.gemv(qtype, draw, hr, y_in=y_in)
+    assert_tol(host(y), yr, ops.down_tol(qtype, draw, hr, th) + 2 * ops.U32 * np.abs(yr), "y")
+    h2 = qg.gateup_silu(G, U, up(env, x.reshape(1, -1)))
+    y2 = up(env, y_in.reshape(1, -1))
+    qg.qgemv(D, h2, y2, accumulate=True)
+    assert torch.equal(h, h2[0]) and torch.equal(y, y2[0])
+    for _ in range(2):
+        y3 = up(env, y_in)
+        h3 = qg.ffn_fused(G, U, D, up(env, x), y3)
+        assert torch.equal(h3, h) and torch.equal(y3, y)
+    assert qg.ffn_wait_error() == 0
+
+
 # ----------------------------------------------------------------- LM head
 def _lm_case(env, qtype, rows, cols, seed, plant=None):
     torch, qg, dev = env
