@@ -94,6 +94,14 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   constexpr int TB = QTraits<QT>::tile_bytes;
   constexpr int QW = (QT == Q4) ? 1 : 2;  // 16-byte loads per lane per tile
   constexpr int XAUX = PH == PH_CONSUME ? 16 : 0;  // sc1: h comes from other XCDs
+  // Wide batches stream their activations in chunks of PF tile columns,
+  // double-buffered in LDS and staged one chunk ahead of the products (the
+  // whole segment would take several L2 round trips before the first
+  // product); narrow ones stage the whole segment up front.
+  constexpr bool XS = NC >= 16;
+  constexpr int CHV = PF * TILE_BLOCKS * NC * 4;   // 8-value pieces per chunk
+  constexpr int CHH = PF * TILE_BLOCKS * NC * 32;  // halves per chunk buffer
+  constexpr int XR = (CHV + NTHR - 1) / NTHR;      // pieces per thread per chunk
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wk = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -105,24 +113,27 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
 
   // activations: a bounded range over the columns; a chunk outside the
   // segment or the matrix reads zeros
-  const int nvec = nkt * TILE_BLOCKS * NC * 4;  // 8-value chunks of real columns
+  const int nvec = nkt * TILE_BLOCKS * NC * 4;  // 8-value pieces of the segment
   const __amdgpu_buffer_rsrc_t rx =
       buf_range(a.X, (uint32_t)(((int64_t)(a.ncols - 1) * a.ldx + a.cols) * 4));
-  auto x_off = [&](int v) -> uint32_t {
+  // piece v of the `span` pieces from tile column rel0 on: (block, column,
+  // 8 k) -> byte offset in X, or past any range (reads zeros) when it lies
+  // outside the span, the segment or the matrix
+  auto x_off = [&](int v, int rel0, int span) -> uint32_t {
     const int qq = v & 3, c = (v >> 2) % NC, bl = (v >> 2) / NC;
-    const int64_t k = ((int64_t)kt0 * TILE_BLOCKS + bl) * 32 + qq * 8;
-    const bool ok = v < nvec && k < a.cols && c < a.ncols;
-    return ok ? (uint32_t)(((int64_t)c * a.ldx + k) * 4) : 0xFFFFFFC0u;  // past any range
+    const int64_t k = ((int64_t)(kt0 + rel0) * TILE_BLOCKS + bl) * 32 + qq * 8;
+    const bool ok = v < span && rel0 * TILE_BLOCKS + bl < nkt * TILE_BLOCKS && k < a.cols && c < a.ncols;
+    return ok ? (uint32_t)(((int64_t)c * a.ldx + k) * 4) : 0xFFFFFFC0u;
   };
-  auto x_ld = [&](int v, u4 &lo, u4 &hi) {
-    const uint32_t o = x_off(v);
+  auto x_ld = [&](int v, int rel0, int span, u4 &lo, u4 &hi) {
+    const uint32_t o = x_off(v, rel0, span);
     lo = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, XAUX);
     hi = __builtin_amdgcn_raw_buffer_load_b128(rx, o + 16u, 0, XAUX);
   };
-  auto x_put = [&](int v, const u4 &lo, const u4 &hi) {
-    if (v < nvec) {
+  auto x_put = [&](int v, int span, _Float16 *dst, const u4 &lo, const u4 &hi) {
+    if (v < span) {
       const int qq = v & 3, c = (v >> 2) % NC, bl = (v >> 2) / NC;
-      *(h8 *)(xs + ((size_t)bl * XC + c) * 32 + qq * 8) =
+      *(h8 *)(dst + ((size_t)bl * XC + c) * 32 + qq * 8) =
           cvt8(__builtin_bit_cast(float4, lo), __builtin_bit_cast(float4, hi));
     }
   };
@@ -155,8 +166,13 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   };
 
   // ---- 1. start the weight stream, and (first round) the activations
-  u4 xlo0, xhi0;
-  if constexpr (PH != PH_CONSUME) x_ld(tid, xlo0, xhi0);
+  constexpr int X0 = XS ? XR : 1;
+  const int span0 = XS ? CHV : nvec;
+  u4 xl[X0], xh[X0];
+  if constexpr (PH != PH_CONSUME) {
+#pragma unroll
+    for (int i = 0; i < X0; ++i) x_ld(tid + i * NTHR, 0, span0, xl[i], xh[i]);
+  }
 #pragma unroll
   for (int p = 0; p < PF; ++p) load(p, p);
 
@@ -176,20 +192,23 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
       }
     }
     __syncthreads();
-    x_ld(tid, xlo0, xhi0);
+#pragma unroll
+    for (int i = 0; i < X0; ++i) x_ld(tid + i * NTHR, 0, span0, xl[i], xh[i]);
   }
 
-  // ---- 2. finish staging: f16 in LDS.  Further chunks (long segments, many
-  // columns) go in batches of XB whose loads are all issued before any is used.
-  x_put(tid, xlo0, xhi0);
-  {
+  // ---- 2. staging: f16 in LDS, [block][column][32] (XS: chunk 0 into
+  // buffer 0).  Otherwise further pieces of the segment go in batches of XB
+  // whose loads are all issued before any is used.
+#pragma unroll
+  for (int i = 0; i < X0; ++i) x_put(tid + i * NTHR, span0, xs, xl[i], xh[i]);
+  if constexpr (!XS) {
     constexpr int XB = 4;
     for (int v0 = tid + NTHR; v0 < nvec; v0 += XB * NTHR) {
       u4 lo[XB], hi[XB];
 #pragma unroll
-      for (int b = 0; b < XB; ++b) x_ld(v0 + b * NTHR, lo[b], hi[b]);
+      for (int b = 0; b < XB; ++b) x_ld(v0 + b * NTHR, 0, nvec, lo[b], hi[b]);
 #pragma unroll
-      for (int b = 0; b < XB; ++b) x_put(v0 + b * NTHR, lo[b], hi[b]);
+      for (int b = 0; b < XB; ++b) x_put(v0 + b * NTHR, nvec, xs, lo[b], hi[b]);
     }
   }
   __syncthreads();
@@ -210,7 +229,9 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   // the register set to zero here stays zero.
   h8 A = {0, 0, 0, 0, 0, 0, 0, 0};
   auto compute = [&](int slot, int rel) {
-    const int bl0 = rel * TILE_BLOCKS;
+    // block index in LDS: the segment's own (rel), or, streaming, the slot
+    // of tile column rel in its chunk's buffer
+    const int bl0 = XS ? ((((rel / PF) & 1) * PF) + rel % PF) * TILE_BLOCKS : rel * TILE_BLOCKS;
     if constexpr (MF) {
       // per block: D (16 columns x 16 rows) = X_blk^T W_blk^T on the matrix
       // cores from the exact f16 weights, then each lane's 4 D values get
@@ -227,13 +248,14 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
             else unpack_q8(wq[slot][m][t][j >> 1][(j & 1) * 2], wq[slot][m][t][j >> 1][(j & 1) * 2 + 1], w);
             const h8 B = {w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
             const f4 D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            // B stays in use past the MFMA, so its result cannot be given
-            // B's registers: the matrix core reads its A and B operands over
-            // several passes while it writes the result
-            __asm__ volatile("" ::"v"(B));
             const float dj = scale_of(wd[slot][m][t], j);
 #pragma unroll
             for (int i = 0; i < NI; ++i) acc[m][t][i] = __builtin_fmaf(dj, D[i], acc[m][t][i]);
+            // A and B stay in use until after the result is read (the
+            // statement takes D, so it follows the MFMA): the result can
+            // then never be given their registers, which the matrix core
+            // reads over several passes while it writes the result
+            __asm__ volatile("" ::"v"(A), "v"(B), "v"(D));
           }
       }
       return;
@@ -268,12 +290,31 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   };
 
   // PF tile columns in flight; loads past the segment read nothing
-  const int nseg = rt_base < a.NT ? nkt : 0;
-  for (int k = 0; k < nseg; k += PF) {
+  if constexpr (XS) {
+    // every wave runs the same trip count: the chunk hand-over is a barrier
+    const bool live = rt_base < a.NT;
+    for (int k = 0; k < nkt; k += PF) {
+      u4 nl[XR], nh[XR];
 #pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      if (k + p < nseg) compute(p, k + p);
-      load(p, k + p + PF);
+      for (int i = 0; i < XR; ++i) x_ld(tid + i * NTHR, k + PF, CHV, nl[i], nh[i]);
+#pragma unroll
+      for (int p = 0; p < PF; ++p) {
+        if (live && k + p < nkt) compute(p, k + p);
+        load(p, k + p + PF);
+      }
+      _Float16 *nb = xs + (((k / PF) + 1) & 1) * CHH;
+#pragma unroll
+      for (int i = 0; i < XR; ++i) x_put(tid + i * NTHR, CHV, nb, nl[i], nh[i]);
+      __syncthreads();
+    }
+  } else {
+    const int nseg = rt_base < a.NT ? nkt : 0;
+    for (int k = 0; k < nseg; k += PF) {
+#pragma unroll
+      for (int p = 0; p < PF; ++p) {
+        if (k + p < nseg) compute(p, k + p);
+        load(p, k + p + PF);
+      }
     }
   }
 

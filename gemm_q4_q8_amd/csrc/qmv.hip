@@ -1,6 +1,6 @@
-// Tiled quantised products on gfx950: the decode GEMV and its batched twins,
-// the fused gate/up with SiLU, the LM head with argmax (dot path, 1..8
-// columns), and the 16-column prefill GEMM on the matrix cores.
+// Tiled quantised products on gfx950: the decode GEMV and its batched twins
+// (1..8 columns), the fused gate/up with SiLU, the LM head with argmax, and
+// the 16-column prefill GEMM.
 //
 // What is computed ("Engine and kernels", Kernel families and What each
 // trick bought): y = W x over Q4_0 / Q8_0 blocks dequantised in registers,
@@ -8,19 +8,19 @@
 // before writing, greedy argmax with lowest-index ties, and a 16-column GEMM
 // with split-K pinned per shape.
 //
-// Dot path (1..8 columns): one workgroup per (row group, K segment); the
-// unit's work (activation staging, weight streaming, reduction, epilogue)
-// is dot_unit.h.  K segments per shape: gemv_segments() below.
-//
-// Matrix-core path (16 columns): WKT waves take WKT consecutive K segments
-// of RT row tiles; per block and row tile one v_mfma_f32_16x16x32_f16 with
-// A = activations (16 columns x 32), B = the block's weights, the block
-// scale applied to the 4 outputs each lane holds; waves of a workgroup, then
-// splits, summed in index order.
+// One kernel, dot_kernel: a workgroup per (row group, K segment) runs the
+// work unit of dot_unit.h (activation staging, weight streaming, block
+// products on the matrix cores, segment reduction, epilogue); the argmax
+// across row groups is added here.  K segments per shape: gemv_segments()
+// (1..8 columns, the same for every column count) and gemm16_splits().
 #include "common.h"
 #include "dot_unit.h"
 #include "internal.h"
 #include "qgemm.h"
+#ifdef GEMM16_EXP
+#include <stdio.h>
+#include <stdlib.h>
+#endif
 
 namespace qg {
 
@@ -88,196 +88,6 @@ __global__ void __launch_bounds__(WKT * 64) dot_kernel(DotArgs a) {
   }
 }
 
-// ------------------------------------------------------- matrix-core path
-struct MmaArgs {
-  const uint8_t *qs, *d;
-  int64_t rows, cols;
-  int NT, KT;
-  int Q;              // K segments: WKT per workgroup, S workgroups per row group
-  int S;
-  int G;              // row groups of RT row tiles
-  int64_t units;
-  int64_t per_xcd;
-  int nkt_max;
-  const float *X;
-  int64_t ldx;
-  float *Y;
-  int64_t ldy;
-  float *part;        // [S][NT*16][16]
-  uint32_t *cnt;
-};
-
-template <int QT, int EPI, int RT, int PF, int WKT>
-__global__ void __launch_bounds__(WKT * 64) mma_kernel(MmaArgs a) {
-  constexpr int NC = 16;
-  constexpr int NTHR = WKT * 64;
-  constexpr int TB = QTraits<QT>::tile_bytes;
-  constexpr int QW = (QT == Q4) ? 1 : 2;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ uint32_t flag;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wk = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t u = xcd_unit(a.per_xcd);
-  if (u >= a.units) return;
-  const int g = (int)(u / a.S), s = (int)(u % a.S);
-  const int q0 = s * WKT;
-  const int q1 = (q0 + WKT < a.Q) ? q0 + WKT : a.Q;
-  const int kt0 = seg_begin(q0, a.KT, a.Q);
-  const int kt1 = seg_begin(q1, a.KT, a.Q);
-  const int nkt = kt1 - kt0;
-  const int q = q0 + wk;
-  const int wb = q < q1 ? seg_begin(q, a.KT, a.Q) : kt1;
-  const int we = q < q1 ? seg_begin(q + 1, a.KT, a.Q) : kt1;
-
-  _Float16 *xs = (_Float16 *)smem;
-  float *red = (float *)smem;
-  const int r = lane & 15, sl = lane >> 4;
-  const int64_t rt_base = (int64_t)g * RT;
-
-  u4 wq[PF][RT][QW];
-  u2 wd[PF][RT];
-  const uint32_t lane_off = (uint32_t)lane * 16u, d_off = (uint32_t)r * 8u;
-  auto load = [&](int slot, int kt) {
-#pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const int64_t trow = (rt_base + t < a.NT) ? rt_base + t : (int64_t)a.NT - 1;
-      const int64_t tile = trow * a.KT + kt;
-      const uint8_t *tq = a.qs + tile * TB;
-      const uint8_t *td = a.d + tile * TILE_D_BYTES;
-      wq[slot][t][0] = ld_stream(tq + lane_off);
-      if constexpr (QW == 2) wq[slot][t][QW - 1] = ld_stream(tq + 1024 + lane_off);
-      wd[slot][t] = ld_stream2(td + d_off);
-    }
-  };
-  const int nseg = we - wb;
-  if (nseg > 0) {
-#pragma unroll
-    for (int p = 0; p < PF; ++p) load(p, wb + (p < nseg ? p : nseg - 1));
-  }
-
-  {
-    constexpr int XB = 4;
-    const int nvec = nkt * TILE_BLOCKS * NC * 4;
-    for (int v0 = tid; v0 < nvec; v0 += XB * NTHR) {
-      float4 lo[XB], hi[XB];
-      bool ok[XB];
-#pragma unroll
-      for (int b = 0; b < XB; ++b) {
-        const int v = v0 + b * NTHR;
-        const int qq = v & 3, c = (v >> 2) % NC, bl = (v >> 2) / NC;
-        const int64_t k = ((int64_t)kt0 * TILE_BLOCKS + bl) * 32 + qq * 8;
-        ok[b] = v < nvec && k < a.cols;
-        const float4 *p = (const float4 *)(a.X + (ok[b] ? (int64_t)c * a.ldx + k : 0));
-        lo[b] = p[0];
-        hi[b] = p[1];
-      }
-#pragma unroll
-      for (int b = 0; b < XB; ++b) {
-        const int v = v0 + b * NTHR;
-        if (v < nvec) {
-          h8 hv = {0, 0, 0, 0, 0, 0, 0, 0};
-          if (ok[b]) hv = cvt8(lo[b], hi[b]);
-          *(h8 *)(xs + (size_t)v * 8) = hv;
-        }
-      }
-    }
-  }
-  __syncthreads();
-
-  float acc[RT][4];
-#pragma unroll
-  for (int t = 0; t < RT; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[t][i] = 0.0f;
-
-  const Q4Magic mg = q4_magic();
-  auto compute = [&](int slot, int kt) {
-    const int bl0 = (kt - kt0) * TILE_BLOCKS;
-#pragma unroll
-    for (int j = 0; j < TILE_BLOCKS; ++j) {
-      const h8 A = *(const h8 *)(xs + ((size_t)(bl0 + j) * 16 + r) * 32 + sl * 8);
-#pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        h2 w[4];
-        if constexpr (QT == Q4) unpack_q4(wq[slot][t][0][j], w, mg);
-        else unpack_q8(wq[slot][t][j >> 1][(j & 1) * 2], wq[slot][t][j >> 1][(j & 1) * 2 + 1], w);
-        h8 B = {w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
-        const f4 D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        const float dj = scale_of(wd[slot][t], j);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(dj, D[i], acc[t][i]);
-      }
-    }
-  };
-
-  int k = 0;
-  for (; k + 2 * PF <= nseg; k += PF) {
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      compute(p, wb + k + p);
-      load(p, wb + k + p + PF);
-    }
-  }
-#pragma unroll
-  for (int p = 0; p < PF; ++p) {
-    if (k + p < nseg) {
-      compute(p, wb + k + p);
-      if (k + p + PF < nseg) load(p, wb + k + p + PF);
-    }
-  }
-#pragma unroll
-  for (int p = 0; p < PF; ++p)
-    if (k + PF + p < nseg) compute(p, wb + k + PF + p);
-
-  // per-wave partials -> LDS: lane holds D[4 sl + i][r] = (column 4 sl + i, row r)
-  __syncthreads();
-#pragma unroll
-  for (int t = 0; t < RT; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red[((wk * RT + t) * 16 + r) * 16 + sl * 4 + i] = acc[t][i];
-  __syncthreads();
-
-  const int64_t rows_pad = (int64_t)a.NT * 16;
-  constexpr int NOUT = RT * 16 * NC;
-  const int nw = q1 - q0;
-  auto red_at = [&](int w, int t, int rr, int c) -> float { return red[((w * RT + t) * 16 + rr) * NC + c]; };
-  auto emit = [&](int t, int rr, int c, float v) {
-    const int64_t row = (rt_base + t) * 16 + rr;
-    if (row >= a.rows) return;
-    float *yp = a.Y + (int64_t)c * a.ldy + row;
-    if constexpr (EPI == EPI_STORE) *yp = v;
-    else *yp = *yp + v;
-  };
-
-  if (a.S == 1) {
-    for (int o = tid; o < NOUT; o += NTHR) {
-      const int c = o % NC, rr = (o / NC) % 16, t = o / (16 * NC);
-      float x = red_at(0, t, rr, c);
-      for (int w = 1; w < nw; ++w) x += red_at(w, t, rr, c);
-      emit(t, rr, c, x);
-    }
-  } else {
-    for (int o = tid; o < NOUT; o += NTHR) {
-      const int c = o % NC, rr = (o / NC) % 16, t = o / (16 * NC);
-      if (rt_base + t >= a.NT) continue;
-      const int64_t row = (rt_base + t) * 16 + rr;
-      float x = red_at(0, t, rr, c);
-      for (int w = 1; w < nw; ++w) x += red_at(w, t, rr, c);
-      st_agent(a.part + ((int64_t)s * rows_pad + row) * NC + c, x);
-    }
-    if (!arrive_last(a.cnt + g, (uint32_t)a.S, &flag)) return;
-    for (int o = tid; o < NOUT; o += NTHR) {
-      const int c = o % NC, rr = (o / NC) % 16, t = o / (16 * NC);
-      if (rt_base + t >= a.NT) continue;
-      const int64_t row = (rt_base + t) * 16 + rr;
-      float x = ld_agent(a.part + row * NC + c);
-      for (int ss = 1; ss < a.S; ++ss) x += ld_agent(a.part + ((int64_t)ss * rows_pad + row) * NC + c);
-      emit(t, rr, c, x);
-    }
-  }
-}
-
 // ---------------------------------------------------------------- host side
 constexpr int DOT_STREAMS = 2048;     // (row tile, segment, matrix) weight streams
 constexpr size_t DOT_X_LDS = 65536;   // staged activations per workgroup
@@ -303,17 +113,18 @@ int gemv_segments(int64_t rows, int64_t cols, int nmat, int ncols_max) {
   return (int)s;
 }
 
-// Splits of K for the matrix-core path (16 columns of f16 activations per
-// workgroup in at most 64 KiB of LDS, two tile columns per wave at least).
+// K segments of the 16-column GEMM (its activations stream through LDS in
+// chunks, so the segment length is free): about GEMM16_STREAMS (row tile,
+// segment) weight streams, at least 4 tile columns per segment.
+constexpr int GEMM16_STREAMS = 2048;
 int gemm16_splits(int64_t rows, int64_t cols) {
   const int64_t NT = cdiv(rows, 16), KT = cdiv(cols / 32, 4);
-  int64_t s = cdiv(2048, NT);
-  const int64_t cap = KT / 8;
-  if (s > cap) s = cap;
-  const int64_t lds_min = cdiv(KT, 16);
-  if (s < lds_min) s = lds_min;
+#ifdef GEMM16_EXP
+  if (const char *e = getenv("QG_EXP_G16S")) return atoi(e);
+#endif
+  int64_t s = GEMM16_STREAMS / NT;
+  if (s > KT / 4) s = KT / 4;
   if (s < 1) s = 1;
-  if (s > KT) s = KT;
   return (int)s;
 }
 
@@ -391,7 +202,9 @@ static int launch_dot_t(const QmvCall &c, int S) {
   const size_t need = off + (S > 1 ? (size_t)S * NMAT * NTu * 16 * NC * 4 : 0);
   if (need > c.ws_bytes) return QG_EWORKSPACE;
 
-  const size_t lds = (size_t)cdiv(KT, S) * TILE_BLOCKS * NC * 64;
+  // staged activations: the whole segment, or (16 columns) two chunks of
+  // PF tile columns
+  const size_t lds = NC >= 16 ? (size_t)2 * PF * TILE_BLOCKS * NC * 64 : (size_t)cdiv(KT, S) * TILE_BLOCKS * NC * 64;
   if (lds > LDS_HARD - 1024) return QG_EUNSUPPORTED;
   auto kern = dot_kernel<QT, NC, NMAT, EPI, RT, PF, WKT, MF>;
   static size_t granted = 65536;  // per instantiation; only ever raised
@@ -445,58 +258,29 @@ static int dispatch_silu(const QmvCall &c, int S) {
   return QG_ESHAPE;
 }
 
-template <int QT, int EPI, int RT, int PF, int WKT>
-static int launch_mma_t(const QmvCall &c) {
+// 16 columns: the shared dot unit on the matrix cores (one row tile per
+// wave, PF = 4 tile columns in flight; measured best on the prefill shapes).
+template <int QT, int EPI>
+static int launch_gemm16(const QmvCall &c) {
   const int S = gemm16_splits(c.rows, c.cols);
-  const int Q = WKT * S;
-  const int64_t NT = cdiv(c.rows, 16), KT = cdiv(c.cols / 32, 4);
-  MmaArgs a;
-  a.qs = (const uint8_t *)c.qs[0];
-  a.d = (const uint8_t *)c.d[0];
-  a.rows = c.rows;
-  a.cols = c.cols;
-  a.NT = (int)NT;
-  a.KT = (int)KT;
-  a.Q = Q;
-  a.S = S;
-  a.G = (int)cdiv(NT, RT);
-  a.units = (int64_t)a.G * S;
-  a.per_xcd = cdiv(a.units, 8);
-  int nkt_max = 0;
-  for (int s = 0; s < S; ++s) {
-    const int q0 = s * WKT, q1 = q0 + WKT < Q ? q0 + WKT : Q;
-    const int n = seg_begin(q1, (int)KT, Q) - seg_begin(q0, (int)KT, Q);
-    if (n > nkt_max) nkt_max = n;
+#ifdef GEMM16_EXP
+  if (const char *e = getenv("QG_EXP_G16")) {
+    int rt = 0, w = 0, pf = 0;
+    if (sscanf(e, "%d,%d,%d", &rt, &w, &pf) == 3) {
+#define G16(R, W, P) if (rt == R && w == W && pf == P) return launch_dot_t<QT, 16, 1, EPI, R, P, W, true>(c, S);
+      G16(1, 8, 2) G16(1, 8, 4) G16(2, 8, 2) G16(2, 8, 4) G16(2, 4, 2) G16(2, 16, 2) G16(1, 16, 4)
+      return QG_EUNSUPPORTED;
+    }
   }
-  a.nkt_max = nkt_max;
-  a.X = c.X;
-  a.ldx = c.ldx;
-  a.Y = c.Y;
-  a.ldy = c.ldy;
-  if (S > 1 && (size_t)a.G + 1 > WS_SYNC_WORDS) return QG_EUNSUPPORTED;
-  uint8_t *ws = (uint8_t *)c.ws;
-  a.cnt = (uint32_t *)ws + 1;
-  a.part = (float *)(ws + QG_WS_SYNC_BYTES);
-  const size_t need = QG_WS_SYNC_BYTES + (S > 1 ? (size_t)S * NT * 16 * 16 * 4 : 0);
-  if (need > c.ws_bytes) return QG_EWORKSPACE;
-  const size_t x_bytes = (size_t)nkt_max * TILE_BLOCKS * 16 * 64;
-  const size_t r_bytes = (size_t)WKT * RT * 16 * 16 * 4;
-  const size_t lds = x_bytes > r_bytes ? x_bytes : r_bytes;
-  if (lds > LDS_HARD - 1024) return QG_EUNSUPPORTED;
-  auto kern = mma_kernel<QT, EPI, RT, PF, WKT>;
-  static size_t granted = 65536;
-  int st = grant_lds((const void *)kern, lds, granted);
-  if (st) return st;
-  clear_hip_error();
-  hipLaunchKernelGGL(kern, dim3((unsigned)(a.per_xcd * 8)), dim3(WKT * 64), lds, c.stream, a);
-  return launch_status();
+#endif
+  return launch_dot_t<QT, 16, 1, EPI, 1, 4, 8, true>(c, S);
 }
 
 template <int QT>
 static int dispatch_qt(const QmvCall &c) {
   if (c.ncols == 16) {
-    if (c.epi == EPI_STORE) return launch_mma_t<QT, EPI_STORE, 4, 2, 4>(c);
-    if (c.epi == EPI_ACC) return launch_mma_t<QT, EPI_ACC, 4, 2, 4>(c);
+    if (c.epi == EPI_STORE) return launch_gemm16<QT, EPI_STORE>(c);
+    if (c.epi == EPI_ACC) return launch_gemm16<QT, EPI_ACC>(c);
     return QG_EUNSUPPORTED;
   }
   switch (c.epi) {
