@@ -70,6 +70,8 @@ struct DotArgs {
   float *out_val;
   uint32_t *ready;    // fused FFN: producer sets ready[g]; consumer waits on ready[kt]
   uint32_t *err;      // fused FFN: set when a wait gave up
+  const int32_t *xmap, *ymap;  // MoE: column c reads X column xmap[c], writes Y column ymap[c]
+  int64_t xspan;      // bytes of X the columns may read (0: the ncols columns)
 };
 
 // Returns true when this workgroup emitted the outputs of row group g (its
@@ -115,7 +117,7 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   // segment or the matrix reads zeros
   const int nvec = nkt * TILE_BLOCKS * NC * 4;  // 8-value pieces of the segment
   const __amdgpu_buffer_rsrc_t rx =
-      buf_range(a.X, (uint32_t)(((int64_t)(a.ncols - 1) * a.ldx + a.cols) * 4));
+      buf_range(a.X, (uint32_t)(a.xspan ? a.xspan : ((int64_t)(a.ncols - 1) * a.ldx + a.cols) * 4));
   // piece v of the `span` pieces from tile column rel0 on: (block, column,
   // 8 k) -> byte offset in X, or past any range (reads zeros) when it lies
   // outside the span, the segment or the matrix
@@ -123,7 +125,8 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
     const int qq = v & 3, c = (v >> 2) % NC, bl = (v >> 2) / NC;
     const int64_t k = ((int64_t)(kt0 + rel0) * TILE_BLOCKS + bl) * 32 + qq * 8;
     const bool ok = v < span && rel0 * TILE_BLOCKS + bl < nkt * TILE_BLOCKS && k < a.cols && c < a.ncols;
-    return ok ? (uint32_t)(((int64_t)c * a.ldx + k) * 4) : 0xFFFFFFC0u;
+    const int64_t xc = ok && a.xmap ? a.xmap[c] : c;
+    return ok ? (uint32_t)((xc * a.ldx + k) * 4) : 0xFFFFFFC0u;
   };
   auto x_ld = [&](int v, int rel0, int span, u4 &lo, u4 &hi) {
     const uint32_t o = x_off(v, rel0, span);
@@ -347,11 +350,11 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
 
   auto emit = [&](int t, int c, const float (&v)[NMAT]) {
     const int64_t row = (rt_base + t) * 16 + r;
-    if (rt_base + t >= a.NT || row >= a.rows) return;
+    if (rt_base + t >= a.NT || row >= a.rows || c >= a.ncols) return;
     if constexpr (EPI == EPI_ARGMAX) {
       if (ranks_before(v[0], (int32_t)row, bv, bi)) { bv = v[0]; bi = (int32_t)row; }
     } else {
-      float *yp = a.Y + (int64_t)c * a.ldy + row;
+      float *yp = a.Y + (int64_t)(a.ymap ? a.ymap[c] : c) * a.ldy + row;
       float out;
       if constexpr (EPI == EPI_STORE) {
         out = v[0];
@@ -425,7 +428,7 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   if constexpr (PH == PH_PRODUCE) {
     // h rows of row group g are out: raise its flag once every wave's
     // stores are acknowledged
-    if (emitted) {
+    if (emitted && a.ready) {
       __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (tid == 0) st_agent_u32(a.ready + g, 1u);

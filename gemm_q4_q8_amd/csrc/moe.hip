@@ -6,31 +6,34 @@
 // Experts are stacked by role ("A 235B model in a browser window": all gate
 // matrices in one tensor, all up in a second, all down in a third).
 //
-//  1. router: f32 logits (f32 operands, f32 FMA), then the last workgroup
-//     picks the top k per token (value descending, index ascending), the
-//     softmax weights, and a work list of the distinct experts in index
-//     order, each with its routed slots (slot = token * k + rank).
-//  2. gate/up: one workgroup per (listed expert, row group) reads that
-//     expert's gate and up tiles once for all of its slots and writes
-//     h = silu(g) * u per slot.
-//  3. down: one workgroup per (listed expert, row group) writes z = D h per
+//  1. router: one wave per (expert, token) forms that f32 logit (f32
+//     operands, f32 FMA); the last workgroup picks the top k per token
+//     (value descending, index ascending), the softmax weights, and a work
+//     list in expert index order of entries of at most 4 routed slots of one
+//     expert (slot = token * k + rank).
+//  2. gate/up: the work unit of dot_unit.h over (listed expert, row group, K
+//     segment): each expert's gate and up tiles are read once for all of its
+//     slots (the unit's activation columns are the routed tokens' x, through
+//     a column map) and h = silu(g) * u is written per slot.
+//  3. down: the same unit over (listed expert, row group) writes z = D h per
 //     slot; the last workgroup to finish a row group forms, per token,
-//     sum_k p_k z_k in rank order, adds the shared expert, and adds the
-//     total to Y once.
+//     sum_k p_k z_k in rank order, adds the shared expert, and adds the total
+//     to Y once.
 // Workgroups beyond the listed experts exit at once (the grid is the worst
 // case, the list is on the device).
+#include <string.h>
+
 #include "common.h"
+#include "dot_unit.h"
 #include "internal.h"
 #include "qgemm.h"
 
 namespace qg {
 
-constexpr int MW = 4;              // waves per workgroup
-constexpr int MTHR = MW * 64;
-constexpr int EPW = 4;             // router experts per wave
-constexpr int TMAX = 16;           // tokens per call
-constexpr int RT_GU = 1;           // row tiles per gate/up workgroup
-constexpr int RT_DN = 2;           // row tiles per down workgroup
+constexpr int RW = 16;      // router: experts (waves) per workgroup, = TMAX
+constexpr int TMAX = 16;    // tokens per call
+constexpr int GU_WKT = 2;   // gate/up: row tiles per workgroup
+constexpr int DN_WKT = 8;   // down: row tiles per workgroup (128 rows)
 
 struct MoeArgs {
   int64_t H, F, SF, Fmax;
@@ -45,27 +48,57 @@ struct MoeArgs {
   int64_t ldy;
   int32_t *topk_idx;
   float *topk_w;
-  uint32_t *rcnt, *dcnt, *nused;
-  float *logits, *pw, *hbuf, *zbuf;
+  uint32_t *rcnt, *dcnt, *gcnt, *nused;
+  float *logits, *pw, *hbuf, *zbuf, *gpart;
   int32_t *sel, *used_e, *used_cnt, *used_slot;
-  int gu_groups, sh_gu_units, dn_groups, sh_dn_units;
+  int S_gu, G_gu, G_dn;   // gate/up K segments and row groups (at Fmax rows); down row groups
+  int nsh;                // shared-expert entries (tokens in groups of the unit width)
+  int64_t gpart_per;      // gate/up partial floats per listed expert
 };
 
 static size_t a256(size_t v) { return (v + 255) & ~size_t(255); }
+__host__ __device__ static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Column capacity of the expert units: a work-list entry holds at most this
+// many routed slots of one expert (an expert with more gets several
+// entries, each reading its weights once for its slots).
+static int moe_nc(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : 4; }
+// gate/up K segments: short streams at one token (latency-bound), longer
+// ones when more columns share each weight tile
+static int moe_s_gu(int64_t H, int T) {
+  const int64_t KT = H / 128;
+  int64_t s = T <= 2 ? KT / 4 : KT / 8;
+  return (int)(s < 1 ? 1 : s);
+}
 
 struct MoeLayout {
-  size_t rcnt, dcnt, nused, logits, sel, pw, used_e, used_cnt, used_slot, hbuf, zbuf, total;
+  size_t nused, logits, sel, pw, used_e, used_cnt, used_slot, hbuf, zbuf, gpart, total;
+  int64_t umax;  // work-list entries at most
+  size_t rcnt_w, dcnt_w, gcnt_w, sync_words;  // counter word offsets
+  int S_gu, G_gu, G_dn, nsh;
+  int64_t gpart_per;
 };
 
 static MoeLayout moe_layout(const qg_moe *m, int T) {
   MoeLayout L;
   const int64_t Fmax = m->sh_ffn > m->ffn ? m->sh_ffn : m->ffn;
-  const int64_t umax = (int64_t)m->n_expert < (int64_t)T * m->top_k ? m->n_expert : (int64_t)T * m->top_k;
+  const int nc = moe_nc(T);
+  // work-list entries: each holds at least one slot and at most nc of one expert
+  const int64_t by_e = (int64_t)m->n_expert * ((T + nc - 1) / nc);
+  const int64_t umax = (int64_t)T * m->top_k < by_e ? (int64_t)T * m->top_k : by_e;
   const int64_t slots = (int64_t)T * m->top_k + T;
-  // counters (in the shared counter words): the router's, then one per
-  // down-projection row group; data after them
-  L.rcnt = 0;
-  L.dcnt = 4;
+  L.umax = umax;
+  L.S_gu = moe_s_gu(m->hidden, T);
+  L.G_gu = (int)cdiv(Fmax / 16, GU_WKT);
+  L.G_dn = (int)cdiv(m->hidden / 16, DN_WKT);
+  L.gpart_per = L.S_gu > 1 ? (int64_t)L.S_gu * 2 * Fmax * nc : 0;
+  // counters (in the shared counter words): the router's, one per down row
+  // group, one per (listed expert, gate/up row group)
+  L.rcnt_w = 0;
+  L.dcnt_w = 4;
+  L.gcnt_w = L.dcnt_w + (size_t)L.G_dn;
+  L.nsh = m->sh_ffn > 0 ? (T + nc - 1) / nc : 0;  // shared-expert entries
+  L.sync_words = L.gcnt_w + (size_t)(umax + L.nsh) * L.G_gu;
   size_t o = QG_WS_SYNC_BYTES;
   L.nused = o; o += 256;
   L.logits = o; o += a256((size_t)T * m->n_expert * 4);
@@ -76,6 +109,7 @@ static MoeLayout moe_layout(const qg_moe *m, int T) {
   L.used_slot = o; o += a256((size_t)umax * TMAX * 4);
   L.hbuf = o; o += a256((size_t)slots * Fmax * 4);
   L.zbuf = o; o += a256((size_t)slots * m->hidden * 4);
+  L.gpart = o; o += a256((size_t)(umax + L.nsh) * L.gpart_per * 4);
   L.total = o;
   return L;
 }
@@ -83,71 +117,67 @@ static MoeLayout moe_layout(const qg_moe *m, int T) {
 size_t moe_ws_bytes(const qg_moe *m, int ntok) { return moe_layout(m, ntok).total; }
 
 // ------------------------------------------------------------ 1. router
-template <int NTC>
-__global__ void __launch_bounds__(MTHR) moe_router_kernel(MoeArgs a) {
+// One wave per (expert, token) pair, the pairs of an expert adjacent (its
+// router row is then read from L2 by all but the first): each wave forms
+// one logit.  The last workgroup stages the logits in LDS (dynamic, T x
+// n_expert floats) and selects, one wave per token (T <= RW).
+template <int NTC, int NCAP>
+__global__ void __launch_bounds__(RW * 64) moe_router_kernel(MoeArgs a) {
+  constexpr int NTHR = RW * 64;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  float *s_l = (float *)smem;
   __shared__ uint32_t flag;
   __shared__ int32_t s_sel[TMAX * 8];
-  __shared__ int32_t s_cnt[MTHR];
+  __shared__ int32_t s_cnt[1024], s_off[1024];  // per expert (n_expert <= 1024)
+  __shared__ int32_t s_wtot[RW];
   const int tid = threadIdx.x, lane = tid & 63, wk = tid >> 6;
-  const int e0 = (blockIdx.x * MW + wk) * EPW;
-  float acc[EPW][NTC];
+  {
+    const int64_t item = (int64_t)blockIdx.x * RW + wk;
+    const int e = (int)(item / a.T), t = (int)(item % a.T);
+    if (e < a.E) {
+      float v = 0.0f;
+      for (int64_t h0 = 0; h0 < a.H; h0 += 2048) {
+        float4 rv[8], xv[8];
 #pragma unroll
-  for (int i = 0; i < EPW; ++i)
+        for (int j = 0; j < 8; ++j) {
+          const int64_t h = h0 + ((int64_t)j * 64 + lane) * 4;
+          rv[j] = h < a.H ? *(const float4 *)(a.R + (int64_t)e * a.H + h) : float4{0, 0, 0, 0};
+          xv[j] = h < a.H ? *(const float4 *)(a.X + (int64_t)t * a.ldx + h) : float4{0, 0, 0, 0};
+        }
 #pragma unroll
-    for (int t = 0; t < NTC; ++t) acc[i][t] = 0.0f;
-
-  for (int64_t h = lane * 4; h < a.H; h += 256) {
-    float4 rv[EPW];
-#pragma unroll
-    for (int i = 0; i < EPW; ++i)
-      rv[i] = (e0 + i < a.E) ? *(const float4 *)(a.R + (int64_t)(e0 + i) * a.H + h) : float4{0, 0, 0, 0};
-#pragma unroll
-    for (int t = 0; t < NTC; ++t) {
-      if (t < a.T) {
-        const float4 xv = *(const float4 *)(a.X + (int64_t)t * a.ldx + h);
-#pragma unroll
-        for (int i = 0; i < EPW; ++i) {
-          float v = acc[i][t];
-          v = __builtin_fmaf(rv[i].x, xv.x, v);
-          v = __builtin_fmaf(rv[i].y, xv.y, v);
-          v = __builtin_fmaf(rv[i].z, xv.z, v);
-          v = __builtin_fmaf(rv[i].w, xv.w, v);
-          acc[i][t] = v;
+        for (int j = 0; j < 8; ++j) {
+          v = __builtin_fmaf(rv[j].x, xv[j].x, v);
+          v = __builtin_fmaf(rv[j].y, xv[j].y, v);
+          v = __builtin_fmaf(rv[j].z, xv[j].z, v);
+          v = __builtin_fmaf(rv[j].w, xv[j].w, v);
         }
       }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+      if (lane == 0) st_agent(a.logits + (int64_t)t * a.E + e, v);
     }
   }
-#pragma unroll
-  for (int i = 0; i < EPW; ++i)
-#pragma unroll
-    for (int t = 0; t < NTC; ++t) {
-      if (t < a.T) {
-        float v = acc[i][t];
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-        if (lane == 0 && e0 + i < a.E) st_agent(a.logits + (int64_t)t * a.E + e0 + i, v);
-      }
-    }
   if (!arrive_last(a.rcnt, gridDim.x, &flag)) return;
 
   // ---- top-k and softmax weights, one wave per token
-  for (int t = wk; t < a.T; t += MW) {
-    float lv[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int e = lane + 64 * j;
-      lv[j] = e < a.E ? ld_agent(a.logits + (int64_t)t * a.E + e) : 0.0f;
-    }
-    uint32_t taken = 0;
-    float selv[8];
-    int32_t seli[8];
+  for (int i = tid; i < a.T * a.E; i += NTHR) s_l[i] = ld_agent(a.logits + i);
+  __syncthreads();
+  if (wk < a.T) {
+    const int t = wk;
+    const float *lt = s_l + (int64_t)t * a.E;
+    const int nj = (a.E + 63) / 64;
+    uint32_t taken = 0;  // bit j: expert lane + 64 j is already selected
+    float mx = 0.0f, sumsel = 0.0f;
+    int32_t my_e = 0;    // lane kk: the expert of rank kk
     for (int kk = 0; kk < a.k; ++kk) {
       float bv = __builtin_nanf("");
       int32_t bi = 0x7fffffff;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int e = lane + 64 * j;
-        if (e < a.E && !((taken >> j) & 1u) && ranks_before(lv[j], e, bv, bi)) { bv = lv[j]; bi = e; }
+      for (int j = 0; j < nj; ++j) {
+        const int ee = lane + 64 * j;
+        if (ee < a.E && !((taken >> j) & 1u)) {
+          const float v = lt[ee];
+          if (ranks_before(v, ee, bv, bi)) { bv = v; bi = ee; }
+        }
       }
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) {
@@ -156,305 +186,270 @@ __global__ void __launch_bounds__(MTHR) moe_router_kernel(MoeArgs a) {
         if (ranks_before(ov, oi, bv, bi)) { bv = ov; bi = oi; }
       }
       if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      selv[kk] = bv;
-      seli[kk] = bi;
+      if (kk == 0) mx = bv;  // the largest logit
+      sumsel += expf(bv - mx);
+      if (lane == kk) my_e = bi;
+      if (lane == 0) s_sel[t * a.k + kk] = bi;
     }
-    const float mx = selv[0];
-    float sum = 0.0f;
-    if (a.norm) {
-      for (int kk = 0; kk < a.k; ++kk) sum += expf(selv[kk] - mx);
-    } else {
+    float sum = sumsel;
+    if (!a.norm) {
       float part = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (lane + 64 * j < a.E) part += expf(lv[j] - mx);
+      for (int j = 0; j < nj; ++j)
+        if (lane + 64 * j < a.E) part += expf(lt[lane + 64 * j] - mx);
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
       sum = part;
     }
-    if (lane == 0) {
-      for (int kk = 0; kk < a.k; ++kk) {
-        const float p = expf(selv[kk] - mx) / sum;
-        a.sel[t * a.k + kk] = seli[kk];
-        a.pw[t * a.k + kk] = p;
-        s_sel[t * a.k + kk] = seli[kk];
-        if (a.topk_idx) a.topk_idx[t * a.k + kk] = seli[kk];
-        if (a.topk_w) a.topk_w[t * a.k + kk] = p;
-      }
+    if (lane < a.k) {
+      const int kk = lane;
+      const int32_t ee = my_e;
+      const float p = expf(lt[ee] - mx) / sum;
+      a.sel[t * a.k + kk] = ee;
+      a.pw[t * a.k + kk] = p;
+      if (a.topk_idx) a.topk_idx[t * a.k + kk] = ee;
+      if (a.topk_w) a.topk_w[t * a.k + kk] = p;
     }
   }
   __syncthreads();
 
-  // ---- work list: used experts in index order, each with its slots in order
+  // ---- work list: entries of at most NCAP slots of one expert, experts in
+  // index order, an expert's slots in slot order.  Per-expert counts by LDS
+  // atomics, entry offsets by a scan over the experts.
   const int nslot = a.T * a.k;
-  const int ept = (a.E + MTHR - 1) / MTHR;
-  const int e_lo = tid * ept;
-  const int e_hi = (e_lo + ept < a.E) ? e_lo + ept : a.E;
-  int mine = 0;
-  for (int e = e_lo; e < e_hi; ++e) {
-    bool used = false;
-    for (int q = 0; q < nslot; ++q) used |= (s_sel[q] == e);
-    mine += used ? 1 : 0;
-  }
-  s_cnt[tid] = mine;
+  for (int ee = tid; ee < a.E; ee += NTHR) s_cnt[ee] = 0;
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < MTHR; ++i) { const int c = s_cnt[i]; s_cnt[i] = run; run += c; }
-    *a.nused = (uint32_t)run;
-  }
+  if (tid < nslot) atomicAdd(&s_cnt[s_sel[tid]], 1);
   __syncthreads();
-  int u = s_cnt[tid];
-  for (int e = e_lo; e < e_hi; ++e) {
-    int c = 0;
-    for (int q = 0; q < nslot; ++q)
-      if (s_sel[q] == e) a.used_slot[u * TMAX + c++] = q;
-    if (c) { a.used_e[u] = e; a.used_cnt[u] = c; ++u; }
+  int run = 0;  // entries of the experts before this pass
+  for (int base = 0; base < a.E; base += NTHR) {
+    const int ee = base + tid;
+    const int ne = ee < a.E ? (s_cnt[ee] + NCAP - 1) / NCAP : 0;
+    int incl = ne;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) s_wtot[wk] = incl;
+    __syncthreads();
+    int before = run;
+    for (int w = 0; w < wk; ++w) before += s_wtot[w];
+    int total = run;
+    for (int w = 0; w < RW; ++w) total += s_wtot[w];
+    if (ee < a.E) s_off[ee] = before + incl - ne;
+    __syncthreads();
+    run = total;
+  }
+  if (tid == 0) *a.nused = (uint32_t)run;
+  // each slot: its position among its expert's slots -> (entry, column)
+  if (tid < nslot) {
+    const int ee = s_sel[tid];
+    int pos = 0;
+    for (int q = 0; q < tid; ++q) pos += s_sel[q] == ee ? 1 : 0;
+    const int u = s_off[ee] + pos / NCAP, col = pos % NCAP;
+    a.used_slot[u * TMAX + col] = tid;
+    if (col == 0) {
+      const int left = s_cnt[ee] - pos;
+      a.used_e[u] = ee;
+      a.used_cnt[u] = left < NCAP ? left : NCAP;
+    }
   }
 }
 
-// ------------------------------------------------- 2./3. grouped experts
-// NMAT = 2: gate/up + SiLU into hbuf.  NMAT = 1: down into zbuf + combine.
-template <int QT, int NCM, int NMAT, int RT>
-__global__ void __launch_bounds__(MTHR) moe_expert_kernel(MoeArgs a) {
+// --------------------------------------------- 2./3. grouped expert units
+// The work-list entry u (or, for u >= nused, the shared expert's entry of
+// tokens (u - nused) * NC ...) of a unit: its matrices, rows, and column
+// maps (activation column -> token or slot, output column -> slot).
+// Returns the column count, 0 when the unit has no entry.
+template <bool GATEUP, int NC>
+__device__ __forceinline__ int moe_expert(const MoeArgs &a, int u, DotArgs &d, int32_t *s_x, int32_t *s_y) {
+  const int tid = threadIdx.x;
+  const int nused = (int)*a.nused;
+  const int nsh = a.SF > 0 ? (a.T + NC - 1) / NC : 0;
+  if (u >= nused + nsh) return 0;
+  const bool shared = u >= nused;
+  int nc;
+  if (shared) {
+    const int t0 = (u - nused) * NC;
+    nc = a.T - t0 < NC ? a.T - t0 : NC;
+    if (tid < nc) {
+      s_x[tid] = GATEUP ? t0 + tid : a.T * a.k + t0 + tid;
+      s_y[tid] = a.T * a.k + t0 + tid;
+    }
+    if (GATEUP) {
+      d.qs0 = a.sgq; d.qs1 = a.suq; d.d0 = a.sgd; d.d1 = a.sud;
+    } else {
+      d.qs0 = d.qs1 = a.sdq; d.d0 = d.d1 = a.sdd;
+    }
+  } else {
+    const int e = a.used_e[u];
+    nc = a.used_cnt[u];
+    if (tid < nc) {
+      const int q = a.used_slot[u * TMAX + tid];
+      s_x[tid] = GATEUP ? q / a.k : q;
+      s_y[tid] = q;
+    }
+    if (GATEUP) {
+      d.qs0 = a.gq + (int64_t)e * a.gu_qs_stride; d.qs1 = a.uq + (int64_t)e * a.gu_qs_stride;
+      d.d0 = a.gd + (int64_t)e * a.gu_d_stride; d.d1 = a.ud + (int64_t)e * a.gu_d_stride;
+    } else {
+      d.qs0 = d.qs1 = a.dq + (int64_t)e * a.dn_qs_stride;
+      d.d0 = d.d1 = a.dd + (int64_t)e * a.dn_d_stride;
+    }
+  }
+  const int64_t f = shared ? a.SF : a.F;  // this expert's ffn width
+  d.rows = GATEUP ? f : a.H;
+  d.cols = GATEUP ? a.H : f;
+  d.NT = (int)(d.rows / 16);
+  d.KT = (int)(d.cols / 128);
+  d.ncols = nc;
+  d.xmap = s_x;
+  d.ymap = s_y;
+  return nc;
+}
+
+template <int QT, int NC, int PF>
+__global__ void __launch_bounds__(GU_WKT * 64) moe_gateup_kernel(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ uint32_t flag;
-  __shared__ int32_t s_slot[TMAX];
-  constexpr int TB = QTraits<QT>::tile_bytes;
-  constexpr int QW = (QT == Q4) ? 1 : 2;
-  const int tid = threadIdx.x, lane = tid & 63, wk = tid >> 6;
+  __shared__ int32_t s_x[TMAX], s_y[TMAX];
+  const int per = a.G_gu * a.S_gu;
+  const int u = blockIdx.x / per, g = (blockIdx.x % per) / a.S_gu, s = blockIdx.x % a.S_gu;
+  DotArgs d = {};
+  if (!moe_expert<true, NC>(a, u, d, s_x, s_y)) return;
+  d.S = a.S_gu;
+  d.G = (int)cdiv(d.NT, GU_WKT);
+  if (g >= d.G) return;
+  d.X = a.X;
+  d.ldx = a.ldx;
+  d.xspan = ((int64_t)(a.T - 1) * a.ldx + a.H) * 4;  // every token's column
+  d.Y = a.hbuf;
+  d.ldy = a.Fmax;
+  d.part = a.gpart + (int64_t)u * a.gpart_per;
+  d.cnt = a.gcnt + (int64_t)u * a.G_gu;
+  __syncthreads();  // the column maps
+  float bv = 0.0f;
+  int32_t bi = 0;
+  dot_unit<QT, NC, 2, EPI_SILU, 1, PF, GU_WKT, PH_PLAIN, true>(d, g, s, smem, &flag, bv, bi);
+}
 
-  const int unit = blockIdx.x;
-  const int sh_units = NMAT == 2 ? a.sh_gu_units : a.sh_dn_units;
-  const int groups = NMAT == 2 ? a.gu_groups : a.dn_groups;
-  const bool shared = unit < sh_units;
-  int nc, rg;
-  const uint8_t *q0, *q1, *d0, *d1;
-  int64_t K;
-  if (shared) {
-    rg = unit;
-    nc = a.T;
-    if (NMAT == 2) { q0 = a.sgq; q1 = a.suq; d0 = a.sgd; d1 = a.sud; K = a.H; }
-    else { q0 = q1 = a.sdq; d0 = d1 = a.sdd; K = a.SF; }
-    if (tid < nc) s_slot[tid] = a.T * a.k + tid;
-  } else {
-    const int uu = (unit - sh_units) / groups;
-    rg = (unit - sh_units) % groups;
-    if (uu >= (int)*a.nused) return;
-    const int e = a.used_e[uu];
-    nc = a.used_cnt[uu];
-    if (NMAT == 2) {
-      q0 = a.gq + (int64_t)e * a.gu_qs_stride; q1 = a.uq + (int64_t)e * a.gu_qs_stride;
-      d0 = a.gd + (int64_t)e * a.gu_d_stride; d1 = a.ud + (int64_t)e * a.gu_d_stride;
-      K = a.H;
-    } else {
-      q0 = q1 = a.dq + (int64_t)e * a.dn_qs_stride;
-      d0 = d1 = a.dd + (int64_t)e * a.dn_d_stride;
-      K = a.F;
-    }
-    if (tid < nc) s_slot[tid] = a.used_slot[uu * TMAX + tid];
-  }
-  const int64_t rows = NMAT == 2 ? (shared ? a.SF : a.F) : a.H;
-  const int NTr = (int)(rows / 16);
-  const int KT = (int)(K / 128);
-  const int64_t rt_base = (int64_t)rg * RT;
-  if (rt_base >= NTr) return;
-  __syncthreads();
+template <int QT, int NC, int PF>
+__global__ void __launch_bounds__(DN_WKT * 64) moe_down_kernel(MoeArgs a) {
+  constexpr int NTHR = DN_WKT * 64;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ uint32_t flag;
+  __shared__ int32_t s_x[TMAX], s_y[TMAX];
+  const int tid = threadIdx.x;
+  const int u = blockIdx.x / a.G_dn, g = blockIdx.x % a.G_dn;
+  DotArgs d = {};
+  if (!moe_expert<false, NC>(a, u, d, s_x, s_y)) return;
+  d.S = 1;
+  d.G = a.G_dn;
+  d.X = a.hbuf;
+  d.ldx = a.Fmax;
+  d.xspan = (int64_t)(a.T * a.k + a.T) * a.Fmax * 4;  // every slot's h
+  d.Y = a.zbuf;
+  d.ldy = a.H;
+  __syncthreads();  // the column maps
+  float bv = 0.0f;
+  int32_t bi = 0;
+  // coherent stores of z (the combine below may run on another XCD)
+  dot_unit<QT, NC, 1, EPI_STORE, 1, PF, DN_WKT, PH_PRODUCE, true>(d, g, 0, smem, &flag, bv, bi);
 
-  // ---- stage the input columns (x of each routed token, or h of each slot)
-  _Float16 *xs = (_Float16 *)smem;
-  float *red = (float *)smem;
-  {
-    const int nvec = KT * 4 * nc * 4;
-    for (int v = tid; v < nvec; v += MTHR) {
-      const int q = v & 3, c = (v >> 2) % nc, bl = (v >> 2) / nc;
-      const int64_t kk = (int64_t)bl * 32 + q * 8;
-      const int slot = s_slot[c];
-      const float *src = NMAT == 2 ? a.X + (int64_t)(shared ? c : slot / a.k) * a.ldx
-                                   : a.hbuf + (int64_t)slot * a.Fmax;
-      const float4 *p = (const float4 *)(src + kk);
-      *(h8 *)(xs + (size_t)v * 8) = cvt8(p[0], p[1]);
-    }
-  }
-  __syncthreads();
-
-  const int r = lane & 15, sl = lane >> 4;
-  float acc[NMAT][RT][NCM];
-#pragma unroll
-  for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-      for (int c = 0; c < NCM; ++c) acc[m][t][c] = 0.0f;
-
-  const Q4Magic mg = q4_magic();
-  for (int kt = wk; kt < KT; kt += MW) {
-    u4 wq[NMAT][RT][QW];
-    u2 wdd[NMAT][RT];
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        const int64_t tile = (rt_base + t) * KT + kt;
-        const uint8_t *tp = (m ? q1 : q0) + tile * TB + lane * 16;
-        wq[m][t][0] = ld_stream(tp);
-        if constexpr (QW == 2) wq[m][t][QW - 1] = ld_stream(tp + 1024);
-        wdd[m][t] = ld_stream2((m ? d1 : d0) + tile * TILE_D_BYTES + r * 8);
-      }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      h2 xv[NCM][4];
-#pragma unroll
-      for (int c = 0; c < NCM; ++c) {
-        if (c < nc) {
-          const h8 xx = *(const h8 *)(xs + ((size_t)(kt * 4 + j) * nc + c) * 32 + sl * 8);
-#pragma unroll
-          for (int p = 0; p < 4; ++p) xv[c][p] = lo_pair(xx, p);
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int t = 0; t < RT; ++t) {
-          h2 w[4];
-          if constexpr (QT == Q4) unpack_q4(wq[m][t][0][j], w, mg);
-          else unpack_q8(wq[m][t][j >> 1][(j & 1) * 2], wq[m][t][j >> 1][(j & 1) * 2 + 1], w);
-          const float dj = scale_of(wdd[m][t], j);
-#pragma unroll
-          for (int c = 0; c < NCM; ++c) {
-            if (c < nc) {
-              float p = dot2_first(w[0], xv[c][0]);
-              p = __builtin_amdgcn_fdot2(w[1], xv[c][1], p, false);
-              p = __builtin_amdgcn_fdot2(w[2], xv[c][2], p, false);
-              p = __builtin_amdgcn_fdot2(w[3], xv[c][3], p, false);
-              acc[m][t][c] = __builtin_fmaf(dj, p, acc[m][t][c]);
-            }
-          }
-        }
-    }
-  }
-
-  __syncthreads();
-#pragma unroll
-  for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-      for (int c = 0; c < NCM; ++c) {
-        if (c < nc) {
-          float v = acc[m][t][c];
-          v += __shfl_xor(v, 16);
-          v += __shfl_xor(v, 32);
-          if (sl == 0) red[(((wk * NMAT + m) * RT + t) * 16 + r) * nc + c] = v;
-        }
-      }
-  __syncthreads();
-
-  const int nout = RT * 16 * nc;
-  for (int o = tid; o < nout; o += MTHR) {
-    const int c = o % nc, rr = (o / nc) % 16, t = o / (16 * nc);
-    float v[NMAT];
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
-      float x = red[((m * RT + t) * 16 + rr) * nc + c];
-#pragma unroll
-      for (int w = 1; w < MW; ++w) x += red[(((w * NMAT + m) * RT + t) * 16 + rr) * nc + c];
-      v[m] = x;
-    }
-    const int64_t row = (rt_base + t) * 16 + rr;
-    const int slot = s_slot[c];
-    if constexpr (NMAT == 2) {
-      const float gg = v[0];
-      a.hbuf[(int64_t)slot * a.Fmax + row] = gg / (1.0f + expf(-gg)) * v[1];
-    } else {
-      st_agent(a.zbuf + (int64_t)slot * a.H + row, v[0]);
-    }
-  }
-
-  if constexpr (NMAT == 1) {
-    // ---- weighted combine of this row group, by the last expert to finish
-    const uint32_t target = *a.nused + (a.SF > 0 ? 1u : 0u);
-    if (!arrive_last(a.dcnt + rg, target, &flag)) return;
-    const int n = RT * 16 * a.T;
-    for (int o = tid; o < n; o += MTHR) {
-      const int t = o / (RT * 16), rr = o % (RT * 16);
-      const int64_t row = rt_base * 16 + rr;
-      float sum = 0.0f;
-      for (int kk = 0; kk < a.k; ++kk)
-        sum = __builtin_fmaf(a.pw[t * a.k + kk], ld_agent(a.zbuf + (int64_t)(t * a.k + kk) * a.H + row), sum);
-      if (a.SF > 0) sum += ld_agent(a.zbuf + (int64_t)(a.T * a.k + t) * a.H + row);
-      float *yp = a.Y + (int64_t)t * a.ldy + row;
-      *yp = *yp + sum;
-    }
+  // ---- weighted combine of this row group, by the last expert to finish
+  const uint32_t target = *a.nused + (a.SF > 0 ? (uint32_t)((a.T + NC - 1) / NC) : 0u);
+  if (!arrive_last(a.dcnt + g, target, &flag)) return;
+  const int64_t r0 = (int64_t)g * DN_WKT * 16;
+  const int nr = (int)((a.H - r0) < DN_WKT * 16 ? (a.H - r0) : DN_WKT * 16);
+  for (int o = tid; o < nr * a.T; o += NTHR) {
+    const int t = o / nr, rr = o % nr;
+    const int64_t row = r0 + rr;
+    float sum = 0.0f;
+    for (int kk = 0; kk < a.k; ++kk)
+      sum = __builtin_fmaf(a.pw[t * a.k + kk], ld_agent(a.zbuf + (int64_t)(t * a.k + kk) * a.H + row), sum);
+    if (a.SF > 0) sum += ld_agent(a.zbuf + (int64_t)(a.T * a.k + t) * a.H + row);
+    float *yp = a.Y + (int64_t)t * a.ldy + row;
+    *yp = *yp + sum;
   }
 }
 
 // ------------------------------------------------------------ host side
-template <int QT, int NCM>
+static int grant(const void *kern, size_t lds, size_t &granted) {
+  if (lds > 163840 - 1024) return QG_EUNSUPPORTED;
+  if (lds > 65536 && lds > granted) {
+    const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) {
+      record_hip_error(e);
+      return QG_EHIP;
+    }
+    granted = lds;
+  }
+  return QG_OK;
+}
+
+// LDS of a unit: the whole segment of activations, or (16 columns) two
+// chunks of PF tile columns
+template <int NC, int PF>
+static size_t unit_lds(int64_t KT, int S) {
+  return NC >= 16 ? (size_t)2 * PF * TILE_BLOCKS * NC * 64 : (size_t)cdiv(KT, S) * TILE_BLOCKS * NC * 64;
+}
+
+template <int QT, int NTC, int NC>
 static int launch_moe_t(const MoeCall &c, MoeArgs &a) {
-  const int ntc = NCM;
-  const unsigned rgrid = (unsigned)((a.E + MW * EPW - 1) / (MW * EPW));
+  constexpr int QW = QT == Q4 ? 1 : 2;
+  constexpr int PFG = 4 / (2 * QW) < 2 ? 2 : 4 / (2 * QW);
+  constexpr int PFD = 4 / QW < 2 ? 2 : 4 / QW;
   clear_hip_error();
-  hipLaunchKernelGGL(moe_router_kernel<ntc>, dim3(rgrid), dim3(MTHR), 0, c.stream, a);
+  const size_t lds_r = (size_t)a.T * a.E * 4;  // at most 16 x 1024 floats
+  // its static LDS (about 9 KiB) comes on top: ask for room above 32 KiB
+  static size_t granted_r = 32768;
+  if (lds_r > granted_r) {
+    const hipError_t e = hipFuncSetAttribute((const void *)moe_router_kernel<NTC, NC>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_r);
+    if (e != hipSuccess) {
+      record_hip_error(e);
+      return QG_EHIP;
+    }
+    granted_r = lds_r;
+  }
+  int st = QG_OK;
+  hipLaunchKernelGGL((moe_router_kernel<NTC, NC>), dim3((unsigned)cdiv((int64_t)a.E * a.T, RW)), dim3(RW * 64), lds_r,
+                     c.stream, a);
   if (launch_status() != QG_OK) return QG_EHIP;
 
-  const int T = a.T;
-  size_t x_gu = (size_t)(a.H / 128) * 4 * T * 64;
-  size_t r_gu = (size_t)MW * 2 * RT_GU * 16 * T * 4;
-  size_t lds_gu = x_gu > r_gu ? x_gu : r_gu;
-  const unsigned ggrid = (unsigned)(a.sh_gu_units + (int64_t)a.Umax * a.gu_groups);
-  auto kg = moe_expert_kernel<QT, NCM, 2, RT_GU>;
-  if (lds_gu > 163840 - 1024) return QG_EUNSUPPORTED;
-  if (lds_gu > 65536) {
-    static size_t granted = 65536;
-    if (lds_gu > granted) {
-      const hipError_t e = hipFuncSetAttribute((const void *)kg, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_gu);
-      if (e != hipSuccess) {
-        record_hip_error(e);
-        return QG_EHIP;
-      }
-      granted = lds_gu;
-    }
-  }
+  auto kg = moe_gateup_kernel<QT, NC, PFG>;
+  const size_t lds_g = unit_lds<NC, PFG>(a.H / 128, a.S_gu);
+  static size_t granted_g = 65536;
+  st = grant((const void *)kg, lds_g, granted_g);
+  if (st) return st;
   clear_hip_error();
-  hipLaunchKernelGGL(kg, dim3(ggrid), dim3(MTHR), lds_gu, c.stream, a);
+  hipLaunchKernelGGL(kg, dim3((unsigned)((int64_t)(a.Umax + a.nsh) * a.G_gu * a.S_gu)), dim3(GU_WKT * 64), lds_g,
+                     c.stream, a);
   if (launch_status() != QG_OK) return QG_EHIP;
 
-  size_t x_dn = (size_t)(a.Fmax / 128) * 4 * T * 64;
-  size_t r_dn = (size_t)MW * 1 * RT_DN * 16 * T * 4;
-  size_t lds_dn = x_dn > r_dn ? x_dn : r_dn;
-  const unsigned dgrid = (unsigned)(a.sh_dn_units + (int64_t)a.Umax * a.dn_groups);
-  auto kd = moe_expert_kernel<QT, NCM, 1, RT_DN>;
-  if (lds_dn > 163840 - 1024) return QG_EUNSUPPORTED;
-  if (lds_dn > 65536) {
-    static size_t granted = 65536;
-    if (lds_dn > granted) {
-      const hipError_t e = hipFuncSetAttribute((const void *)kd, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dn);
-      if (e != hipSuccess) {
-        record_hip_error(e);
-        return QG_EHIP;
-      }
-      granted = lds_dn;
-    }
-  }
+  auto kd = moe_down_kernel<QT, NC, PFD>;
+  const size_t lds_d = unit_lds<NC, PFD>(a.Fmax / 128, 1);
+  static size_t granted_d = 65536;
+  if ((st = grant((const void *)kd, lds_d, granted_d))) return st;
   clear_hip_error();
-  hipLaunchKernelGGL(kd, dim3(dgrid), dim3(MTHR), lds_dn, c.stream, a);
+  hipLaunchKernelGGL(kd, dim3((unsigned)((int64_t)(a.Umax + a.nsh) * a.G_dn)), dim3(DN_WKT * 64), lds_d, c.stream, a);
   return launch_status();
 }
 
 template <int QT>
 static int launch_moe_q(const MoeCall &c, MoeArgs &a) {
-  if (a.T <= 1) return launch_moe_t<QT, 1>(c, a);
-  if (a.T <= 2) return launch_moe_t<QT, 2>(c, a);
-  if (a.T <= 4) return launch_moe_t<QT, 4>(c, a);
-  if (a.T <= 8) return launch_moe_t<QT, 8>(c, a);
-  return launch_moe_t<QT, 16>(c, a);
+  if (a.T <= 1) return launch_moe_t<QT, 1, 1>(c, a);
+  if (a.T <= 2) return launch_moe_t<QT, 2, 2>(c, a);
+  if (a.T <= 4) return launch_moe_t<QT, 4, 4>(c, a);
+  if (a.T <= 8) return launch_moe_t<QT, 8, 4>(c, a);
+  return launch_moe_t<QT, 16, 4>(c, a);
 }
 
 int launch_moe(const MoeCall &c) {
   const qg_moe *m = c.m;
   const MoeLayout L = moe_layout(m, c.ntok);
   if (c.ws_bytes < L.total) return QG_EWORKSPACE;
+  if (L.sync_words > WS_SYNC_WORDS) return QG_EUNSUPPORTED;
   MoeArgs a;
   a.H = m->hidden;
   a.F = m->ffn;
@@ -464,7 +459,7 @@ int launch_moe(const MoeCall &c) {
   a.k = m->top_k;
   a.norm = m->normalize_topk ? 1 : 0;
   a.T = c.ntok;
-  a.Umax = (int)((int64_t)a.E < (int64_t)a.T * a.k ? a.E : a.T * a.k);
+  a.Umax = (int)L.umax;
   a.R = m->router;
   a.gq = (const uint8_t *)m->gate_qs; a.uq = (const uint8_t *)m->up_qs; a.dq = (const uint8_t *)m->down_qs;
   a.gd = (const uint8_t *)m->gate_d; a.ud = (const uint8_t *)m->up_d; a.dd = (const uint8_t *)m->down_d;
@@ -484,8 +479,10 @@ int launch_moe(const MoeCall &c) {
   a.topk_idx = c.topk_idx;
   a.topk_w = c.topk_w;
   uint8_t *ws = (uint8_t *)c.ws;
-  a.rcnt = (uint32_t *)(ws + L.rcnt);
-  a.dcnt = (uint32_t *)(ws + L.dcnt);
+  uint32_t *w32 = (uint32_t *)ws;
+  a.rcnt = w32 + L.rcnt_w;
+  a.dcnt = w32 + L.dcnt_w;
+  a.gcnt = w32 + L.gcnt_w;
   a.nused = (uint32_t *)(ws + L.nused);
   a.logits = (float *)(ws + L.logits);
   a.sel = (int32_t *)(ws + L.sel);
@@ -495,10 +492,12 @@ int launch_moe(const MoeCall &c) {
   a.used_slot = (int32_t *)(ws + L.used_slot);
   a.hbuf = (float *)(ws + L.hbuf);
   a.zbuf = (float *)(ws + L.zbuf);
-  a.gu_groups = (int)((a.F / 16 + RT_GU - 1) / RT_GU);
-  a.sh_gu_units = a.SF > 0 ? (int)((a.SF / 16 + RT_GU - 1) / RT_GU) : 0;
-  a.dn_groups = (int)((a.H / 16 + RT_DN - 1) / RT_DN);
-  a.sh_dn_units = a.SF > 0 ? a.dn_groups : 0;
+  a.gpart = (float *)(ws + L.gpart);
+  a.S_gu = L.S_gu;
+  a.G_gu = L.G_gu;
+  a.G_dn = L.G_dn;
+  a.gpart_per = L.gpart_per;
+  a.nsh = L.nsh;
   if (m->qtype == QG_Q4_0) return launch_moe_q<Q4>(c, a);
   return launch_moe_q<Q8>(c, a);
 }

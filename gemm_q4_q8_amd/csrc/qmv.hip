@@ -198,6 +198,8 @@ static int launch_dot_t(const QmvCall &c, int S) {
   a.out_val = c.out_val;
   a.ready = nullptr;
   a.err = nullptr;
+  a.xmap = a.ymap = nullptr;
+  a.xspan = 0;
   if (!ranges_fit(c, NT, KT, QTraits<QT>::tile_bytes)) return QG_EUNSUPPORTED;
   const size_t need = off + (S > 1 ? (size_t)S * NMAT * NTu * 16 * NC * 4 : 0);
   if (need > c.ws_bytes) return QG_EWORKSPACE;
