@@ -180,6 +180,64 @@ __device__ __forceinline__ bool ranks_before(float va, int32_t ia, float vb, int
   return va > vb || (va == vb && ia < ib);
 }
 
+// Wave-wide reductions without LDS round trips.  Lane exchanges by DPP: the
+// quad permutes [1,0,3,2] and [2,3,0,1] pair lanes at distance 1 and 2; once
+// values agree within groups of 4 (then 8), the half-row mirror (then the
+// row mirror) pairs each group with its neighbour; a swizzle (xor 16 within
+// 32 lanes) joins the two rows of each half, and the halves meet through
+// readlane.  The combine is symmetric, so every lane ends with the same bits.
+__device__ __forceinline__ int dpp_partner(int v, int step) {
+  switch (step) {
+    case 0: return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    case 1: return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    case 2: return __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    case 3: return __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false);  // row_mirror
+  }
+  return __builtin_amdgcn_ds_swizzle(v, 0x401F);                          // xor 16
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int step = 0; step < 5; ++step)
+    v += __builtin_bit_cast(float, dpp_partner(__builtin_bit_cast(int, v), step));
+  const int b = __builtin_bit_cast(int, v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
+         __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int step = 0; step < 5; ++step) {
+    const uint32_t lo = (uint32_t)dpp_partner((int)(uint32_t)v, step);
+    const uint32_t hi = (uint32_t)dpp_partner((int)(uint32_t)(v >> 32), step);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+  }
+  const uint64_t a = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 0) << 32) |
+                     (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 0);
+  const uint64_t b = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 32) << 32) |
+                     (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 32);
+  return a > b ? a : b;
+}
+
+// The order of ranks_before as one unsigned key: the value's bits mapped to
+// an order-preserving code (negatives complemented, positives with the sign
+// bit set, -0 as +0, every NaN as 0), above the complemented index.  Larger
+// key = ranks first; every key of a real index is above 0.
+__device__ __forceinline__ uint64_t rank_key(float v, int32_t i) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  uint32_t c = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  if (v == 0.0f) c = 0x80000000u;
+  if (v != v) c = 0u;
+  return ((uint64_t)c << 32) | (0xFFFFFFFFu - (uint32_t)i);
+}
+__device__ __forceinline__ int32_t rank_key_index(uint64_t k) { return (int32_t)(0xFFFFFFFFu - (uint32_t)k); }
+// the value back (a NaN for code 0)
+__device__ __forceinline__ float rank_key_value(uint64_t k) {
+  const uint32_t c = (uint32_t)(k >> 32);
+  return __builtin_bit_cast(float, (c & 0x80000000u) ? (c & 0x7FFFFFFFu) : ~c);
+}
+
 // blockIdx -> work unit, so that each XCD (workgroups are dealt to the eight
 // XCDs round-robin) takes a contiguous range of units.
 __device__ __forceinline__ int64_t xcd_unit(int64_t per_xcd) {

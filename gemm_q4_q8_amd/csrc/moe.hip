@@ -6,7 +6,7 @@
 // Experts are stacked by role ("A 235B model in a browser window": all gate
 // matrices in one tensor, all up in a second, all down in a third).
 //
-//  1. router: one wave per (expert, token) forms that f32 logit (f32
+//  1. router: a few waves per (expert, token) form that f32 logit (f32
 //     operands, f32 FMA); the last workgroup picks the top k per token
 //     (value descending, index ascending), the softmax weights, and a work
 //     list in expert index order of entries of at most 4 routed slots of one
@@ -38,6 +38,7 @@ constexpr int DN_WKT = 8;   // down: row tiles per workgroup (128 rows)
 struct MoeArgs {
   int64_t H, F, SF, Fmax;
   int E, k, norm, T, Umax;
+  int rparts;             // router: waves per logit (parts of the hidden range)
   const float *R;
   const uint8_t *gq, *uq, *dq, *gd, *ud, *dd;
   const uint8_t *sgq, *suq, *sdq, *sgd, *sud, *sdd;
@@ -117,32 +118,39 @@ static MoeLayout moe_layout(const qg_moe *m, int T) {
 size_t moe_ws_bytes(const qg_moe *m, int ntok) { return moe_layout(m, ntok).total; }
 
 // ------------------------------------------------------------ 1. router
-// One wave per (expert, token) pair, the pairs of an expert adjacent (its
-// router row is then read from L2 by all but the first): each wave forms
-// one logit.  The last workgroup stages the logits in LDS (dynamic, T x
-// n_expert floats) and selects, one wave per token (T <= RW).
-template <int NTC, int NCAP>
+// P waves per (expert, token) pair (P parts of the hidden range, P larger
+// when there are few pairs, so that the router matrix is read by many CUs),
+// the pairs of an expert adjacent (its router row is then read from L2 by
+// all but the first); the parts meet in LDS in part order.  The last workgroup selects, one wave per token (T <= RW),
+// with the token's logits in registers (NJ per lane, n_expert <= 64 NJ):
+// k rounds of a wave maximum over each lane's best remaining key, after
+// which only the lane that owned the winner looks at its keys again.
+template <int NCAP, int NJ>
 __global__ void __launch_bounds__(RW * 64) moe_router_kernel(MoeArgs a) {
   constexpr int NTHR = RW * 64;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  float *s_l = (float *)smem;
   __shared__ uint32_t flag;
   __shared__ int32_t s_sel[TMAX * 8];
   __shared__ int32_t s_cnt[1024], s_off[1024];  // per expert (n_expert <= 1024)
   __shared__ int32_t s_wtot[RW];
+  __shared__ float s_part[RW];
   const int tid = threadIdx.x, lane = tid & 63, wk = tid >> 6;
   {
-    const int64_t item = (int64_t)blockIdx.x * RW + wk;
+    // wave -> (expert, token, part of the hidden range); the P parts of a
+    // logit are adjacent waves of one workgroup
+    const int P = a.rparts, hp = (int)cdiv(cdiv(a.H, P), 4) * 4;
+    const int64_t item = ((int64_t)blockIdx.x * RW + wk) / P;
+    const int p = wk % P;
     const int e = (int)(item / a.T), t = (int)(item % a.T);
+    float v = 0.0f;
     if (e < a.E) {
-      float v = 0.0f;
-      for (int64_t h0 = 0; h0 < a.H; h0 += 2048) {
+      const int64_t hb = (int64_t)p * hp, he = hb + hp < a.H ? hb + hp : a.H;
+      for (int64_t h0 = hb; h0 < he; h0 += 2048) {
         float4 rv[8], xv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int64_t h = h0 + ((int64_t)j * 64 + lane) * 4;
-          rv[j] = h < a.H ? *(const float4 *)(a.R + (int64_t)e * a.H + h) : float4{0, 0, 0, 0};
-          xv[j] = h < a.H ? *(const float4 *)(a.X + (int64_t)t * a.ldx + h) : float4{0, 0, 0, 0};
+          rv[j] = h < he ? *(const float4 *)(a.R + (int64_t)e * a.H + h) : float4{0, 0, 0, 0};
+          xv[j] = h < he ? *(const float4 *)(a.X + (int64_t)t * a.ldx + h) : float4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -152,61 +160,72 @@ __global__ void __launch_bounds__(RW * 64) moe_router_kernel(MoeArgs a) {
           v = __builtin_fmaf(rv[j].w, xv[j].w, v);
         }
       }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-      if (lane == 0) st_agent(a.logits + (int64_t)t * a.E + e, v);
+      v = wave_sum(v);
+    }
+    if (lane == 0) s_part[wk] = v;
+    __syncthreads();
+    if (tid < RW / P) {
+      const int64_t it = (int64_t)blockIdx.x * (RW / P) + tid;
+      if (it < (int64_t)a.E * a.T) {
+        float l = s_part[tid * P];
+        for (int q = 1; q < P; ++q) l += s_part[tid * P + q];
+        st_agent(a.logits + (it % a.T) * a.E + it / a.T, l);
+      }
     }
   }
   if (!arrive_last(a.rcnt, gridDim.x, &flag)) return;
 
   // ---- top-k and softmax weights, one wave per token
-  for (int i = tid; i < a.T * a.E; i += NTHR) s_l[i] = ld_agent(a.logits + i);
-  __syncthreads();
   if (wk < a.T) {
     const int t = wk;
-    const float *lt = s_l + (int64_t)t * a.E;
-    const int nj = (a.E + 63) / 64;
-    uint32_t taken = 0;  // bit j: expert lane + 64 j is already selected
-    float mx = 0.0f, sumsel = 0.0f;
-    int32_t my_e = 0;    // lane kk: the expert of rank kk
+    float lv[NJ];
+    uint64_t key[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int ee = lane + 64 * j;
+      lv[j] = ee < a.E ? ld_agent(a.logits + (int64_t)t * a.E + ee) : 0.0f;
+      key[j] = ee < a.E ? rank_key(lv[j], ee) : 0;
+    }
+    uint64_t loc = 0;  // this lane's best remaining key
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) loc = key[j] > loc ? key[j] : loc;
+    float mx = 0.0f, sumsel = 0.0f, my_ex = 0.0f;
+    int32_t my_e = 0;  // lane kk: the expert of rank kk
     for (int kk = 0; kk < a.k; ++kk) {
-      float bv = __builtin_nanf("");
-      int32_t bi = 0x7fffffff;
-      for (int j = 0; j < nj; ++j) {
-        const int ee = lane + 64 * j;
-        if (ee < a.E && !((taken >> j) & 1u)) {
-          const float v = lt[ee];
-          if (ranks_before(v, ee, bv, bi)) { bv = v; bi = ee; }
+      const uint64_t w = wave_max_u64(loc);
+      const int32_t bi = rank_key_index(w);
+      const float bv = rank_key_value(w);
+      if (kk == 0) mx = bv;  // the largest logit
+      const float ex = expf(bv - mx);
+      sumsel += ex;
+      if (lane == kk) {
+        my_e = bi;
+        my_ex = ex;
+      }
+      if (loc == w) {  // the owner: drop the winner, find its next best
+        loc = 0;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          if (key[j] == w) key[j] = 0;
+          loc = key[j] > loc ? key[j] : loc;
         }
       }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int32_t oi = __shfl_xor(bi, off);
-        if (ranks_before(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-      }
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      if (kk == 0) mx = bv;  // the largest logit
-      sumsel += expf(bv - mx);
-      if (lane == kk) my_e = bi;
-      if (lane == 0) s_sel[t * a.k + kk] = bi;
     }
     float sum = sumsel;
     if (!a.norm) {
       float part = 0.0f;
-      for (int j = 0; j < nj; ++j)
-        if (lane + 64 * j < a.E) part += expf(lt[lane + 64 * j] - mx);
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-      sum = part;
+      for (int j = 0; j < NJ; ++j)
+        if (lane + 64 * j < a.E) part += expf(lv[j] - mx);
+      sum = wave_sum(part);
     }
     if (lane < a.k) {
       const int kk = lane;
-      const int32_t ee = my_e;
-      const float p = expf(lt[ee] - mx) / sum;
-      a.sel[t * a.k + kk] = ee;
+      const float p = my_ex / sum;
+      s_sel[t * a.k + kk] = my_e;
+      a.sel[t * a.k + kk] = my_e;
       a.pw[t * a.k + kk] = p;
-      if (a.topk_idx) a.topk_idx[t * a.k + kk] = ee;
+      if (a.topk_idx) a.topk_idx[t * a.k + kk] = my_e;
       if (a.topk_w) a.topk_w[t * a.k + kk] = p;
     }
   }
@@ -394,27 +413,18 @@ static size_t unit_lds(int64_t KT, int S) {
   return NC >= 16 ? (size_t)2 * PF * TILE_BLOCKS * NC * 64 : (size_t)cdiv(KT, S) * TILE_BLOCKS * NC * 64;
 }
 
-template <int QT, int NTC, int NC>
+template <int QT, int NC>
 static int launch_moe_t(const MoeCall &c, MoeArgs &a) {
   constexpr int QW = QT == Q4 ? 1 : 2;
   constexpr int PFG = 4 / (2 * QW) < 2 ? 2 : 4 / (2 * QW);
   constexpr int PFD = 4 / QW < 2 ? 2 : 4 / QW;
   clear_hip_error();
-  const size_t lds_r = (size_t)a.T * a.E * 4;  // at most 16 x 1024 floats
-  // its static LDS (about 9 KiB) comes on top: ask for room above 32 KiB
-  static size_t granted_r = 32768;
-  if (lds_r > granted_r) {
-    const hipError_t e = hipFuncSetAttribute((const void *)moe_router_kernel<NTC, NC>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_r);
-    if (e != hipSuccess) {
-      record_hip_error(e);
-      return QG_EHIP;
-    }
-    granted_r = lds_r;
-  }
   int st = QG_OK;
-  hipLaunchKernelGGL((moe_router_kernel<NTC, NC>), dim3((unsigned)cdiv((int64_t)a.E * a.T, RW)), dim3(RW * 64), lds_r,
-                     c.stream, a);
+  const dim3 rgrid((unsigned)cdiv((int64_t)a.E * a.T * a.rparts, RW));
+  if (a.E <= 256)
+    hipLaunchKernelGGL((moe_router_kernel<NC, 4>), rgrid, dim3(RW * 64), 0, c.stream, a);
+  else
+    hipLaunchKernelGGL((moe_router_kernel<NC, 16>), rgrid, dim3(RW * 64), 0, c.stream, a);
   if (launch_status() != QG_OK) return QG_EHIP;
 
   auto kg = moe_gateup_kernel<QT, NC, PFG>;
@@ -438,11 +448,9 @@ static int launch_moe_t(const MoeCall &c, MoeArgs &a) {
 
 template <int QT>
 static int launch_moe_q(const MoeCall &c, MoeArgs &a) {
-  if (a.T <= 1) return launch_moe_t<QT, 1, 1>(c, a);
-  if (a.T <= 2) return launch_moe_t<QT, 2, 2>(c, a);
-  if (a.T <= 4) return launch_moe_t<QT, 4, 4>(c, a);
-  if (a.T <= 8) return launch_moe_t<QT, 8, 4>(c, a);
-  return launch_moe_t<QT, 16, 4>(c, a);
+  if (a.T <= 1) return launch_moe_t<QT, 1>(c, a);
+  if (a.T <= 2) return launch_moe_t<QT, 2>(c, a);
+  return launch_moe_t<QT, 4>(c, a);
 }
 
 int launch_moe(const MoeCall &c) {
@@ -460,6 +468,10 @@ int launch_moe(const MoeCall &c) {
   a.norm = m->normalize_topk ? 1 : 0;
   a.T = c.ntok;
   a.Umax = (int)L.umax;
+  // enough router waves to spread the router matrix over the device, each
+  // part at least one float4 per lane
+  a.rparts = 1;
+  while (a.rparts < RW && (int64_t)a.E * a.T * a.rparts < 2048 && a.H / (2 * a.rparts) >= 256) a.rparts *= 2;
   a.R = m->router;
   a.gq = (const uint8_t *)m->gate_qs; a.uq = (const uint8_t *)m->up_qs; a.dq = (const uint8_t *)m->down_qs;
   a.gd = (const uint8_t *)m->gate_d; a.ud = (const uint8_t *)m->up_d; a.dd = (const uint8_t *)m->down_d;
