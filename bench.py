@@ -227,6 +227,11 @@ def read_ceiling(B):
     return 2 * POOL_BYTES / t / 1e9
 
 
+# the sources of the gate/up kernel whose counters the traffic summary holds
+TRAFFIC_SOURCES = ("gemm_q4_q8_amd/csrc/qmv.hip", "gemm_q4_q8_amd/csrc/dot_unit.h",
+                   "gemm_q4_q8_amd/csrc/common.h")
+
+
 def measured_traffic():
     """HBM bytes per gate/up launch from the committed counter summary, or
     None when the kernel source changed since the counters were taken."""
@@ -238,15 +243,16 @@ def measured_traffic():
     except OSError:
         return None
     h = hashlib.sha256()
-    for f in ("gemm_q4_q8_amd/csrc/qmv.hip", "gemm_q4_q8_amd/csrc/common.h"):
+    for f in TRAFFIC_SOURCES:
         h.update(open(os.path.join(ROOT, f), "rb").read())
     if fields.get("kernel_source_hash") != h.hexdigest()[:16]:
         return None
     return int(float(fields["traffic_bytes_per_launch"]))
 
 
-def cpu_baseline(raws):
-    """The oracle, as it stands, on one full decode-FFN step (2 repetitions)."""
+def cpu_baseline(raws, min_seconds=12.0):
+    """The oracle, as it stands, on full decode-FFN steps, repeated until at
+    least `min_seconds` of host work."""
     import synth
     from oracle import ops
     try:
@@ -257,17 +263,21 @@ def cpu_baseline(raws):
     graw, uraw, draw = raws
     x = synth.gen_x(5120, 1, cfg_id=2)[:, 0]
     y_in = synth.rng(2, 90).standard_normal(5120).astype(np.float32)
-    reps = 2
+    reps = 0
     t0 = time.perf_counter()
-    for _ in range(reps):
+    while True:
         h, _, _, _ = ops.gateup_silu(2, graw, uraw, x)
         ops.gemv(2, draw, h.astype(np.float32), y_in=y_in)
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
     dt = (time.perf_counter() - t0) / reps
     nbytes = 3 * qbytes(2, 17408, 5120) + 4 * 5120 + 4 * 17408 + 4 * 17408 + 8 * 5120
     return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"one full decode-FFN step (gate/up 17408x5120 + down 5120x17408, Q4_0, batch 1), "
-                      f"{reps} repetitions, {dt:.2f} s per step; f64 numpy, BLAS threads={threads}"}
+            "sample": f"full decode-FFN steps (gate/up 17408x5120 + down 5120x17408, Q4_0, batch 1), "
+                      f"{reps} repetitions in {dt * reps:.1f} s, {dt:.2f} s per step; f64 numpy, "
+                      f"BLAS threads={threads}"}
 
 
 def traffic_run(B):

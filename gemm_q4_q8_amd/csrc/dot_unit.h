@@ -84,11 +84,32 @@ struct NoHook {
 // `staged` runs once the activations are in LDS and the first weight loads
 // are in flight (the fused FFN takes its next work unit there, so that
 // round trip overlaps the stream).
+// Register fence after a matrix-core product and the FMAs that read its
+// result.  The matrix core reads A and B and writes all four result
+// registers over several passes after the instruction issues; a register it
+// still reads or writes must not be handed to another value meanwhile.  The
+// statement takes A, B and the whole result and rewrites the accumulators
+// the FMAs produced, so it is ordered after those FMAs (which wait for the
+// product to complete) and all of A, B and D stay allocated until then, also
+// the result values no FMA reads (fewer than four columns).
+template <int NI>
+__device__ __forceinline__ void mfma_fence(float (&acc)[NI], const h8 &A, const h8 &B, const f4 &D) {
+  static_assert(NI >= 1 && NI <= 4, "columns per lane");
+  if constexpr (NI == 1) __asm__ volatile("" : "+v"(acc[0]) : "v"(A), "v"(B), "v"(D));
+  else if constexpr (NI == 2) __asm__ volatile("" : "+v"(acc[0]), "+v"(acc[1]) : "v"(A), "v"(B), "v"(D));
+  else if constexpr (NI == 3)
+    __asm__ volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]) : "v"(A), "v"(B), "v"(D));
+  else
+    __asm__ volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]) : "v"(A), "v"(B), "v"(D));
+}
+
 template <int QT, int NC, int NMAT, int EPI, int RT, int PF, int WKT, int PH, bool MF = false,
           class Hook = NoHook>
 __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t *smem, uint32_t *flag,
                                           float &bv, int32_t &bi, Hook staged = Hook()) {
-  constexpr int NTHR = WKT * 64;
+  // WKT == 0: one row tile per wave of the workgroup as launched
+  static_assert(WKT > 0 || NC < 16, "streamed staging needs a fixed workgroup size");
+  const int NTHR = WKT > 0 ? WKT * 64 : (int)blockDim.x;
   constexpr int XC = NC;  // activation columns in the LDS layout
   // accumulators per lane: dot form, one per column; matrix-core form, the
   // 4 D values of lane (r, sl) are columns 4 sl + i
@@ -103,13 +124,13 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   constexpr bool XS = NC >= 16;
   constexpr int CHV = PF * TILE_BLOCKS * NC * 4;   // 8-value pieces per chunk
   constexpr int CHH = PF * TILE_BLOCKS * NC * 32;  // halves per chunk buffer
-  constexpr int XR = (CHV + NTHR - 1) / NTHR;      // pieces per thread per chunk
+  constexpr int XR = WKT > 0 ? (CHV + WKT * 64 - 1) / (WKT * 64) : 1;  // pieces per thread per chunk
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wk = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kt0 = seg_begin(s, a.KT, a.S);
   const int nkt = seg_begin(s + 1, a.KT, a.S) - kt0;
-  const int64_t rt_base = ((int64_t)g * WKT + wk) * RT;
+  const int64_t rt_base = ((int64_t)g * (NTHR >> 6) + wk) * RT;
   const int r = lane & 15, sl = lane >> 4;
   _Float16 *xs = (_Float16 *)smem;
 
@@ -254,11 +275,7 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
             const float dj = scale_of(wd[slot][m][t], j);
 #pragma unroll
             for (int i = 0; i < NI; ++i) acc[m][t][i] = __builtin_fmaf(dj, D[i], acc[m][t][i]);
-            // A and B stay in use until after the result is read (the
-            // statement takes D, so it follows the MFMA): the result can
-            // then never be given their registers, which the matrix core
-            // reads over several passes while it writes the result
-            __asm__ volatile("" ::"v"(A), "v"(B), "v"(D));
+            mfma_fence(acc[m][t], A, B, D);
           }
       }
       return;

@@ -36,6 +36,8 @@ struct QmvCall {
 // widest batch the entry point takes) only, so that every column count gives
 // the same per-row reduction order.
 int gemv_segments(int64_t rows, int64_t cols, int nmat, int ncols_max);
+// Compute units of the current device (queried once per device).
+int device_cus();
 // K splits of the 16-column matrix-core path.
 int gemm16_splits(int64_t rows, int64_t cols);
 

@@ -28,13 +28,17 @@ static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // --------------------------------------------------------------- dot path
-template <int QT, int NC, int NMAT, int EPI, int RT, int PF, int WKT, bool MF>
-__global__ void __launch_bounds__(WKT * 64) dot_kernel(DotArgs a) {
-  constexpr int NTHR = WKT * 64;
+// WKT > 0: workgroups of WKT waves; WKT == 0: as many waves as launched, at
+// most WMAX (the launch planner picks the size per shape).
+template <int QT, int NC, int NMAT, int EPI, int RT, int PF, int WKT, bool MF, int WMAX>
+__global__ void __launch_bounds__(WMAX * 64) dot_kernel(DotArgs a) {
+  static_assert(WKT <= WMAX, "workgroup size");
+  const int NTHR = WKT > 0 ? WKT * 64 : (int)blockDim.x;
+  const int NW = NTHR >> 6;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ uint32_t flag;
-  __shared__ float wave_v[WKT];
-  __shared__ int32_t wave_i[WKT];
+  __shared__ float wave_v[WMAX];
+  __shared__ int32_t wave_i[WMAX];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wk = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -57,7 +61,7 @@ __global__ void __launch_bounds__(WKT * 64) dot_kernel(DotArgs a) {
     if (lane == 0) { wave_v[wk] = bv; wave_i[wk] = bi; }
     __syncthreads();
     if (tid == 0) {
-      for (int w = 1; w < WKT; ++w)
+      for (int w = 1; w < NW; ++w)
         if (ranks_before(wave_v[w], wave_i[w], bv, bi)) { bv = wave_v[w]; bi = wave_i[w]; }
       st_agent(a.cand_v + g, bv);
       st_agent_u32((uint32_t *)a.cand_i + g, (uint32_t)bi);
@@ -80,7 +84,7 @@ __global__ void __launch_bounds__(WKT * 64) dot_kernel(DotArgs a) {
     if (lane == 0) { wave_v[wk] = bv; wave_i[wk] = bi; }
     __syncthreads();
     if (tid == 0) {
-      for (int w = 1; w < WKT; ++w)
+      for (int w = 1; w < NW; ++w)
         if (ranks_before(wave_v[w], wave_i[w], bv, bi)) { bv = wave_v[w]; bi = wave_i[w]; }
       *a.out_idx = bi;
       if (a.out_val) *a.out_val = bv;
@@ -89,6 +93,18 @@ __global__ void __launch_bounds__(WKT * 64) dot_kernel(DotArgs a) {
 }
 
 // ---------------------------------------------------------------- host side
+int device_cus() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 constexpr int DOT_STREAMS = 2048;     // (row tile, segment, matrix) weight streams
 constexpr size_t DOT_X_LDS = 65536;   // staged activations per workgroup
 constexpr size_t LDS_HARD = 163840;   // gfx950 LDS per workgroup
@@ -157,8 +173,8 @@ static int grant_lds(const void *kern, size_t lds, size_t &granted) {
   return QG_OK;
 }
 
-template <int QT, int NC, int NMAT, int EPI, int RT, int PF, int WKT, bool MF>
-static int launch_dot_t(const QmvCall &c, int S) {
+template <int QT, int NC, int NMAT, int EPI, int RT, int PF, int WKT, bool MF, int WMAX = WKT>
+static int launch_dot_t(const QmvCall &c, int S, int W = WKT) {
   const int64_t NT = cdiv(c.rows, 16), KT = cdiv(c.cols / 32, 4);
   const int64_t NTu = cdiv(c.n_rows, 16);  // row tiles actually produced
   DotArgs a;
@@ -171,7 +187,8 @@ static int launch_dot_t(const QmvCall &c, int S) {
   a.NT = (int)NTu;
   a.KT = (int)KT;
   a.S = S;
-  a.G = (int)cdiv(NTu, (int64_t)WKT * RT);
+  if (W < 1 || W > WMAX || (WKT > 0 && W != WKT)) return QG_EUNSUPPORTED;
+  a.G = (int)cdiv(NTu, (int64_t)W * RT);
   a.units = (int64_t)a.G * S;
   a.per_xcd = cdiv(a.units, 8);
   a.X = c.X;
@@ -208,17 +225,32 @@ static int launch_dot_t(const QmvCall &c, int S) {
   // PF tile columns
   const size_t lds = NC >= 16 ? (size_t)2 * PF * TILE_BLOCKS * NC * 64 : (size_t)cdiv(KT, S) * TILE_BLOCKS * NC * 64;
   if (lds > LDS_HARD - 1024) return QG_EUNSUPPORTED;
-  auto kern = dot_kernel<QT, NC, NMAT, EPI, RT, PF, WKT, MF>;
+  auto kern = dot_kernel<QT, NC, NMAT, EPI, RT, PF, WKT, MF, WMAX>;
   static size_t granted = 65536;  // per instantiation; only ever raised
   int st = grant_lds((const void *)kern, lds, granted);
   if (st) return st;
   clear_hip_error();
-  hipLaunchKernelGGL(kern, dim3((unsigned)(a.per_xcd * 8)), dim3(WKT * 64), lds, c.stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(a.per_xcd * 8)), dim3(W * 64), lds, c.stream, a);
   return launch_status();
 }
 
+// Workgroup size, one row tile per wave.  A CU that holds two of the
+// launch's workgroups streams twice the bytes and finishes last (measured:
+// a launch of a few more workgroups than CUs takes about 1.4x as long), so
+// when the workgroups can be made few enough to take one CU each, they are:
+// 4 waves where that already holds (small matrices: more CUs busy), else the
+// smallest size from 8 to 16 waves that does.  Launches that take several
+// rounds anyway use 8 waves.
+static int dot_waves(int64_t NTu, int S) {
+  const int64_t ncu = device_cus();
+  if (cdiv(NTu, 4) * S <= ncu) return 4;
+  for (int w = 8; w <= 16; ++w)
+    if (cdiv(NTu, w) * S <= ncu) return w;
+  return 8;
+}
+
 // One row tile per wave, about 4 KiB of weights in flight per wave (PF tile
-// columns).  Workgroups of 8 waves unless that leaves CUs idle.
+// columns).
 template <int QT, int NC, int NMAT, int EPI>
 static int launch_dot(const QmvCall &c, int S) {
   constexpr int QW = QT == Q4 ? 1 : 2;
@@ -226,8 +258,9 @@ static int launch_dot(const QmvCall &c, int S) {
   constexpr int PF = PF0 < 2 ? 2 : PF0;
   const int64_t NTu = cdiv(c.n_rows, 16);
   constexpr bool MF = DOT_MF;
-  if (cdiv(NTu, 8) * S >= 256) return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 8, MF>(c, S);
-  return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 4, MF>(c, S);
+  const int W = dot_waves(NTu, S);
+  if (W <= 8) return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 8>(c, S, W);
+  return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 16>(c, S, W);
 }
 
 template <int QT, int EPI>
