@@ -92,6 +92,10 @@ struct NoHook {
 // the FMAs produced, so it is ordered after those FMAs (which wait for the
 // product to complete) and all of A, B and D stay allocated until then, also
 // the result values no FMA reads (fewer than four columns).
+// Smallest workgroup (waves) a streamed-staging unit of launch-time size
+// runs with: its per-thread chunk pieces are sized for it.
+constexpr int DOT_XS_WMIN = 8;
+
 template <int NI>
 __device__ __forceinline__ void mfma_fence(float (&acc)[NI], const h8 &A, const h8 &B, const f4 &D) {
   static_assert(NI >= 1 && NI <= 4, "columns per lane");
@@ -107,8 +111,8 @@ template <int QT, int NC, int NMAT, int EPI, int RT, int PF, int WKT, int PH, bo
           class Hook = NoHook>
 __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t *smem, uint32_t *flag,
                                           float &bv, int32_t &bi, Hook staged = Hook()) {
-  // WKT == 0: one row tile per wave of the workgroup as launched
-  static_assert(WKT > 0 || NC < 16, "streamed staging needs a fixed workgroup size");
+  // WKT == 0: one row tile per wave of the workgroup as launched (at least
+  // XWMIN waves when the activations stream in chunks)
   const int NTHR = WKT > 0 ? WKT * 64 : (int)blockDim.x;
   constexpr int XC = NC;  // activation columns in the LDS layout
   // accumulators per lane: dot form, one per column; matrix-core form, the
@@ -124,7 +128,8 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   constexpr bool XS = NC >= 16;
   constexpr int CHV = PF * TILE_BLOCKS * NC * 4;   // 8-value pieces per chunk
   constexpr int CHH = PF * TILE_BLOCKS * NC * 32;  // halves per chunk buffer
-  constexpr int XR = WKT > 0 ? (CHV + WKT * 64 - 1) / (WKT * 64) : 1;  // pieces per thread per chunk
+  constexpr int XWMIN = WKT > 0 ? WKT : DOT_XS_WMIN;
+  constexpr int XR = (CHV + XWMIN * 64 - 1) / (XWMIN * 64);  // pieces per thread per chunk (at most)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wk = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -422,6 +427,16 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
       }
     emitted = arrive_last(a.cnt + g, (uint32_t)a.S, flag);
     if (emitted) {
+      // every segment's partial of a value is loaded before any is added
+      // (one round trip per RB segments, not one per segment), then they
+      // are added in segment order; coherent loads (sc1) over a bounded
+      // range of this launch's partials
+      constexpr int RB = 8;
+      const int64_t pbytes = (int64_t)a.S * NMAT * rows_pad * NC * 4;
+      const __amdgpu_buffer_rsrc_t rp = buf_range(a.part, (uint32_t)(pbytes < 0x7FFFFFFF ? pbytes : 0x7FFFFFFF));
+      auto poff = [&](int ss, int m, int64_t row, int c) -> uint32_t {
+        return ss < a.S ? (uint32_t)(((((int64_t)ss * NMAT + m) * rows_pad + row) * NC + c) * 4) : 0xFFFFFFC0u;
+      };
 #pragma unroll
       for (int t = 0; t < RT; ++t)
 #pragma unroll
@@ -430,11 +445,19 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
           if (c >= 0 && rt_base + t < a.NT) {
             const int64_t row = (rt_base + t) * 16 + r;
             float v[NMAT];
+            for (int s0 = 0; s0 < a.S; s0 += RB) {
+              float p[NMAT][RB];
 #pragma unroll
-            for (int m = 0; m < NMAT; ++m) {
-              float x = ld_agent(slot_of(0, m, row, c));
-              for (int ss = 1; ss < a.S; ++ss) x += ld_agent(slot_of(ss, m, row, c));
-              v[m] = x;
+              for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                for (int j = 0; j < RB; ++j)
+                  p[m][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                          rp, poff(s0 + j, m, row, c), 0, 16));
+#pragma unroll
+              for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                for (int j = 0; j < RB; ++j)
+                  if (s0 + j < a.S) v[m] = s0 + j == 0 ? p[m][j] : v[m] + p[m][j];
             }
             emit(t, c, v);
           }

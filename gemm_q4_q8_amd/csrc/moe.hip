@@ -380,15 +380,31 @@ __global__ void __launch_bounds__(DN_WKT * 64) moe_down_kernel(MoeArgs a) {
   if (!arrive_last(a.dcnt + g, target, &flag)) return;
   const int64_t r0 = (int64_t)g * DN_WKT * 16;
   const int nr = (int)((a.H - r0) < DN_WKT * 16 ? (a.H - r0) : DN_WKT * 16);
+  const __amdgpu_buffer_rsrc_t rz = buf_range(a.zbuf, (uint32_t)((int64_t)(a.T * a.k + a.T) * a.H * 4));
+  const __amdgpu_buffer_rsrc_t rpw = buf_range(a.pw, (uint32_t)(a.T * a.k * 4));
   for (int o = tid; o < nr * a.T; o += NTHR) {
     const int t = o / nr, rr = o % nr;
     const int64_t row = r0 + rr;
-    float sum = 0.0f;
-    for (int kk = 0; kk < a.k; ++kk)
-      sum = __builtin_fmaf(a.pw[t * a.k + kk], ld_agent(a.zbuf + (int64_t)(t * a.k + kk) * a.H + row), sum);
-    if (a.SF > 0) sum += ld_agent(a.zbuf + (int64_t)(a.T * a.k + t) * a.H + row);
+    // all k (<= 8) slot outputs and weights, and the shared expert's, are
+    // loaded before the sum: bounded ranges, offsets past them read zeros
+    float z[8], p[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const uint32_t zo = kk < a.k ? (uint32_t)(((int64_t)(t * a.k + kk) * a.H + row) * 4) : 0xFFFFFFC0u;
+      const uint32_t po = kk < a.k ? (uint32_t)((t * a.k + kk) * 4) : 0xFFFFFFC0u;
+      z[kk] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rz, zo, 0, 16));
+      p[kk] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rpw, po, 0, 0));
+    }
+    const uint32_t so = a.SF > 0 ? (uint32_t)(((int64_t)(a.T * a.k + t) * a.H + row) * 4) : 0xFFFFFFC0u;
+    const float zs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rz, so, 0, 16));
     float *yp = a.Y + (int64_t)t * a.ldy + row;
-    *yp = *yp + sum;
+    const float y0 = *yp;
+    float sum = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      if (kk < a.k) sum = __builtin_fmaf(p[kk], z[kk], sum);
+    if (a.SF > 0) sum += zs;
+    *yp = y0 + sum;
   }
 }
 

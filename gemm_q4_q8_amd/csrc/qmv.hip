@@ -69,10 +69,23 @@ __global__ void __launch_bounds__(WMAX * 64) dot_kernel(DotArgs a) {
     if (!arrive_last(a.gcnt, (uint32_t)a.G, &flag)) return;
     bv = __builtin_nanf("");
     bi = 0x7fffffff;
-    for (int qq = tid; qq < a.G; qq += NTHR) {
-      const float v = ld_agent(a.cand_v + qq);
-      const int32_t i = (int32_t)ld_agent_u32((const uint32_t *)a.cand_i + qq);
-      if (ranks_before(v, i, bv, bi)) { bv = v; bi = i; }
+    // candidates in batches of 4 per thread, all loaded before any is used
+    // (coherent loads over bounded ranges; slots past G are skipped)
+    const __amdgpu_buffer_rsrc_t rv = buf_range(a.cand_v, (uint32_t)a.G * 4u);
+    const __amdgpu_buffer_rsrc_t ri = buf_range(a.cand_i, (uint32_t)a.G * 4u);
+    for (int q0 = tid; q0 < a.G; q0 += 4 * NTHR) {
+      float v[4];
+      int32_t id[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int q = q0 + j * NTHR;
+        const uint32_t o = q < a.G ? (uint32_t)q * 4u : 0xFFFFFFC0u;
+        v[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rv, o, 0, 16));
+        id[j] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ri, o, 0, 16);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (q0 + j * NTHR < a.G && ranks_before(v[j], id[j], bv, bi)) { bv = v[j]; bi = id[j]; }
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -138,7 +151,7 @@ int gemm16_splits(int64_t rows, int64_t cols) {
 #ifdef GEMM16_EXP
   if (const char *e = getenv("QG_EXP_G16S")) return atoi(e);
 #endif
-  int64_t s = GEMM16_STREAMS / NT;
+  int64_t s = (GEMM16_STREAMS + NT / 2) / NT;  // nearest
   if (s > KT / 4) s = KT / 4;
   if (s < 1) s = 1;
   return (int)s;
@@ -188,6 +201,7 @@ static int launch_dot_t(const QmvCall &c, int S, int W = WKT) {
   a.KT = (int)KT;
   a.S = S;
   if (W < 1 || W > WMAX || (WKT > 0 && W != WKT)) return QG_EUNSUPPORTED;
+  if (NC >= 16 && WKT == 0 && W < DOT_XS_WMIN) return QG_EUNSUPPORTED;
   a.G = (int)cdiv(NTu, (int64_t)W * RT);
   a.units = (int64_t)a.G * S;
   a.per_xcd = cdiv(a.units, 8);
@@ -218,7 +232,9 @@ static int launch_dot_t(const QmvCall &c, int S, int W = WKT) {
   a.xmap = a.ymap = nullptr;
   a.xspan = 0;
   if (!ranges_fit(c, NT, KT, QTraits<QT>::tile_bytes)) return QG_EUNSUPPORTED;
-  const size_t need = off + (S > 1 ? (size_t)S * NMAT * NTu * 16 * NC * 4 : 0);
+  const size_t pbytes = S > 1 ? (size_t)S * NMAT * NTu * 16 * NC * 4 : 0;
+  if (pbytes >= ((size_t)1 << 31)) return QG_EUNSUPPORTED;  // one bounded range
+  const size_t need = off + pbytes;
   if (need > c.ws_bytes) return QG_EWORKSPACE;
 
   // staged activations: the whole segment, or (16 columns) two chunks of
@@ -294,21 +310,34 @@ static int dispatch_silu(const QmvCall &c, int S) {
 }
 
 // 16 columns: the shared dot unit on the matrix cores (one row tile per
-// wave, PF = 4 tile columns in flight; measured best on the prefill shapes).
+// wave, PF = 4 tile columns in flight; measured best on the prefill shapes,
+// as was the workgroup size below: a smaller workgroup waits less at the
+// per-chunk barrier, so the smallest size that keeps one per CU).
 template <int QT, int EPI>
 static int launch_gemm16(const QmvCall &c) {
   const int S = gemm16_splits(c.rows, c.cols);
 #ifdef GEMM16_EXP
   if (const char *e = getenv("QG_EXP_G16")) {
-    int rt = 0, w = 0, pf = 0;
-    if (sscanf(e, "%d,%d,%d", &rt, &w, &pf) == 3) {
-#define G16(R, W, P) if (rt == R && w == W && pf == P) return launch_dot_t<QT, 16, 1, EPI, R, P, W, true>(c, S);
-      G16(1, 8, 2) G16(1, 8, 4) G16(2, 8, 2) G16(2, 8, 4) G16(2, 4, 2) G16(2, 16, 2) G16(1, 16, 4)
+    int w = 0, pf = 0;
+    if (sscanf(e, "%d,%d", &w, &pf) == 2) {
+      if (pf == 2) return launch_dot_t<QT, 16, 1, EPI, 1, 2, 0, true, 16>(c, S, w);
+      if (pf == 4) return launch_dot_t<QT, 16, 1, EPI, 1, 4, 0, true, 16>(c, S, w);
+      if (pf == 8) return launch_dot_t<QT, 16, 1, EPI, 1, 8, 0, true, 16>(c, S, w);
       return QG_EUNSUPPORTED;
     }
   }
 #endif
-  return launch_dot_t<QT, 16, 1, EPI, 1, 4, 8, true>(c, S);
+  // at least 8 waves (the activation chunks are sized for them), else as
+  // for the GEMV: one workgroup per CU when 8 to 16 waves allow it
+  const int64_t NTu = cdiv(c.n_rows, 16), ncu = device_cus();
+  int W = 8;
+  for (int w = 8; w <= 16; ++w)
+    if (cdiv(NTu, w) * S <= ncu) {
+      W = w;
+      break;
+    }
+  if (W == 8) return launch_dot_t<QT, 16, 1, EPI, 1, 4, 8, true>(c, S);
+  return launch_dot_t<QT, 16, 1, EPI, 1, 4, 0, true, 16>(c, S, W);
 }
 
 template <int QT>
