@@ -52,8 +52,10 @@ struct DotArgs {
   int64_t rows;       // outputs produced (n_rows for the LM head)
   int64_t cols;
   int NT, KT;         // row tiles produced, tile columns of the matrix
-  int S;              // K segments
-  int G;              // row groups of WKT * RT row tiles
+  int S;              // K segments across workgroups
+  int SW;             // K segments inside one workgroup (<= 1: none): wave wk
+                      // streams segment wk / R of row tile wk % R, R = waves / SW
+  int G;              // row groups of R * RT row tiles
   int64_t units;      // G * S workgroups
   int64_t per_xcd;
   const float *X;
@@ -133,9 +135,16 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wk = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // the workgroup's K range (staged in LDS), and inside it this wave's
+  // stream: all of it, or (SW > 1) in-workgroup segment wsg of SW
+  const int SW = (!XS && a.SW > 1) ? a.SW : 1;
+  const int R = (NTHR >> 6) / SW;
+  const int wrt = wk % R, wsg = wk / R;
   const int kt0 = seg_begin(s, a.KT, a.S);
   const int nkt = seg_begin(s + 1, a.KT, a.S) - kt0;
-  const int64_t rt_base = ((int64_t)g * (NTHR >> 6) + wk) * RT;
+  const int wkt0 = seg_begin(wsg, nkt, SW);         // relative to kt0
+  const int wnkt = seg_begin(wsg + 1, nkt, SW) - wkt0;
+  const int64_t rt_base = ((int64_t)g * R + wrt) * RT;
   const int r = lane & 15, sl = lane >> 4;
   _Float16 *xs = (_Float16 *)smem;
 
@@ -175,9 +184,9 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const bool in = rt_base + t < a.NT;
-      const int64_t tile = (in ? rt_base + t : 0) * a.KT + kt0;
-      rq[m][t] = buf_range((m ? a.qs1 : a.qs0) + tile * TB, in ? (uint32_t)nkt * TB : 0u);
-      rd[m][t] = buf_range((m ? a.d1 : a.d0) + tile * TILE_D_BYTES, in ? (uint32_t)nkt * TILE_D_BYTES : 0u);
+      const int64_t tile = (in ? rt_base + t : 0) * a.KT + kt0 + wkt0;
+      rq[m][t] = buf_range((m ? a.qs1 : a.qs0) + tile * TB, in ? (uint32_t)wnkt * TB : 0u);
+      rd[m][t] = buf_range((m ? a.d1 : a.d0) + tile * TILE_D_BYTES, in ? (uint32_t)wnkt * TILE_D_BYTES : 0u);
     }
   u4 wq[PF][NMAT][RT][QW];
   u2 wd[PF][NMAT][RT];
@@ -258,9 +267,10 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   // the register set to zero here stays zero.
   h8 A = {0, 0, 0, 0, 0, 0, 0, 0};
   auto compute = [&](int slot, int rel) {
-    // block index in LDS: the segment's own (rel), or, streaming, the slot
-    // of tile column rel in its chunk's buffer
-    const int bl0 = XS ? ((((rel / PF) & 1) * PF) + rel % PF) * TILE_BLOCKS : rel * TILE_BLOCKS;
+    // block index in LDS: the staged range's own (this wave's stream starts
+    // wkt0 tile columns in), or, streaming, the slot of tile column rel in
+    // its chunk's buffer
+    const int bl0 = XS ? ((((rel / PF) & 1) * PF) + rel % PF) * TILE_BLOCKS : (wkt0 + rel) * TILE_BLOCKS;
     if constexpr (MF) {
       // per block: D (16 columns x 16 rows) = X_blk^T W_blk^T on the matrix
       // cores from the exact f16 weights, then each lane's 4 D values get
@@ -333,7 +343,7 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
       __syncthreads();
     }
   } else {
-    const int nseg = rt_base < a.NT ? nkt : 0;
+    const int nseg = rt_base < a.NT ? wnkt : 0;
     for (int k = 0; k < nseg; k += PF) {
 #pragma unroll
       for (int p = 0; p < PF; ++p) {
@@ -392,6 +402,35 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
     }
   };
 
+  // in-workgroup segments: the waves of segments 1.. leave their sums in
+  // LDS (past the staged activations, which slower waves may still read);
+  // the segment-0 wave of each row tile adds them in segment order, the
+  // same order as the partials of segments across workgroups
+  if (SW > 1) {
+    constexpr int NV = NMAT * RT * NI;
+    float *red = (float *)(smem + (size_t)((a.KT + a.S - 1) / a.S) * TILE_BLOCKS * NC * 64);
+    if (wsg > 0) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+          for (int i = 0; i < NI; ++i)
+            red[((((wsg - 1) * R + wrt) * NV) + (m * RT + t) * NI + i) * 64 + lane] = acc[m][t][i];
+    }
+    __syncthreads();
+    if (wsg == 0) {
+      for (int q = 1; q < SW; ++q)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+              acc[m][t][i] += red[((((q - 1) * R + wrt) * NV) + (m * RT + t) * NI + i) * 64 + lane];
+    }
+  }
+
   bool emitted;
   if (a.S == 1) {
 #pragma unroll
@@ -399,7 +438,7 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int c = col_of(t, i);
-        if (c >= 0) {
+        if (c >= 0 && wsg == 0) {
           float v[NMAT];
 #pragma unroll
           for (int m = 0; m < NMAT; ++m) v[m] = acc[m][t][i];

@@ -17,7 +17,7 @@
 #include "dot_unit.h"
 #include "internal.h"
 #include "qgemm.h"
-#ifdef GEMM16_EXP
+#if defined(GEMM16_EXP) || defined(DOT_EXP)
 #include <stdio.h>
 #include <stdlib.h>
 #endif
@@ -121,6 +121,7 @@ int device_cus() {
 constexpr int DOT_STREAMS = 2048;     // (row tile, segment, matrix) weight streams
 constexpr size_t DOT_X_LDS = 65536;   // staged activations per workgroup
 constexpr size_t LDS_HARD = 163840;   // gfx950 LDS per workgroup
+constexpr size_t DOT_SW_LDS = 98304;  // in-workgroup segments: activations + sums
 
 // K segments of the dot path: about DOT_STREAMS weight streams of one row
 // tile and one segment each (measured on the decode shapes: more streams,
@@ -186,8 +187,10 @@ static int grant_lds(const void *kern, size_t lds, size_t &granted) {
   return QG_OK;
 }
 
+// S segments across workgroups; SW > 1: segments inside each workgroup
+// instead (S must then be 1), W = R * SW waves for R row tiles.
 template <int QT, int NC, int NMAT, int EPI, int RT, int PF, int WKT, bool MF, int WMAX = WKT>
-static int launch_dot_t(const QmvCall &c, int S, int W = WKT) {
+static int launch_dot_t(const QmvCall &c, int S, int W = WKT, int SW = 1) {
   const int64_t NT = cdiv(c.rows, 16), KT = cdiv(c.cols / 32, 4);
   const int64_t NTu = cdiv(c.n_rows, 16);  // row tiles actually produced
   DotArgs a;
@@ -200,9 +203,11 @@ static int launch_dot_t(const QmvCall &c, int S, int W = WKT) {
   a.NT = (int)NTu;
   a.KT = (int)KT;
   a.S = S;
+  a.SW = SW;
   if (W < 1 || W > WMAX || (WKT > 0 && W != WKT)) return QG_EUNSUPPORTED;
   if (NC >= 16 && WKT == 0 && W < DOT_XS_WMIN) return QG_EUNSUPPORTED;
-  a.G = (int)cdiv(NTu, (int64_t)W * RT);
+  if (SW < 1 || (SW > 1 && (S != 1 || NC >= 16 || W % SW != 0))) return QG_EUNSUPPORTED;
+  a.G = (int)cdiv(NTu, (int64_t)(W / SW) * RT);
   a.units = (int64_t)a.G * S;
   a.per_xcd = cdiv(a.units, 8);
   a.X = c.X;
@@ -239,7 +244,9 @@ static int launch_dot_t(const QmvCall &c, int S, int W = WKT) {
 
   // staged activations: the whole segment, or (16 columns) two chunks of
   // PF tile columns
-  const size_t lds = NC >= 16 ? (size_t)2 * PF * TILE_BLOCKS * NC * 64 : (size_t)cdiv(KT, S) * TILE_BLOCKS * NC * 64;
+  // PF tile columns (+ the in-workgroup segment sums)
+  size_t lds = NC >= 16 ? (size_t)2 * PF * TILE_BLOCKS * NC * 64 : (size_t)cdiv(KT, S) * TILE_BLOCKS * NC * 64;
+  lds += (size_t)(SW - 1) * (W / SW) * NMAT * RT * (MF ? (NC < 4 ? NC : 4) : NC) * 64 * 4;
   if (lds > LDS_HARD - 1024) return QG_EUNSUPPORTED;
   auto kern = dot_kernel<QT, NC, NMAT, EPI, RT, PF, WKT, MF, WMAX>;
   static size_t granted = 65536;  // per instantiation; only ever raised
@@ -275,6 +282,31 @@ static int launch_dot(const QmvCall &c, int S) {
   const int64_t NTu = cdiv(c.n_rows, 16);
   constexpr bool MF = DOT_MF;
   const int W = dot_waves(NTu, S);
+  if (S > 1) {
+    // The segments as waves of one workgroup, summed through LDS: no
+    // partials in memory and no second round trip at the end (about 2-3 us
+    // on the decode shapes), same segments and order, so the same bits as
+    // across workgroups.  Possible when a workgroup of R row tiles x S
+    // segments (at most 16 waves) leaves one workgroup per CU and the whole
+    // K range of activations fits in LDS; chosen when it keeps at least 90%
+    // of the CUs the split across workgroups would use, or when each CU's
+    // share of the weights is small (<= 192 KiB: the tail is then a large
+    // part of the time).  Measured: faster for verify at 4 / 8 columns and
+    // small GEMVs, slower for the decode gate/up and down projections.
+    const int64_t ncu = device_cus();
+    const int64_t R = cdiv(NTu, ncu);
+    const int64_t KT = cdiv(c.cols / 32, 4);
+    constexpr int NI = MF ? (NC < 4 ? NC : 4) : NC;
+    const size_t lds = (size_t)KT * TILE_BLOCKS * NC * 64 + (size_t)(S - 1) * R * NMAT * NI * 64 * 4;
+    const int64_t u_sw = cdiv(NTu, R), u_cross = cdiv(NTu, (int64_t)W) * S;
+    const int64_t cu_bytes = (int64_t)NMAT * R * KT * (QTraits<QT>::tile_bytes + TILE_D_BYTES);
+    bool sw = R * S <= 16 && lds <= DOT_SW_LDS && (10 * u_sw >= 9 * u_cross || cu_bytes <= 196608);
+#ifdef DOT_EXP
+    if (getenv("QG_NO_SW")) sw = false;
+    if (getenv("QG_FORCE_SW")) sw = R * S <= 16 && lds <= DOT_SW_LDS;
+#endif
+    if (sw) return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 16>(c, 1, (int)(R * S), S);
+  }
   if (W <= 8) return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 8>(c, S, W);
   return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 16>(c, S, W);
 }
