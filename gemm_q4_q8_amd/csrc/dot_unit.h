@@ -63,7 +63,7 @@ struct DotArgs {
   int ncols;
   float *Y;
   int64_t ldy;
-  float *part;        // segment partials [S][NMAT][NT*16][NC]
+  float *part;        // segment partials [S][NMAT][NT][NI][64 lanes]
   uint32_t *cnt;      // [G]
   uint32_t *gcnt;     // argmax: one counter
   float *cand_v;      // argmax: [G]
@@ -94,6 +94,10 @@ struct NoHook {
 // the FMAs produced, so it is ordered after those FMAs (which wait for the
 // product to complete) and all of A, B and D stay allocated until then, also
 // the result values no FMA reads (fewer than four columns).
+// Floats of one row tile's segment partial: NI values per lane, 64 lanes
+// (NI: columns per lane, at most 4 in the matrix-core form).
+__host__ __device__ constexpr int dot_part_floats(int nc) { return (DOT_MF ? (nc < 4 ? nc : 4) : nc) * 64; }
+
 // Smallest workgroup (waves) a streamed-staging unit of launch-time size
 // runs with: its per-thread chunk pieces are sized for it.
 constexpr int DOT_XS_WMIN = 8;
@@ -449,9 +453,10 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   } else {
     // publish the segment partials; the last workgroup of the row group
     // adds them in segment order
-    const int64_t rows_pad = (int64_t)a.NT * 16;
-    auto slot_of = [&](int ss, int m, int64_t row, int c) {
-      return a.part + (((int64_t)ss * NMAT + m) * rows_pad + row) * NC + c;
+    // layout [segment][matrix][row tile][value i][lane]: each store and
+    // load instruction of a wave covers one contiguous run
+    auto pidx = [&](int ss, int m, int t, int i) -> int64_t {
+      return ((((int64_t)ss * NMAT + m) * a.NT + (rt_base + t)) * NI + i) * 64 + lane;
     };
 #pragma unroll
     for (int t = 0; t < RT; ++t)
@@ -459,47 +464,52 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
       for (int i = 0; i < NI; ++i) {
         const int c = col_of(t, i);
         if (c >= 0 && rt_base + t < a.NT) {
-          const int64_t row = (rt_base + t) * 16 + r;
 #pragma unroll
-          for (int m = 0; m < NMAT; ++m) st_agent(slot_of(s, m, row, c), acc[m][t][i]);
+          for (int m = 0; m < NMAT; ++m) st_agent(a.part + pidx(s, m, t, i), acc[m][t][i]);
         }
       }
     emitted = arrive_last(a.cnt + g, (uint32_t)a.S, flag);
     if (emitted) {
-      // every segment's partial of a value is loaded before any is added
-      // (one round trip per RB segments, not one per segment), then they
-      // are added in segment order; coherent loads (sc1) over a bounded
-      // range of this launch's partials
-      constexpr int RB = 8;
-      const int64_t pbytes = (int64_t)a.S * NMAT * rows_pad * NC * 4;
+      // every segment's partial of every value this lane emits is loaded
+      // before any is added (one round trip per RB segments, not one per
+      // segment and value), then they are added in segment order; coherent
+      // loads (sc1) over a bounded range of this launch's partials
+      constexpr int RB = RT * NI * NMAT >= 8 ? 4 : 8;
+      const int64_t pbytes = (int64_t)a.S * NMAT * a.NT * NI * 64 * 4;
       const __amdgpu_buffer_rsrc_t rp = buf_range(a.part, (uint32_t)(pbytes < 0x7FFFFFFF ? pbytes : 0x7FFFFFFF));
-      auto poff = [&](int ss, int m, int64_t row, int c) -> uint32_t {
-        return ss < a.S ? (uint32_t)(((((int64_t)ss * NMAT + m) * rows_pad + row) * NC + c) * 4) : 0xFFFFFFC0u;
+      auto poff = [&](int ss, int m, int t, int i) -> uint32_t {
+        return (ss < a.S && col_of(t, i) >= 0 && rt_base + t < a.NT) ? (uint32_t)(pidx(ss, m, t, i) * 4)
+                                                                      : 0xFFFFFFC0u;
       };
+      float v[RT][NI][NMAT];
+      for (int s0 = 0; s0 < a.S; s0 += RB) {
+        float p[RT][NI][NMAT][RB];
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+          for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+              for (int j = 0; j < RB; ++j)
+                p[t][i][m][j] = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(rp, poff(s0 + j, m, t, i), 0, 16));
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+          for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+              for (int j = 0; j < RB; ++j)
+                if (s0 + j < a.S) v[t][i][m] = s0 + j == 0 ? p[t][i][m][j] : v[t][i][m] + p[t][i][m][j];
+      }
 #pragma unroll
       for (int t = 0; t < RT; ++t)
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
           const int c = col_of(t, i);
-          if (c >= 0 && rt_base + t < a.NT) {
-            const int64_t row = (rt_base + t) * 16 + r;
-            float v[NMAT];
-            for (int s0 = 0; s0 < a.S; s0 += RB) {
-              float p[NMAT][RB];
-#pragma unroll
-              for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                for (int j = 0; j < RB; ++j)
-                  p[m][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                          rp, poff(s0 + j, m, row, c), 0, 16));
-#pragma unroll
-              for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                for (int j = 0; j < RB; ++j)
-                  if (s0 + j < a.S) v[m] = s0 + j == 0 ? p[m][j] : v[m] + p[m][j];
-            }
-            emit(t, c, v);
-          }
+          if (c >= 0 && rt_base + t < a.NT) emit(t, c, v[t][i]);
         }
     }
   }

@@ -92,10 +92,10 @@ static FfnLayout ffn_layout(int64_t hidden, int64_t ffn) {
   L.GB = (int)cdiv(cdiv(hidden, 16), FFN_WKT);
   size_t o = QG_WS_SYNC_BYTES;
   L.part_a = o;
-  if (L.SA > 1) o += (size_t)L.SA * 2 * cdiv(ffn, 16) * 16 * 4;
+  if (L.SA > 1) o += (size_t)L.SA * 2 * cdiv(ffn, 16) * dot_part_floats(1) * 4;
   o = (o + 255) & ~size_t(255);
   L.part_b = o;
-  if (L.SB > 1) o += (size_t)L.SB * cdiv(hidden, 16) * 16 * 4;
+  if (L.SB > 1) o += (size_t)L.SB * cdiv(hidden, 16) * dot_part_floats(1) * 4;
   L.total = (o + 255) & ~size_t(255);
   return L;
 }

@@ -92,7 +92,7 @@ static MoeLayout moe_layout(const qg_moe *m, int T) {
   L.S_gu = moe_s_gu(m->hidden, T);
   L.G_gu = (int)cdiv(Fmax / 16, GU_WKT);
   L.G_dn = (int)cdiv(m->hidden / 16, DN_WKT);
-  L.gpart_per = L.S_gu > 1 ? (int64_t)L.S_gu * 2 * Fmax * nc : 0;
+  L.gpart_per = L.S_gu > 1 ? (int64_t)L.S_gu * 2 * (Fmax / 16) * dot_part_floats(nc) : 0;
   // counters (in the shared counter words): the router's, one per down row
   // group, one per (listed expert, gate/up row group)
   L.rcnt_w = 0;

@@ -163,7 +163,7 @@ size_t qmv_ws_bytes(int64_t rows, int64_t cols, int slots, int nmat, int ncols_m
   (void)cols;
   size_t b = QG_WS_SYNC_BYTES;                      // counters
   if (argmax) b += 2 * align256((size_t)NT * 4);    // candidates
-  if (slots > 1) b += (size_t)slots * nmat * NT * 16 * ncols_max * 4;
+  if (slots > 1) b += (size_t)slots * nmat * NT * dot_part_floats(ncols_max) * 4;
   return b;
 }
 
@@ -237,7 +237,7 @@ static int launch_dot_t(const QmvCall &c, int S, int W = WKT, int SW = 1) {
   a.xmap = a.ymap = nullptr;
   a.xspan = 0;
   if (!ranges_fit(c, NT, KT, QTraits<QT>::tile_bytes)) return QG_EUNSUPPORTED;
-  const size_t pbytes = S > 1 ? (size_t)S * NMAT * NTu * 16 * NC * 4 : 0;
+  const size_t pbytes = S > 1 ? (size_t)S * NMAT * NTu * dot_part_floats(NC) * 4 : 0;
   if (pbytes >= ((size_t)1 << 31)) return QG_EUNSUPPORTED;  // one bounded range
   const size_t need = off + pbytes;
   if (need > c.ws_bytes) return QG_EWORKSPACE;

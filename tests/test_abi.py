@@ -58,7 +58,8 @@ def test_packed_bytes_rejects():
 def test_ws_queries():
     assert L.qg_gemv_ws_bytes(5120, 17408) > 0
     assert L.qg_gemv_ws_bytes(5120, 17) == 0
-    assert L.qg_gemm16_ws_bytes(2, 5120, 17408) > L.qg_gemv_ws_bytes(5120, 17408)
+    # 16 columns hold at least the partials of 8 (4 values per lane either way)
+    assert L.qg_gemm16_ws_bytes(2, 5120, 17408) >= L.qg_gemv_ws_bytes(5120, 17408)
     assert L.qg_gateup_ws_bytes(17408, 5120) >= L.qg_gemv_ws_bytes(17408, 5120)
     assert L.qg_lmhead_ws_bytes(248320, 5120) > 0
 
