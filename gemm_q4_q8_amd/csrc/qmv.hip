@@ -145,14 +145,17 @@ int gemv_segments(int64_t rows, int64_t cols, int nmat, int ncols_max) {
 
 // K segments of the 16-column GEMM (its activations stream through LDS in
 // chunks, so the segment length is free): about GEMM16_STREAMS (row tile,
-// segment) weight streams, at least 4 tile columns per segment.
-constexpr int GEMM16_STREAMS = 2048;
+// segment) weight streams, at least 4 tile columns per segment, and few
+// enough that workgroups of at most 16 waves fit one per CU of a 256-CU
+// part (a constant, so the reduction order stays a function of the shape).
+constexpr int GEMM16_STREAMS = 3000;
 int gemm16_splits(int64_t rows, int64_t cols) {
   const int64_t NT = cdiv(rows, 16), KT = cdiv(cols / 32, 4);
 #ifdef GEMM16_EXP
   if (const char *e = getenv("QG_EXP_G16S")) return atoi(e);
 #endif
   int64_t s = (GEMM16_STREAMS + NT / 2) / NT;  // nearest
+  if (s > 256 / cdiv(NT, 16)) s = 256 / cdiv(NT, 16);
   if (s > KT / 4) s = KT / 4;
   if (s < 1) s = 1;
   return (int)s;
@@ -342,7 +345,7 @@ static int dispatch_silu(const QmvCall &c, int S) {
 }
 
 // 16 columns: the shared dot unit on the matrix cores (one row tile per
-// wave, PF = 4 tile columns in flight; measured best on the prefill shapes,
+// wave, PF = 2 tile columns in flight; measured best on the prefill shapes,
 // as was the workgroup size below: a smaller workgroup waits less at the
 // per-chunk barrier, so the smallest size that keeps one per CU).
 template <int QT, int EPI>
@@ -368,8 +371,8 @@ static int launch_gemm16(const QmvCall &c) {
       W = w;
       break;
     }
-  if (W == 8) return launch_dot_t<QT, 16, 1, EPI, 1, 4, 8, true>(c, S);
-  return launch_dot_t<QT, 16, 1, EPI, 1, 4, 0, true, 16>(c, S, W);
+  if (W == 8) return launch_dot_t<QT, 16, 1, EPI, 1, 2, 8, true>(c, S);
+  return launch_dot_t<QT, 16, 1, EPI, 1, 2, 0, true, 16>(c, S, W);
 }
 
 template <int QT>
