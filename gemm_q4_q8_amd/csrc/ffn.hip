@@ -40,7 +40,7 @@ struct FfnArgs {
 constexpr int FFN_WKT = 8;  // 8 row tiles = 128 h rows = one down tile column
 
 template <int QT, int PFA, int PFB>
-__global__ void __launch_bounds__(FFN_WKT * 64) ffn_kernel(FfnArgs f) {
+__global__ void __launch_bounds__(FFN_WKT * 64, 2) ffn_kernel(FfnArgs f) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ uint32_t flag;
   __shared__ int s_next;

@@ -22,6 +22,10 @@
 // Workgroups beyond the listed experts exit at once (the grid is the worst
 // case, the list is on the device).
 #include <string.h>
+#ifdef MOE_EXP
+#include <stdio.h>
+#include <stdlib.h>
+#endif
 
 #include "common.h"
 #include "dot_unit.h"
@@ -32,8 +36,7 @@ namespace qg {
 
 constexpr int RW = 16;      // router: experts (waves) per workgroup, = TMAX
 constexpr int TMAX = 16;    // tokens per call
-constexpr int GU_WKT = 2;   // gate/up: row tiles per workgroup
-constexpr int DN_WKT = 8;   // down: row tiles per workgroup (128 rows)
+constexpr int MOE_WMAX = 16;  // expert units: at most 16 waves (row tiles) per workgroup
 
 struct MoeArgs {
   int64_t H, F, SF, Fmax;
@@ -53,6 +56,7 @@ struct MoeArgs {
   float *logits, *pw, *hbuf, *zbuf, *gpart;
   int32_t *sel, *used_e, *used_cnt, *used_slot;
   int S_gu, G_gu, G_dn;   // gate/up K segments and row groups (at Fmax rows); down row groups
+  int W_gu, W_dn;         // waves (row tiles) per gate/up and per down workgroup
   int nsh;                // shared-expert entries (tokens in groups of the unit width)
   int64_t gpart_per;      // gate/up partial floats per listed expert
 };
@@ -64,12 +68,27 @@ __host__ __device__ static inline int64_t cdiv(int64_t a, int64_t b) { return (a
 // many routed slots of one expert (an expert with more gets several
 // entries, each reading its weights once for its slots).
 static int moe_nc(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : 4; }
-// gate/up K segments: short streams at one token (latency-bound), longer
-// ones when more columns share each weight tile
+// gate/up K segments: short streams at one or two tokens (latency-bound),
+// one segment when more columns share each weight tile
 static int moe_s_gu(int64_t H, int T) {
   const int64_t KT = H / 128;
-  int64_t s = T <= 2 ? KT / 4 : KT / 8;
+  int64_t s = T <= 2 ? KT / 4 : 1;
+#ifdef MOE_EXP
+  if (const char *e = getenv("QG_MOE_S")) s = atoi(e);
+#endif
   return (int)(s < 1 ? 1 : s);
+}
+
+// Waves (row tiles) per expert workgroup: gate/up, down.
+static void moe_waves(int T, int &w_gu, int &w_dn) {
+  // measured on the 256-expert layer: small gate/up workgroups at one or
+  // two tokens (many short streams), 8 row tiles once several tokens share
+  // the experts (fewer, longer units)
+  w_gu = T <= 2 ? 2 : 8;
+  w_dn = 8;
+#ifdef MOE_EXP
+  if (const char *e = getenv("QG_MOE_W")) sscanf(e, "%d,%d", &w_gu, &w_dn);
+#endif
 }
 
 struct MoeLayout {
@@ -77,6 +96,7 @@ struct MoeLayout {
   int64_t umax;  // work-list entries at most
   size_t rcnt_w, dcnt_w, gcnt_w, sync_words;  // counter word offsets
   int S_gu, G_gu, G_dn, nsh;
+  int W_gu, W_dn;
   int64_t gpart_per;
 };
 
@@ -90,8 +110,9 @@ static MoeLayout moe_layout(const qg_moe *m, int T) {
   const int64_t slots = (int64_t)T * m->top_k + T;
   L.umax = umax;
   L.S_gu = moe_s_gu(m->hidden, T);
-  L.G_gu = (int)cdiv(Fmax / 16, GU_WKT);
-  L.G_dn = (int)cdiv(m->hidden / 16, DN_WKT);
+  moe_waves(T, L.W_gu, L.W_dn);
+  L.G_gu = (int)cdiv(Fmax / 16, L.W_gu);
+  L.G_dn = (int)cdiv(m->hidden / 16, L.W_dn);
   L.gpart_per = L.S_gu > 1 ? (int64_t)L.S_gu * 2 * (Fmax / 16) * dot_part_floats(nc) : 0;
   // counters (in the shared counter words): the router's, one per down row
   // group, one per (listed expert, gate/up row group)
@@ -328,7 +349,7 @@ __device__ __forceinline__ int moe_expert(const MoeArgs &a, int u, DotArgs &d, i
 }
 
 template <int QT, int NC, int PF>
-__global__ void __launch_bounds__(GU_WKT * 64) moe_gateup_kernel(MoeArgs a) {
+__global__ void __launch_bounds__(MOE_WMAX * 64) moe_gateup_kernel(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ uint32_t flag;
   __shared__ int32_t s_x[TMAX], s_y[TMAX];
@@ -337,7 +358,7 @@ __global__ void __launch_bounds__(GU_WKT * 64) moe_gateup_kernel(MoeArgs a) {
   DotArgs d = {};
   if (!moe_expert<true, NC>(a, u, d, s_x, s_y)) return;
   d.S = a.S_gu;
-  d.G = (int)cdiv(d.NT, GU_WKT);
+  d.G = (int)cdiv(d.NT, a.W_gu);
   if (g >= d.G) return;
   d.X = a.X;
   d.ldx = a.ldx;
@@ -349,12 +370,12 @@ __global__ void __launch_bounds__(GU_WKT * 64) moe_gateup_kernel(MoeArgs a) {
   __syncthreads();  // the column maps
   float bv = 0.0f;
   int32_t bi = 0;
-  dot_unit<QT, NC, 2, EPI_SILU, 1, PF, GU_WKT, PH_PLAIN, true>(d, g, s, smem, &flag, bv, bi);
+  dot_unit<QT, NC, 2, EPI_SILU, 1, PF, 0, PH_PLAIN, true>(d, g, s, smem, &flag, bv, bi);
 }
 
 template <int QT, int NC, int PF>
-__global__ void __launch_bounds__(DN_WKT * 64) moe_down_kernel(MoeArgs a) {
-  constexpr int NTHR = DN_WKT * 64;
+__global__ void __launch_bounds__(MOE_WMAX * 64) moe_down_kernel(MoeArgs a) {
+  const int NTHR = a.W_dn * 64;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ uint32_t flag;
   __shared__ int32_t s_x[TMAX], s_y[TMAX];
@@ -373,13 +394,13 @@ __global__ void __launch_bounds__(DN_WKT * 64) moe_down_kernel(MoeArgs a) {
   float bv = 0.0f;
   int32_t bi = 0;
   // coherent stores of z (the combine below may run on another XCD)
-  dot_unit<QT, NC, 1, EPI_STORE, 1, PF, DN_WKT, PH_PRODUCE, true>(d, g, 0, smem, &flag, bv, bi);
+  dot_unit<QT, NC, 1, EPI_STORE, 1, PF, 0, PH_PRODUCE, true>(d, g, 0, smem, &flag, bv, bi);
 
   // ---- weighted combine of this row group, by the last expert to finish
   const uint32_t target = *a.nused + (a.SF > 0 ? (uint32_t)((a.T + NC - 1) / NC) : 0u);
   if (!arrive_last(a.dcnt + g, target, &flag)) return;
-  const int64_t r0 = (int64_t)g * DN_WKT * 16;
-  const int nr = (int)((a.H - r0) < DN_WKT * 16 ? (a.H - r0) : DN_WKT * 16);
+  const int64_t r0 = (int64_t)g * a.W_dn * 16;
+  const int nr = (int)((a.H - r0) < a.W_dn * 16 ? (a.H - r0) : a.W_dn * 16);
   const __amdgpu_buffer_rsrc_t rz = buf_range(a.zbuf, (uint32_t)((int64_t)(a.T * a.k + a.T) * a.H * 4));
   const __amdgpu_buffer_rsrc_t rpw = buf_range(a.pw, (uint32_t)(a.T * a.k * 4));
   for (int o = tid; o < nr * a.T; o += NTHR) {
@@ -449,7 +470,7 @@ static int launch_moe_t(const MoeCall &c, MoeArgs &a) {
   st = grant((const void *)kg, lds_g, granted_g);
   if (st) return st;
   clear_hip_error();
-  hipLaunchKernelGGL(kg, dim3((unsigned)((int64_t)(a.Umax + a.nsh) * a.G_gu * a.S_gu)), dim3(GU_WKT * 64), lds_g,
+  hipLaunchKernelGGL(kg, dim3((unsigned)((int64_t)(a.Umax + a.nsh) * a.G_gu * a.S_gu)), dim3(a.W_gu * 64), lds_g,
                      c.stream, a);
   if (launch_status() != QG_OK) return QG_EHIP;
 
@@ -458,7 +479,7 @@ static int launch_moe_t(const MoeCall &c, MoeArgs &a) {
   static size_t granted_d = 65536;
   if ((st = grant((const void *)kd, lds_d, granted_d))) return st;
   clear_hip_error();
-  hipLaunchKernelGGL(kd, dim3((unsigned)((int64_t)(a.Umax + a.nsh) * a.G_dn)), dim3(DN_WKT * 64), lds_d, c.stream, a);
+  hipLaunchKernelGGL(kd, dim3((unsigned)((int64_t)(a.Umax + a.nsh) * a.G_dn)), dim3(a.W_dn * 64), lds_d, c.stream, a);
   return launch_status();
 }
 
@@ -525,6 +546,9 @@ int launch_moe(const MoeCall &c) {
   a.G_gu = L.G_gu;
   a.G_dn = L.G_dn;
   a.gpart_per = L.gpart_per;
+  a.W_gu = L.W_gu;
+  a.W_dn = L.W_dn;
+  if (a.W_gu < 1 || a.W_gu > MOE_WMAX || a.W_dn < 1 || a.W_dn > MOE_WMAX) return QG_EUNSUPPORTED;
   a.nsh = L.nsh;
   if (m->qtype == QG_Q4_0) return launch_moe_q<Q4>(c, a);
   return launch_moe_q<Q8>(c, a);
