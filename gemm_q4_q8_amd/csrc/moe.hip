@@ -56,7 +56,8 @@ struct MoeArgs {
   float *logits, *pw, *hbuf, *zbuf, *gpart;
   int32_t *sel, *used_e, *used_cnt, *used_slot;
   int S_gu, G_gu, G_dn;   // gate/up K segments and row groups (at Fmax rows); down row groups
-  int W_gu, W_dn;         // waves (row tiles) per gate/up and per down workgroup
+  int W_gu, W_dn;         // row tiles per gate/up and per down workgroup
+  int sw_gu;              // gate/up K segments as waves of one workgroup (summed in LDS)
   int nsh;                // shared-expert entries (tokens in groups of the unit width)
   int64_t gpart_per;      // gate/up partial floats per listed expert
 };
@@ -96,7 +97,7 @@ struct MoeLayout {
   int64_t umax;  // work-list entries at most
   size_t rcnt_w, dcnt_w, gcnt_w, sync_words;  // counter word offsets
   int S_gu, G_gu, G_dn, nsh;
-  int W_gu, W_dn;
+  int W_gu, W_dn, sw_gu;
   int64_t gpart_per;
 };
 
@@ -111,6 +112,14 @@ static MoeLayout moe_layout(const qg_moe *m, int T) {
   L.umax = umax;
   L.S_gu = moe_s_gu(m->hidden, T);
   moe_waves(T, L.W_gu, L.W_dn);
+  // gate/up segments as waves of one workgroup (no partials in memory)
+  // when the workgroup stays within 16 waves and its activations (all of
+  // K, nc columns) plus the segment sums fit comfortably in LDS
+  L.sw_gu = L.S_gu > 1 && L.W_gu * L.S_gu <= MOE_WMAX &&
+            (size_t)(m->hidden / 128) * TILE_BLOCKS * nc * 64 + (size_t)L.S_gu * L.W_gu * 2 * 4 * 64 * 4 <= 65536;
+#ifdef MOE_EXP
+  if (const char *e = getenv("QG_MOE_SW")) L.sw_gu = L.sw_gu && atoi(e) != 0;
+#endif
   L.G_gu = (int)cdiv(Fmax / 16, L.W_gu);
   L.G_dn = (int)cdiv(m->hidden / 16, L.W_dn);
   L.gpart_per = L.S_gu > 1 ? (int64_t)L.S_gu * 2 * (Fmax / 16) * dot_part_floats(nc) : 0;
@@ -353,11 +362,13 @@ __global__ void __launch_bounds__(MOE_WMAX * 64) moe_gateup_kernel(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ uint32_t flag;
   __shared__ int32_t s_x[TMAX], s_y[TMAX];
-  const int per = a.G_gu * a.S_gu;
-  const int u = blockIdx.x / per, g = (blockIdx.x % per) / a.S_gu, s = blockIdx.x % a.S_gu;
+  const int sx = a.sw_gu ? 1 : a.S_gu;  // segments across workgroups
+  const int per = a.G_gu * sx;
+  const int u = blockIdx.x / per, g = (blockIdx.x % per) / sx, s = blockIdx.x % sx;
   DotArgs d = {};
   if (!moe_expert<true, NC>(a, u, d, s_x, s_y)) return;
-  d.S = a.S_gu;
+  d.S = sx;
+  d.SW = a.sw_gu ? a.S_gu : 1;
   d.G = (int)cdiv(d.NT, a.W_gu);
   if (g >= d.G) return;
   d.X = a.X;
@@ -465,12 +476,17 @@ static int launch_moe_t(const MoeCall &c, MoeArgs &a) {
   if (launch_status() != QG_OK) return QG_EHIP;
 
   auto kg = moe_gateup_kernel<QT, NC, PFG>;
-  const size_t lds_g = unit_lds<NC, PFG>(a.H / 128, a.S_gu);
+  // in-workgroup segments: all of K staged, plus the segment sums
+  const size_t lds_g = a.sw_gu ? unit_lds<NC, PFG>(a.H / 128, 1) + (size_t)(a.S_gu - 1) * a.W_gu * 2 *
+                                                                      (NC < 4 ? NC : 4) * 64 * 4
+                               : unit_lds<NC, PFG>(a.H / 128, a.S_gu);
+  const int sx = a.sw_gu ? 1 : a.S_gu;
+  const int wg_threads = a.W_gu * (a.sw_gu ? a.S_gu : 1) * 64;
   static size_t granted_g = 65536;
   st = grant((const void *)kg, lds_g, granted_g);
   if (st) return st;
   clear_hip_error();
-  hipLaunchKernelGGL(kg, dim3((unsigned)((int64_t)(a.Umax + a.nsh) * a.G_gu * a.S_gu)), dim3(a.W_gu * 64), lds_g,
+  hipLaunchKernelGGL(kg, dim3((unsigned)((int64_t)(a.Umax + a.nsh) * a.G_gu * sx)), dim3(wg_threads), lds_g,
                      c.stream, a);
   if (launch_status() != QG_OK) return QG_EHIP;
 
@@ -548,7 +564,9 @@ int launch_moe(const MoeCall &c) {
   a.gpart_per = L.gpart_per;
   a.W_gu = L.W_gu;
   a.W_dn = L.W_dn;
-  if (a.W_gu < 1 || a.W_gu > MOE_WMAX || a.W_dn < 1 || a.W_dn > MOE_WMAX) return QG_EUNSUPPORTED;
+  a.sw_gu = L.sw_gu;
+  if (a.W_gu < 1 || a.W_dn < 1 || a.W_dn > MOE_WMAX || a.W_gu * (a.sw_gu ? a.S_gu : 1) > MOE_WMAX)
+    return QG_EUNSUPPORTED;
   a.nsh = L.nsh;
   if (m->qtype == QG_Q4_0) return launch_moe_q<Q4>(c, a);
   return launch_moe_q<Q8>(c, a);
