@@ -15,10 +15,13 @@
 //     segment): each expert's gate and up tiles are read once for all of its
 //     slots (the unit's activation columns are the routed tokens' x, through
 //     a column map) and h = silu(g) * u is written per slot.
-//  3. down: the same unit over (listed expert, row group) writes z = D h per
-//     slot; the last workgroup to finish a row group forms, per token,
-//     sum_k p_k z_k in rank order, adds the shared expert, and adds the total
-//     to Y once.
+//  3. down, token-major (3'): one workgroup per (token, output row group),
+//     one wave per rank and one for the shared expert, each a 1-column
+//     product of its expert's rows with its slot's h; the waves meet in LDS,
+//     sum_k p_k z_k in rank order plus the shared expert, added to Y once.
+//     For wide experts (h columns too large for LDS) the entry-grouped form:
+//     the dot unit over (listed expert, row group) writes z = D h per slot
+//     and the last workgroup to finish a row group forms the same sum.
 // Workgroups beyond the listed experts exit at once (the grid is the worst
 // case, the list is on the device).
 #include <string.h>
@@ -58,6 +61,7 @@ struct MoeArgs {
   int S_gu, G_gu, G_dn;   // gate/up K segments and row groups (at Fmax rows); down row groups
   int W_gu, W_dn;         // row tiles per gate/up and per down workgroup
   int sw_gu;              // gate/up K segments as waves of one workgroup (summed in LDS)
+  int dn_tok, R_dt, G_dt; // token-major down: on/off, row tiles per wave, row groups
   int nsh;                // shared-expert entries (tokens in groups of the unit width)
   int64_t gpart_per;      // gate/up partial floats per listed expert
 };
@@ -97,7 +101,7 @@ struct MoeLayout {
   int64_t umax;  // work-list entries at most
   size_t rcnt_w, dcnt_w, gcnt_w, sync_words;  // counter word offsets
   int S_gu, G_gu, G_dn, nsh;
-  int W_gu, W_dn, sw_gu;
+  int W_gu, W_dn, sw_gu, dn_tok, R_dt;
   int64_t gpart_per;
 };
 
@@ -117,8 +121,14 @@ static MoeLayout moe_layout(const qg_moe *m, int T) {
   // K, nc columns) plus the segment sums fit comfortably in LDS
   L.sw_gu = L.S_gu > 1 && L.W_gu * L.S_gu <= MOE_WMAX &&
             (size_t)(m->hidden / 128) * TILE_BLOCKS * nc * 64 + (size_t)L.S_gu * L.W_gu * 2 * 4 * 64 * 4 <= 65536;
+  // the token-major down projection (see moe_down_tok_kernel; measured
+  // faster than the entry-grouped one at 1 to 16 tokens) while each wave's
+  // h column fits in LDS; more row tiles per wave as tokens add workgroups
+  L.R_dt = T <= 2 ? 1 : T <= 8 ? 2 : 4;
+  L.dn_tok = (size_t)(m->top_k + 1) * (Fmax * 2 + (size_t)L.R_dt * 64) <= 131072;
 #ifdef MOE_EXP
   if (const char *e = getenv("QG_MOE_SW")) L.sw_gu = L.sw_gu && atoi(e) != 0;
+  if (const char *e = getenv("QG_MOE_DT")) sscanf(e, "%d,%d", &L.dn_tok, &L.R_dt);
 #endif
   L.G_gu = (int)cdiv(Fmax / 16, L.W_gu);
   L.G_dn = (int)cdiv(m->hidden / 16, L.W_dn);
@@ -440,6 +450,114 @@ __global__ void __launch_bounds__(MOE_WMAX * 64) moe_down_kernel(MoeArgs a) {
   }
 }
 
+// ------------------------------------- 3'. down, token-major (few tokens)
+// One workgroup per (token, group of R row tiles of the output), one wave
+// per routed slot of the token plus one for the shared expert.  Each wave
+// stages its slot's h column in LDS (f16) and streams its expert's R row
+// tiles over all of K; the waves' row sums meet in LDS and are combined in
+// rank order, sum_k p_k z_k + shared, then added to Y once.  An expert is
+// read once per token that routed to it (not once for all of them, as in
+// the entry-grouped form), in exchange for no per-slot outputs in memory,
+// no cross-workgroup counters and one launch-wide round trip less.
+template <int QT, int PF>
+__global__ void __launch_bounds__(576) moe_down_tok_kernel(MoeArgs a) {
+  constexpr int TB = QTraits<QT>::tile_bytes;
+  constexpr int QW = QT == Q4 ? 1 : 2;
+  constexpr int RMAX = 4;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nw = a.k + (a.SF > 0 ? 1 : 0);
+  const int t = blockIdx.x / a.G_dt, g = blockIdx.x % a.G_dt;
+  const int R = a.R_dt;
+  const int r = lane & 15, sl = lane >> 4;
+  const bool shared = w == a.k;
+  const int slot = shared ? a.T * a.k + t : t * a.k + w;
+  const int e = shared ? 0 : a.sel[t * a.k + w];
+  const int64_t K = shared ? a.SF : a.F;
+  const int KT = (int)(K / 128);
+  const uint8_t *qs = shared ? a.sdq : a.dq + (int64_t)e * a.dn_qs_stride;
+  const uint8_t *ds = shared ? a.sdd : a.dd + (int64_t)e * a.dn_d_stride;
+
+  // this wave's R row tiles, all of K: one bounded range each for the
+  // weights and the scales (rows past the matrix: an empty range)
+  const int NT = (int)(a.H / 16);
+  const int rt0 = g * R;
+  const int nrt = NT - rt0 < R ? NT - rt0 : R;
+  const __amdgpu_buffer_rsrc_t rq = buf_range(qs + (int64_t)rt0 * KT * TB, (uint32_t)(nrt * KT * TB));
+  const __amdgpu_buffer_rsrc_t rd = buf_range(ds + (int64_t)rt0 * KT * TILE_D_BYTES, (uint32_t)(nrt * KT * TILE_D_BYTES));
+  const int ntile = R * KT;  // tile n: row tile n / KT, tile column n % KT
+  u4 wq[PF][QW];
+  u2 wd[PF];
+  auto load = [&](int slotp, int n) {
+    const uint32_t qo = (uint32_t)n * TB + (uint32_t)lane * 16u;
+    wq[slotp][0] = buf_ld16(rq, qo);
+    if constexpr (QW == 2) wq[slotp][1] = buf_ld16(rq, qo + 1024u);
+    wd[slotp] = buf_ld8(rd, (uint32_t)n * TILE_D_BYTES + (uint32_t)r * 8u);
+  };
+#pragma unroll
+  for (int p = 0; p < PF; ++p) load(p, p);
+
+  // h column of this slot, f16 in LDS, [block][32]
+  _Float16 *xs = (_Float16 *)smem + (size_t)w * a.Fmax;
+  const float *hcol = a.hbuf + (int64_t)slot * a.Fmax;
+  for (int v = lane; v < (int)(K / 8); v += 64) {
+    const float4 lo = *(const float4 *)(hcol + v * 8), hi = *(const float4 *)(hcol + v * 8 + 4);
+    *(h8 *)(xs + v * 8) = cvt8(lo, hi);
+  }
+  __syncthreads();
+
+  const Q4Magic mg = q4_magic();
+  float acc[RMAX];
+#pragma unroll
+  for (int i = 0; i < RMAX; ++i) acc[i] = 0.0f;
+  for (int n0 = 0; n0 < ntile; n0 += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const int n = n0 + p;
+      if (n < ntile) {
+        const int i = n / KT, kt = n % KT;
+        float part = 0.0f;
+#pragma unroll
+        for (int j = 0; j < TILE_BLOCKS; ++j) {
+          h2 wv[4];
+          if constexpr (QT == Q4) unpack_q4(wq[p][0][j], wv, mg);
+          else unpack_q8(wq[p][j >> 1][(j & 1) * 2], wq[p][j >> 1][(j & 1) * 2 + 1], wv);
+          const h8 xx = *(const h8 *)(xs + (kt * TILE_BLOCKS + j) * 32 + sl * 8);
+          float q = dot2_first(wv[0], lo_pair(xx, 0));
+          q = __builtin_amdgcn_fdot2(wv[1], lo_pair(xx, 1), q, false);
+          q = __builtin_amdgcn_fdot2(wv[2], lo_pair(xx, 2), q, false);
+          q = __builtin_amdgcn_fdot2(wv[3], lo_pair(xx, 3), q, false);
+          part = __builtin_fmaf(scale_of(wd[p], j), q, part);
+        }
+#pragma unroll
+        for (int ii = 0; ii < RMAX; ++ii)
+          if (ii == i) acc[ii] += part;
+      }
+      load(p, n + PF);
+    }
+  }
+
+  // row sums (the 4 slices of each row), then the combine through LDS
+  float *zs = (float *)(smem + (size_t)nw * a.Fmax * 2);  // [wave][R * 16]
+#pragma unroll
+  for (int i = 0; i < RMAX; ++i) {
+    float v = acc[i];
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    if (i < R && sl == 0) zs[w * R * 16 + i * 16 + r] = v;
+  }
+  __syncthreads();
+  if (tid < nrt * 16) {
+    const int64_t row = (int64_t)rt0 * 16 + tid;
+    float sum = 0.0f;
+    for (int kk = 0; kk < a.k; ++kk) sum = __builtin_fmaf(a.pw[t * a.k + kk], zs[kk * R * 16 + tid], sum);
+    if (a.SF > 0) sum += zs[a.k * R * 16 + tid];
+    float *yp = a.Y + (int64_t)t * a.ldy + row;
+    *yp = *yp + sum;
+  }
+}
+
 // ------------------------------------------------------------ host side
 static int grant(const void *kern, size_t lds, size_t &granted) {
   if (lds > 163840 - 1024) return QG_EUNSUPPORTED;
@@ -490,6 +608,16 @@ static int launch_moe_t(const MoeCall &c, MoeArgs &a) {
                      c.stream, a);
   if (launch_status() != QG_OK) return QG_EHIP;
 
+  if (a.dn_tok) {
+    auto kt = moe_down_tok_kernel<QT, PFD>;
+    const int nw = a.k + (a.SF > 0 ? 1 : 0);
+    const size_t lds_t = (size_t)nw * a.Fmax * 2 + (size_t)nw * a.R_dt * 16 * 4;
+    static size_t granted_t = 65536;
+    if ((st = grant((const void *)kt, lds_t, granted_t))) return st;
+    clear_hip_error();
+    hipLaunchKernelGGL(kt, dim3((unsigned)(a.T * a.G_dt)), dim3(nw * 64), lds_t, c.stream, a);
+    return launch_status();
+  }
   auto kd = moe_down_kernel<QT, NC, PFD>;
   const size_t lds_d = unit_lds<NC, PFD>(a.Fmax / 128, 1);
   static size_t granted_d = 65536;
@@ -565,6 +693,10 @@ int launch_moe(const MoeCall &c) {
   a.W_gu = L.W_gu;
   a.W_dn = L.W_dn;
   a.sw_gu = L.sw_gu;
+  a.dn_tok = L.dn_tok;
+  a.R_dt = L.R_dt;
+  a.G_dt = (int)cdiv(a.H / 16, L.R_dt);
+  if (a.R_dt < 1 || a.R_dt > 4) return QG_EUNSUPPORTED;
   if (a.W_gu < 1 || a.W_dn < 1 || a.W_dn > MOE_WMAX || a.W_gu * (a.sw_gu ? a.S_gu : 1) > MOE_WMAX)
     return QG_EUNSUPPORTED;
   a.nsh = L.nsh;

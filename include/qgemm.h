@@ -223,7 +223,10 @@ int lmhead_argmax(int qtype, const void *qs, const void *d, int64_t rows, int64_
  * then the total is added to Y once.  Gate and up stacks: qg_repack with
  * n_mat = n_expert, rows = ffn, cols = hidden; down stack: n_mat = n_expert,
  * rows = hidden, cols = ffn; the shared matrices: n_mat = 1, ffn -> sh_ffn.
- * Each selected expert's weights are read once for all tokens routed to it.
+ * The gate and up matrices of each selected expert are read once for all
+ * tokens routed to it (up to 4 tokens per pass); the down matrices once per
+ * (token, rank) when ffn is at most a few thousand (the combine then runs
+ * in on-chip memory), else once for all tokens routed to the expert.
  * topk_idx / topk_w (ntok x top_k, row-major, may be NULL) receive sel and p.
  * Limits: ntok 1..16 per call, top_k 1..8, n_expert 1..1024,
  * hidden and ffn multiples of 128 and at most 16384.

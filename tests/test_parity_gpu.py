@@ -326,6 +326,14 @@ def test_moe_small(env, T, shared):
     _moe_check(env, m, hw, T, 4, cfg=70 + T)
 
 
+def test_moe_wide_experts(env):
+    # experts too wide for the token-major down projection's on-chip h
+    # columns: the entry-grouped down path and its cross-workgroup combine
+    say("moe wide experts (ffn 11008)")
+    m, hw = _moe_build(env, E=6, H=128, F=11008, k=5, seed=85)
+    _moe_check(env, m, hw, 3, 5, cfg=86)
+
+
 def test_moe_unnormalized(env):
     m, hw = _moe_build(env, E=12, H=256, F=128, k=3, seed=80, normalize=False)
     _moe_check(env, m, hw, 5, 3, cfg=81, normalize=False)
