@@ -62,6 +62,7 @@ struct MoeArgs {
   int W_gu, W_dn;         // row tiles per gate/up and per down workgroup
   int sw_gu;              // gate/up K segments as waves of one workgroup (summed in LDS)
   int dn_tok, R_dt, G_dt; // token-major down: on/off, row tiles per wave, row groups
+  int sel_local;          // one token: each gate/up workgroup selects the experts itself
   int nsh;                // shared-expert entries (tokens in groups of the unit width)
   int64_t gpart_per;      // gate/up partial floats per listed expert
 };
@@ -157,6 +158,58 @@ static MoeLayout moe_layout(const qg_moe *m, int T) {
 
 size_t moe_ws_bytes(const qg_moe *m, int ntok) { return moe_layout(m, ntok).total; }
 
+// One token's selection, by one wave: the token's logits in registers (NJ
+// per lane, n_expert <= 64 NJ), k rounds of a wave maximum over each lane's
+// best remaining key (after which only the lane that owned the winner looks
+// at its keys again), then the softmax weights.  Lane kk < k receives the
+// expert of rank kk and its weight.
+template <int NJ>
+__device__ __forceinline__ void select_token(const MoeArgs &a, int t, int lane, int32_t &out_e, float &out_p) {
+  float lv[NJ];
+  uint64_t key[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int ee = lane + 64 * j;
+    lv[j] = ee < a.E ? ld_agent(a.logits + (int64_t)t * a.E + ee) : 0.0f;
+    key[j] = ee < a.E ? rank_key(lv[j], ee) : 0;
+  }
+  uint64_t loc = 0;  // this lane's best remaining key
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) loc = key[j] > loc ? key[j] : loc;
+  float mx = 0.0f, sumsel = 0.0f, my_ex = 0.0f;
+  int32_t my_e = 0;  // lane kk: the expert of rank kk
+  for (int kk = 0; kk < a.k; ++kk) {
+    const uint64_t w = wave_max_u64(loc);
+    const int32_t bi = rank_key_index(w);
+    const float bv = rank_key_value(w);
+    if (kk == 0) mx = bv;  // the largest logit
+    const float ex = expf(bv - mx);
+    sumsel += ex;
+    if (lane == kk) {
+      my_e = bi;
+      my_ex = ex;
+    }
+    if (loc == w) {  // the owner: drop the winner, find its next best
+      loc = 0;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        if (key[j] == w) key[j] = 0;
+        loc = key[j] > loc ? key[j] : loc;
+      }
+    }
+  }
+  float sum = sumsel;
+  if (!a.norm) {
+    float part = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      if (lane + 64 * j < a.E) part += expf(lv[j] - mx);
+    sum = wave_sum(part);
+  }
+  out_e = my_e;
+  out_p = my_ex / sum;
+}
+
 // ------------------------------------------------------------ 1. router
 // P waves per (expert, token) pair (P parts of the hidden range, P larger
 // when there are few pairs, so that the router matrix is read by many CUs),
@@ -213,60 +266,22 @@ __global__ void __launch_bounds__(RW * 64) moe_router_kernel(MoeArgs a) {
       }
     }
   }
+  // one token: the gate/up workgroups select (no work list needed)
+  if (a.sel_local) return;
   if (!arrive_last(a.rcnt, gridDim.x, &flag)) return;
 
   // ---- top-k and softmax weights, one wave per token
   if (wk < a.T) {
-    const int t = wk;
-    float lv[NJ];
-    uint64_t key[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int ee = lane + 64 * j;
-      lv[j] = ee < a.E ? ld_agent(a.logits + (int64_t)t * a.E + ee) : 0.0f;
-      key[j] = ee < a.E ? rank_key(lv[j], ee) : 0;
-    }
-    uint64_t loc = 0;  // this lane's best remaining key
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) loc = key[j] > loc ? key[j] : loc;
-    float mx = 0.0f, sumsel = 0.0f, my_ex = 0.0f;
-    int32_t my_e = 0;  // lane kk: the expert of rank kk
-    for (int kk = 0; kk < a.k; ++kk) {
-      const uint64_t w = wave_max_u64(loc);
-      const int32_t bi = rank_key_index(w);
-      const float bv = rank_key_value(w);
-      if (kk == 0) mx = bv;  // the largest logit
-      const float ex = expf(bv - mx);
-      sumsel += ex;
-      if (lane == kk) {
-        my_e = bi;
-        my_ex = ex;
-      }
-      if (loc == w) {  // the owner: drop the winner, find its next best
-        loc = 0;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          if (key[j] == w) key[j] = 0;
-          loc = key[j] > loc ? key[j] : loc;
-        }
-      }
-    }
-    float sum = sumsel;
-    if (!a.norm) {
-      float part = 0.0f;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        if (lane + 64 * j < a.E) part += expf(lv[j] - mx);
-      sum = wave_sum(part);
-    }
+    int32_t my_e;
+    float my_p;
+    select_token<NJ>(a, wk, lane, my_e, my_p);
     if (lane < a.k) {
-      const int kk = lane;
-      const float p = my_ex / sum;
+      const int kk = lane, t = wk;
       s_sel[t * a.k + kk] = my_e;
       a.sel[t * a.k + kk] = my_e;
-      a.pw[t * a.k + kk] = p;
+      a.pw[t * a.k + kk] = my_p;
       if (a.topk_idx) a.topk_idx[t * a.k + kk] = my_e;
-      if (a.topk_w) a.topk_w[t * a.k + kk] = p;
+      if (a.topk_w) a.topk_w[t * a.k + kk] = my_p;
     }
   }
   __syncthreads();
@@ -321,9 +336,10 @@ __global__ void __launch_bounds__(RW * 64) moe_router_kernel(MoeArgs a) {
 // maps (activation column -> token or slot, output column -> slot).
 // Returns the column count, 0 when the unit has no entry.
 template <bool GATEUP, int NC>
-__device__ __forceinline__ int moe_expert(const MoeArgs &a, int u, DotArgs &d, int32_t *s_x, int32_t *s_y) {
+__device__ __forceinline__ int moe_expert(const MoeArgs &a, int u, DotArgs &d, int32_t *s_x, int32_t *s_y,
+                                          const int32_t *loc_e = nullptr, const int32_t *loc_slot = nullptr) {
   const int tid = threadIdx.x;
-  const int nused = (int)*a.nused;
+  const int nused = loc_e ? a.k : (int)*a.nused;
   const int nsh = a.SF > 0 ? (a.T + NC - 1) / NC : 0;
   if (u >= nused + nsh) return 0;
   const bool shared = u >= nused;
@@ -341,10 +357,12 @@ __device__ __forceinline__ int moe_expert(const MoeArgs &a, int u, DotArgs &d, i
       d.qs0 = d.qs1 = a.sdq; d.d0 = d.d1 = a.sdd;
     }
   } else {
-    const int e = a.used_e[u];
-    nc = a.used_cnt[u];
+    // the work-list entry, or (one token, selected locally) the expert of
+    // index-order position u and its slot
+    const int e = loc_e ? loc_e[u] : a.used_e[u];
+    nc = loc_e ? 1 : a.used_cnt[u];
     if (tid < nc) {
-      const int q = a.used_slot[u * TMAX + tid];
+      const int q = loc_e ? loc_slot[u] : a.used_slot[u * TMAX + tid];
       s_x[tid] = GATEUP ? q / a.k : q;
       s_y[tid] = q;
     }
@@ -372,11 +390,37 @@ __global__ void __launch_bounds__(MOE_WMAX * 64) moe_gateup_kernel(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ uint32_t flag;
   __shared__ int32_t s_x[TMAX], s_y[TMAX];
+  __shared__ int32_t s_le[8], s_ls[8];
   const int sx = a.sw_gu ? 1 : a.S_gu;  // segments across workgroups
   const int per = a.G_gu * sx;
   const int u = blockIdx.x / per, g = (blockIdx.x % per) / sx, s = blockIdx.x % sx;
+  if (a.sel_local) {
+    // one token: wave 0 selects the experts (the same bits in every
+    // workgroup) and lists them in expert index order; workgroup 0 also
+    // publishes the selection and the weights
+    const int tid = threadIdx.x;
+    if (tid < 64) {
+      int32_t my_e;
+      float my_p;
+      if (a.E <= 256) select_token<4>(a, 0, tid, my_e, my_p);
+      else select_token<16>(a, 0, tid, my_e, my_p);
+      int pos = 0;
+      for (int j = 0; j < a.k; ++j) pos += __shfl(my_e, j) < my_e ? 1 : 0;
+      if (tid < a.k) {
+        s_le[pos] = my_e;
+        s_ls[pos] = tid;
+        if (blockIdx.x == 0) {
+          a.sel[tid] = my_e;
+          a.pw[tid] = my_p;
+          if (a.topk_idx) a.topk_idx[tid] = my_e;
+          if (a.topk_w) a.topk_w[tid] = my_p;
+        }
+      }
+    }
+    __syncthreads();
+  }
   DotArgs d = {};
-  if (!moe_expert<true, NC>(a, u, d, s_x, s_y)) return;
+  if (!moe_expert<true, NC>(a, u, d, s_x, s_y, a.sel_local ? s_le : nullptr, s_ls)) return;
   d.S = sx;
   d.SW = a.sw_gu ? a.S_gu : 1;
   d.G = (int)cdiv(d.NT, a.W_gu);
@@ -694,6 +738,10 @@ int launch_moe(const MoeCall &c) {
   a.W_dn = L.W_dn;
   a.sw_gu = L.sw_gu;
   a.dn_tok = L.dn_tok;
+  a.sel_local = c.ntok == 1 && L.dn_tok;
+#ifdef MOE_EXP
+  if (const char *e = getenv("QG_MOE_SL")) a.sel_local = a.sel_local && atoi(e) != 0;
+#endif
   a.R_dt = L.R_dt;
   a.G_dt = (int)cdiv(a.H / 16, L.R_dt);
   if (a.R_dt < 1 || a.R_dt > 4) return QG_EUNSUPPORTED;
