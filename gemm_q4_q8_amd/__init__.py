@@ -74,6 +74,7 @@ _SIGS = {
     "qg_moe_ws_bytes": (_sz, [ctypes.POINTER(qg_moe), _i32]),
     "moe_ffn": (ctypes.c_int, [ctypes.POINTER(qg_moe), _vp, _i64, _i32, _vp, _i64, _vp, _vp,
                                _vp, _sz, _vp]),
+    "qg_read_probe": (ctypes.c_int, [_vp, _sz, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -257,6 +258,18 @@ def ffn_wait_error(device=None) -> int:
     torch = _torch()
     ws = _WS.get((torch.device(device or "cuda:0").index or 0, "ffn"))
     return 0 if ws is None else int(ws[8:12].view(torch.int32).item())
+
+
+def read_probe(t, sink=None):
+    """Measurement aid: read every byte of device tensor `t` once (the
+    bench's streaming-read ceiling).  Returns the sink tensor."""
+    torch = _torch()
+    _check_dev(t)
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=t.device)
+    _check(lib.qg_read_probe(t.data_ptr(), t.numel() * t.element_size(), sink.data_ptr(),
+                             _stream(t.device)), "qg_read_probe")
+    return sink
 
 
 def lmhead_argmax(w: QMatrix, x, n_rows: Optional[int] = None, out_idx=None, out_val=None):

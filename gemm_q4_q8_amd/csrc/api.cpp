@@ -321,6 +321,13 @@ size_t qg_moe_ws_bytes(const qg_moe *m, int32_t ntok) {
   return moe_ws_bytes(m, ntok);
 }
 
+int qg_read_probe(const void *p, size_t bytes, uint32_t *sink, void *stream) {
+  if (!p || !sink) return QG_EINVAL;
+  if (bytes == 0 || bytes % 16) return QG_ESHAPE;
+  if (!aligned(p, 16) || !aligned(sink, 4)) return QG_EALIGN;
+  return launch_read_probe(p, bytes, sink, stream);
+}
+
 int moe_ffn(const qg_moe *m, const float *X, int64_t ldx, int32_t ntok, float *Y, int64_t ldy,
             int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes, void *stream) {
   int st = check_moe(m, ntok);

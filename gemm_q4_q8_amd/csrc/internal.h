@@ -68,6 +68,9 @@ struct FfnCall {
 size_t ffn_ws_bytes(int64_t hidden, int64_t ffn);
 int launch_ffn(const FfnCall &c);
 
+// Streaming-read probe (the bench's measured read ceiling).
+int launch_read_probe(const void *p, size_t bytes, uint32_t *sink, void *stream);
+
 struct MoeCall {
   const qg_moe *m;
   const float *X;

@@ -83,6 +83,16 @@ const char *qg_strerror(int status);
  * thread (thread-local storage, valid until the next failing call). */
 const char *qg_last_hip_error(void);
 
+/* Measurement aid, not part of the product path  [ARCH: the pages time a
+ * plain copy at load and quote their GEMV against the streaming limit they
+ * measure]: reads every byte of [p, p + bytes) once, as the product kernels
+ * stream weights (nontemporal 16-byte loads, one contiguous run per wave),
+ * and computes nothing from it, so its rate is a measured read ceiling.
+ * p: device pointer, 16-byte aligned; bytes: a multiple of 16, > 0; sink: a
+ * device uint32 the kernel may write (almost never does).  Asynchronous on
+ * `stream`.  Errors: QG_EINVAL (null), QG_EALIGN, QG_ESHAPE, QG_EHIP. */
+int qg_read_probe(const void *p, size_t bytes, uint32_t *sink, void *stream);
+
 /* ------------------------------------------------------------------------
  * Load-time repack  [ARCH Memory and caching; ENG Reading weights]
  *

@@ -190,3 +190,12 @@ def test_moe_checks():
     assert call(_moe(router=FAKE + 4)) == EALIGN
     assert call(_moe(sh_ffn=128)) == EINVAL          # shared expert pointers missing
     assert call(_moe(), wsb=8) == EWS
+
+
+def test_read_probe_checks():
+    sink = ctypes.c_void_p(256)
+    assert L.qg_read_probe(None, 1024, sink, None) == EINVAL
+    assert L.qg_read_probe(ctypes.c_void_p(4096), 1024, None, None) == EINVAL
+    assert L.qg_read_probe(ctypes.c_void_p(4096), 0, sink, None) == ESHAPE
+    assert L.qg_read_probe(ctypes.c_void_p(4096), 1000, sink, None) == ESHAPE
+    assert L.qg_read_probe(ctypes.c_void_p(4104), 1024, sink, None) == EALIGN
