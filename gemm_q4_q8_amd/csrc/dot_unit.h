@@ -55,6 +55,9 @@ struct DotArgs {
   int S;              // K segments across workgroups
   int SW;             // K segments inside one workgroup (<= 1: none): wave wk
                       // streams segment wk / R of row tile wk % R, R = waves / SW
+  int IL;             // interleaved segments: segment q of n holds tile columns
+                      // q, q + n, q + 2n, ... (every unit stages all of K);
+                      // otherwise contiguous ranges
   int G;              // row groups of R * RT row tiles
   int64_t units;      // G * S workgroups
   int64_t per_xcd;
@@ -140,14 +143,20 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   const int tid = threadIdx.x, lane = tid & 63;
   const int wk = __builtin_amdgcn_readfirstlane(tid >> 6);
   // the workgroup's K range (staged in LDS), and inside it this wave's
-  // stream: all of it, or (SW > 1) in-workgroup segment wsg of SW
+  // stream: all of it, or (SW > 1) in-workgroup segment wsg of SW.
+  // Interleaved segments: the workgroup stages all of K and the wave's
+  // segment q of nq takes tile columns q, q + nq, ... (wst = nq);
+  // contiguous ones: its range [wkt0, wkt0 + wnkt) of the staged columns.
   const int SW = (!XS && a.SW > 1) ? a.SW : 1;
   const int R = (NTHR >> 6) / SW;
   const int wrt = wk % R, wsg = wk / R;
-  const int kt0 = seg_begin(s, a.KT, a.S);
-  const int nkt = seg_begin(s + 1, a.KT, a.S) - kt0;
-  const int wkt0 = seg_begin(wsg, nkt, SW);         // relative to kt0
-  const int wnkt = seg_begin(wsg + 1, nkt, SW) - wkt0;
+  const bool IL = !XS && a.IL;
+  const int kt0 = IL ? 0 : seg_begin(s, a.KT, a.S);
+  const int nkt = IL ? a.KT : seg_begin(s + 1, a.KT, a.S) - kt0;
+  const int wq_i = SW > 1 ? wsg : s, wq_n = SW > 1 ? SW : a.S;  // this wave's segment of how many
+  const int wkt0 = IL ? wq_i : seg_begin(wsg, nkt, SW);        // first tile column, relative to kt0
+  const int wst = IL ? wq_n : 1;                               // step between its tile columns
+  const int wnkt = IL ? (nkt - wq_i + wq_n - 1) / wq_n : seg_begin(wsg + 1, nkt, SW) - wkt0;
   const int64_t rt_base = ((int64_t)g * R + wrt) * RT;
   const int r = lane & 15, sl = lane >> 4;
   _Float16 *xs = (_Float16 *)smem;
@@ -188,14 +197,19 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const bool in = rt_base + t < a.NT;
+      // the range starts at the wave's first tile column and spans its
+      // last one (interleaved: the tiles between belong to other waves)
       const int64_t tile = (in ? rt_base + t : 0) * a.KT + kt0 + wkt0;
-      rq[m][t] = buf_range((m ? a.qs1 : a.qs0) + tile * TB, in ? (uint32_t)wnkt * TB : 0u);
-      rd[m][t] = buf_range((m ? a.d1 : a.d0) + tile * TILE_D_BYTES, in ? (uint32_t)wnkt * TILE_D_BYTES : 0u);
+      const uint32_t span = wnkt > 0 ? (uint32_t)((wnkt - 1) * wst + 1) : 0u;
+      rq[m][t] = buf_range((m ? a.qs1 : a.qs0) + tile * TB, in ? span * TB : 0u);
+      rd[m][t] = buf_range((m ? a.d1 : a.d0) + tile * TILE_D_BYTES, in ? span * TILE_D_BYTES : 0u);
     }
   u4 wq[PF][NMAT][RT][QW];
   u2 wd[PF][NMAT][RT];
   const uint32_t lane_off = (uint32_t)lane * 16u, d_off = (uint32_t)r * 8u;
-  auto load = [&](int slot, int rel) {  // rel: tile column within the segment
+  auto load = [&](int slot, int rel_) {  // rel_: the wave's rel_-th tile column
+    // past the wave's last tile column: an offset beyond every range
+    const int rel = rel_ < wnkt ? rel_ * wst : 0x7FFF;
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -274,7 +288,7 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
     // block index in LDS: the staged range's own (this wave's stream starts
     // wkt0 tile columns in), or, streaming, the slot of tile column rel in
     // its chunk's buffer
-    const int bl0 = XS ? ((((rel / PF) & 1) * PF) + rel % PF) * TILE_BLOCKS : (wkt0 + rel) * TILE_BLOCKS;
+    const int bl0 = XS ? ((((rel / PF) & 1) * PF) + rel % PF) * TILE_BLOCKS : (wkt0 + rel * wst) * TILE_BLOCKS;
     if constexpr (MF) {
       // per block: D (16 columns x 16 rows) = X_blk^T W_blk^T on the matrix
       // cores from the exact f16 weights, then each lane's 4 D values get

@@ -119,6 +119,7 @@ static DotArgs phase_args(const void *qs0, const void *d0, const void *qs1, cons
   a.NT = (int)cdiv(rows, 16);
   a.KT = (int)cdiv(cols / 32, 4);
   a.S = S;
+  a.IL = dot_interleaved(cols) ? 1 : 0;  // as the separate calls
   a.G = (int)cdiv(a.NT, FFN_WKT);
   a.units = (int64_t)a.G * S;
   a.X = X;
@@ -161,8 +162,8 @@ static int launch_ffn_t(const FfnCall &c) {
   f.NA = (int)f.A.units;
   f.NB = (int)f.B.units;
 
-  const size_t lds_a = (size_t)cdiv(KTA, L.SA) * TILE_BLOCKS * 64;
-  const size_t lds_b = (size_t)cdiv(KTB, L.SB) * TILE_BLOCKS * 64;
+  const size_t lds_a = (size_t)(f.A.IL ? KTA : cdiv(KTA, L.SA)) * TILE_BLOCKS * 64;
+  const size_t lds_b = (size_t)(f.B.IL ? KTB : cdiv(KTB, L.SB)) * TILE_BLOCKS * 64;
   const size_t lds = lds_a > lds_b ? lds_a : lds_b;
   if (lds > 65536) return QG_EUNSUPPORTED;
   auto kern = ffn_kernel<QT, PFA, PFB>;

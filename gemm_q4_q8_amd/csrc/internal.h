@@ -38,6 +38,8 @@ struct QmvCall {
 int gemv_segments(int64_t rows, int64_t cols, int nmat, int ncols_max);
 // Compute units of the current device (queried once per device).
 int device_cus();
+// Interleaved K segments for a matrix of `cols` inputs (1..8 columns).
+bool dot_interleaved(int64_t cols);
 // K splits of the 16-column matrix-core path.
 int gemm16_splits(int64_t rows, int64_t cols);
 

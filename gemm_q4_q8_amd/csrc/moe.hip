@@ -63,6 +63,7 @@ struct MoeArgs {
   int sw_gu;              // gate/up K segments as waves of one workgroup (summed in LDS)
   int dn_tok, R_dt, G_dt; // token-major down: on/off, row tiles per wave, row groups
   int sel_local;          // one token: each gate/up workgroup selects the experts itself
+  int il_gu;              // gate/up: interleaved K segments
   int nsh;                // shared-expert entries (tokens in groups of the unit width)
   int64_t gpart_per;      // gate/up partial floats per listed expert
 };
@@ -423,6 +424,7 @@ __global__ void __launch_bounds__(MOE_WMAX * 64) moe_gateup_kernel(MoeArgs a) {
   if (!moe_expert<true, NC>(a, u, d, s_x, s_y, a.sel_local ? s_le : nullptr, s_ls)) return;
   d.S = sx;
   d.SW = a.sw_gu ? a.S_gu : 1;
+  d.IL = a.il_gu;
   d.G = (int)cdiv(d.NT, a.W_gu);
   if (g >= d.G) return;
   d.X = a.X;
@@ -638,9 +640,10 @@ static int launch_moe_t(const MoeCall &c, MoeArgs &a) {
   if (launch_status() != QG_OK) return QG_EHIP;
 
   auto kg = moe_gateup_kernel<QT, NC, PFG>;
-  // in-workgroup segments: all of K staged, plus the segment sums
-  const size_t lds_g = a.sw_gu ? unit_lds<NC, PFG>(a.H / 128, 1) + (size_t)(a.S_gu - 1) * a.W_gu * 2 *
-                                                                      (NC < 4 ? NC : 4) * 64 * 4
+  // in-workgroup or interleaved segments: all of K staged (plus, in the
+  // workgroup, the segment sums)
+  const size_t lds_g = (a.sw_gu || a.il_gu) ? unit_lds<NC, PFG>(a.H / 128, 1) + (a.sw_gu ? (size_t)(a.S_gu - 1) * a.W_gu * 2 *
+                                                                      (NC < 4 ? NC : 4) * 64 * 4 : 0)
                                : unit_lds<NC, PFG>(a.H / 128, a.S_gu);
   const int sx = a.sw_gu ? 1 : a.S_gu;
   const int wg_threads = a.W_gu * (a.sw_gu ? a.S_gu : 1) * 64;
@@ -739,6 +742,7 @@ int launch_moe(const MoeCall &c) {
   a.sw_gu = L.sw_gu;
   a.dn_tok = L.dn_tok;
   a.sel_local = c.ntok == 1 && L.dn_tok;
+  a.il_gu = dot_interleaved(a.H) ? 1 : 0;
 #ifdef MOE_EXP
   if (const char *e = getenv("QG_MOE_SL")) a.sel_local = a.sel_local && atoi(e) != 0;
 #endif

@@ -121,7 +121,19 @@ int device_cus() {
 constexpr int DOT_STREAMS = 2048;     // (row tile, segment, matrix) weight streams
 constexpr size_t DOT_X_LDS = 65536;   // staged activations per workgroup
 constexpr size_t LDS_HARD = 163840;   // gfx950 LDS per workgroup
-constexpr size_t DOT_SW_LDS = 98304;  // in-workgroup segments: activations + sums
+constexpr size_t DOT_SW_LDS = 131072;  // in-workgroup segments: activations + sums
+constexpr size_t DOT_IL_LDS = 81920;   // interleaved segments: all of K for 8 columns
+
+// Interleaved K segments (segment q of n: tile columns q, q + n, ...) when
+// every unit can stage all of K for up to 8 columns; a function of the
+// shape only, so every column count of a shape sums in the same order.
+// Measured (K = 5120 and 2048): the waves of a workgroup then stream
+// neighbouring tiles and finish together (gate/up 21.7 -> 20.3 us, verify
+// Q4_0 4 columns 15.5 -> 15.1 us).
+bool dot_interleaved(int64_t cols) {
+  const int64_t KT = cdiv(cols / 32, 4);
+  return (size_t)KT * TILE_BLOCKS * 8 * 64 <= DOT_IL_LDS;
+}
 
 // K segments of the dot path: about DOT_STREAMS weight streams of one row
 // tile and one segment each (measured on the decode shapes: more streams,
@@ -207,6 +219,7 @@ static int launch_dot_t(const QmvCall &c, int S, int W = WKT, int SW = 1) {
   a.KT = (int)KT;
   a.S = S;
   a.SW = SW;
+  a.IL = NC < 16 && dot_interleaved(c.cols) ? 1 : 0;
   if (W < 1 || W > WMAX || (WKT > 0 && W != WKT)) return QG_EUNSUPPORTED;
   if (NC >= 16 && WKT == 0 && W < DOT_XS_WMIN) return QG_EUNSUPPORTED;
   if (SW < 1 || (SW > 1 && (S != 1 || NC >= 16 || W % SW != 0))) return QG_EUNSUPPORTED;
@@ -248,7 +261,8 @@ static int launch_dot_t(const QmvCall &c, int S, int W = WKT, int SW = 1) {
   // staged activations: the whole segment, or (16 columns) two chunks of
   // PF tile columns
   // PF tile columns (+ the in-workgroup segment sums)
-  size_t lds = NC >= 16 ? (size_t)2 * PF * TILE_BLOCKS * NC * 64 : (size_t)cdiv(KT, S) * TILE_BLOCKS * NC * 64;
+  size_t lds = NC >= 16 ? (size_t)2 * PF * TILE_BLOCKS * NC * 64
+                        : (size_t)(a.IL ? KT : cdiv(KT, S)) * TILE_BLOCKS * NC * 64;
   lds += (size_t)(SW - 1) * (W / SW) * NMAT * RT * (MF ? (NC < 4 ? NC : 4) : NC) * 64 * 4;
   if (lds > LDS_HARD - 1024) return QG_EUNSUPPORTED;
   auto kern = dot_kernel<QT, NC, NMAT, EPI, RT, PF, WKT, MF, WMAX>;
@@ -291,11 +305,12 @@ static int launch_dot(const QmvCall &c, int S) {
     // on the decode shapes), same segments and order, so the same bits as
     // across workgroups.  Possible when a workgroup of R row tiles x S
     // segments (at most 16 waves) leaves one workgroup per CU and the whole
-    // K range of activations fits in LDS; chosen when it keeps at least 90%
-    // of the CUs the split across workgroups would use, or when each CU's
-    // share of the weights is small (<= 192 KiB: the tail is then a large
-    // part of the time).  Measured: faster for verify at 4 / 8 columns and
-    // small GEMVs, slower for the decode gate/up and down projections.
+    // K range of activations fits in LDS; chosen with interleaved segments
+    // (measured faster on every such shape), or with contiguous ones when
+    // it keeps at least 90% of the CUs the split across workgroups would
+    // use or each CU's share of the weights is small (<= 192 KiB: the tail
+    // is then a large part of the time); the decode down projection stays
+    // across workgroups (its waves would finish far apart).
     const int64_t ncu = device_cus();
     const int64_t R = cdiv(NTu, ncu);
     const int64_t KT = cdiv(c.cols / 32, 4);
@@ -303,7 +318,8 @@ static int launch_dot(const QmvCall &c, int S) {
     const size_t lds = (size_t)KT * TILE_BLOCKS * NC * 64 + (size_t)(S - 1) * R * NMAT * NI * 64 * 4;
     const int64_t u_sw = cdiv(NTu, R), u_cross = cdiv(NTu, (int64_t)W) * S;
     const int64_t cu_bytes = (int64_t)NMAT * R * KT * (QTraits<QT>::tile_bytes + TILE_D_BYTES);
-    bool sw = R * S <= 16 && lds <= DOT_SW_LDS && (10 * u_sw >= 9 * u_cross || cu_bytes <= 196608);
+    bool sw = R * S <= 16 && lds <= DOT_SW_LDS &&
+              (dot_interleaved(c.cols) || 10 * u_sw >= 9 * u_cross || cu_bytes <= 196608);
 #ifdef DOT_EXP
     if (getenv("QG_NO_SW")) sw = false;
     if (getenv("QG_FORCE_SW")) sw = R * S <= 16 && lds <= DOT_SW_LDS;
