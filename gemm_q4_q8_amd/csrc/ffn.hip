@@ -22,9 +22,6 @@
 // wait, so every wait ends.  (A bounded wait still guards the kernel: should
 // one ever time out, it sets the error word and the kernel ends.)
 #include <string.h>
-#ifdef FFN_EXP
-#include <stdlib.h>
-#endif
 
 #include "common.h"
 #include "dot_unit.h"
@@ -187,9 +184,6 @@ static int launch_ffn_t(const FfnCall &c) {
     }
     if (per_cu < 1 || ncu < 1) return QG_EUNSUPPORTED;
     resident[dev] = per_cu * ncu;
-#ifdef FFN_EXP
-    if (const char *e = getenv("QG_FFN_PERCU")) resident[dev] = (atoi(e) < per_cu ? atoi(e) : per_cu) * ncu;
-#endif
     resident_lds[dev] = lds;
   }
   const int grid = f.NA < resident[dev] ? f.NA : resident[dev];

@@ -25,10 +25,6 @@
 // Workgroups beyond the listed experts exit at once (the grid is the worst
 // case, the list is on the device).
 #include <string.h>
-#ifdef MOE_EXP
-#include <stdio.h>
-#include <stdlib.h>
-#endif
 
 #include "common.h"
 #include "dot_unit.h"
@@ -80,9 +76,6 @@ static int moe_nc(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : 4; }
 static int moe_s_gu(int64_t H, int T) {
   const int64_t KT = H / 128;
   int64_t s = T <= 2 ? KT / 4 : 1;
-#ifdef MOE_EXP
-  if (const char *e = getenv("QG_MOE_S")) s = atoi(e);
-#endif
   return (int)(s < 1 ? 1 : s);
 }
 
@@ -93,9 +86,6 @@ static void moe_waves(int T, int &w_gu, int &w_dn) {
   // the experts (fewer, longer units)
   w_gu = T <= 2 ? 2 : 8;
   w_dn = 8;
-#ifdef MOE_EXP
-  if (const char *e = getenv("QG_MOE_W")) sscanf(e, "%d,%d", &w_gu, &w_dn);
-#endif
 }
 
 struct MoeLayout {
@@ -128,10 +118,6 @@ static MoeLayout moe_layout(const qg_moe *m, int T) {
   // h column fits in LDS; more row tiles per wave as tokens add workgroups
   L.R_dt = T <= 2 ? 1 : T <= 8 ? 2 : 4;
   L.dn_tok = (size_t)(m->top_k + 1) * (Fmax * 2 + (size_t)L.R_dt * 64) <= 131072;
-#ifdef MOE_EXP
-  if (const char *e = getenv("QG_MOE_SW")) L.sw_gu = L.sw_gu && atoi(e) != 0;
-  if (const char *e = getenv("QG_MOE_DT")) sscanf(e, "%d,%d", &L.dn_tok, &L.R_dt);
-#endif
   L.G_gu = (int)cdiv(Fmax / 16, L.W_gu);
   L.G_dn = (int)cdiv(m->hidden / 16, L.W_dn);
   L.gpart_per = L.S_gu > 1 ? (int64_t)L.S_gu * 2 * (Fmax / 16) * dot_part_floats(nc) : 0;
@@ -743,9 +729,6 @@ int launch_moe(const MoeCall &c) {
   a.dn_tok = L.dn_tok;
   a.sel_local = c.ntok == 1 && L.dn_tok;
   a.il_gu = dot_interleaved(a.H) ? 1 : 0;
-#ifdef MOE_EXP
-  if (const char *e = getenv("QG_MOE_SL")) a.sel_local = a.sel_local && atoi(e) != 0;
-#endif
   a.R_dt = L.R_dt;
   a.G_dt = (int)cdiv(a.H / 16, L.R_dt);
   if (a.R_dt < 1 || a.R_dt > 4) return QG_EUNSUPPORTED;

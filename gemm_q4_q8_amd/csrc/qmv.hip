@@ -17,10 +17,6 @@
 #include "dot_unit.h"
 #include "internal.h"
 #include "qgemm.h"
-#if defined(GEMM16_EXP) || defined(DOT_EXP)
-#include <stdio.h>
-#include <stdlib.h>
-#endif
 
 namespace qg {
 
@@ -163,9 +159,6 @@ int gemv_segments(int64_t rows, int64_t cols, int nmat, int ncols_max) {
 constexpr int GEMM16_STREAMS = 3000;
 int gemm16_splits(int64_t rows, int64_t cols) {
   const int64_t NT = cdiv(rows, 16), KT = cdiv(cols / 32, 4);
-#ifdef GEMM16_EXP
-  if (const char *e = getenv("QG_EXP_G16S")) return atoi(e);
-#endif
   int64_t s = (GEMM16_STREAMS + NT / 2) / NT;  // nearest
   if (s > 256 / cdiv(NT, 16)) s = 256 / cdiv(NT, 16);
   if (s > KT / 4) s = KT / 4;
@@ -320,10 +313,6 @@ static int launch_dot(const QmvCall &c, int S) {
     const int64_t cu_bytes = (int64_t)NMAT * R * KT * (QTraits<QT>::tile_bytes + TILE_D_BYTES);
     bool sw = R * S <= 16 && lds <= DOT_SW_LDS &&
               (dot_interleaved(c.cols) || 10 * u_sw >= 9 * u_cross || cu_bytes <= 196608);
-#ifdef DOT_EXP
-    if (getenv("QG_NO_SW")) sw = false;
-    if (getenv("QG_FORCE_SW")) sw = R * S <= 16 && lds <= DOT_SW_LDS;
-#endif
     if (sw) return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 16>(c, 1, (int)(R * S), S);
   }
   if (W <= 8) return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 8>(c, S, W);
@@ -367,17 +356,6 @@ static int dispatch_silu(const QmvCall &c, int S) {
 template <int QT, int EPI>
 static int launch_gemm16(const QmvCall &c) {
   const int S = gemm16_splits(c.rows, c.cols);
-#ifdef GEMM16_EXP
-  if (const char *e = getenv("QG_EXP_G16")) {
-    int w = 0, pf = 0;
-    if (sscanf(e, "%d,%d", &w, &pf) == 2) {
-      if (pf == 2) return launch_dot_t<QT, 16, 1, EPI, 1, 2, 0, true, 16>(c, S, w);
-      if (pf == 4) return launch_dot_t<QT, 16, 1, EPI, 1, 4, 0, true, 16>(c, S, w);
-      if (pf == 8) return launch_dot_t<QT, 16, 1, EPI, 1, 8, 0, true, 16>(c, S, w);
-      return QG_EUNSUPPORTED;
-    }
-  }
-#endif
   // at least 8 waves (the activation chunks are sized for them), else as
   // for the GEMV: one workgroup per CU when 8 to 16 waves allow it
   const int64_t NTu = cdiv(c.n_rows, 16), ncu = device_cus();
