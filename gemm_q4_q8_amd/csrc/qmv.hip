@@ -138,11 +138,23 @@ bool dot_interleaved(int64_t cols) {
 // per segment that `ncols_max` columns of f16 activations fit in DOT_X_LDS.
 int gemv_segments(int64_t rows, int64_t cols, int nmat, int ncols_max) {
   const int64_t NT = cdiv(rows, 16), KT = cdiv(cols / 32, 4);
-  // rounded down (the fused FFN needs the gate/up units in one round of
-  // resident workgroups), except that 1.5 or more becomes 2
-  const int64_t want = (int64_t)DOT_STREAMS * nmat;
-  int64_t s = want / NT;
-  if (s < 2 && 2 * want >= 3 * NT) s = 2;
+  int64_t s;
+  if (dot_interleaved(cols)) {
+    // interleaved segments run inside one workgroup of R row tiles x S
+    // segments, one per CU of a 256-CU part (a constant: the order must not
+    // depend on the device): the most segments that keep it within 15
+    // waves (measured: 12 to 15 waves per CU beat 10 and 16 on the verify
+    // and gate/up shapes)
+    const int64_t R = cdiv(NT, 256);
+    s = 15 / R;
+  } else {
+    // about DOT_STREAMS weight streams per matrix, rounded down (the fused
+    // FFN needs its gate/up units in one round of resident workgroups),
+    // except that 1.5 or more becomes 2
+    const int64_t want = (int64_t)DOT_STREAMS * nmat;
+    s = want / NT;
+    if (s < 2 && 2 * want >= 3 * NT) s = 2;
+  }
   if (s > KT / 4) s = KT / 4;
   const int64_t lds_min = cdiv(KT * TILE_BLOCKS * ncols_max * 64, (int64_t)DOT_X_LDS);
   if (s < lds_min) s = lds_min;
