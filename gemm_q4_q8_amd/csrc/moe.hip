@@ -209,7 +209,7 @@ template <int NCAP, int NJ>
 __global__ void __launch_bounds__(RW * 64) moe_router_kernel(MoeArgs a) {
   constexpr int NTHR = RW * 64;
   __shared__ uint32_t flag;
-  __shared__ int32_t s_sel[TMAX * 8];
+  __shared__ __attribute__((aligned(16))) int32_t s_sel[TMAX * 8];
   __shared__ int32_t s_cnt[1024], s_off[1024];  // per expert (n_expert <= 1024)
   __shared__ int32_t s_wtot[RW];
   __shared__ float s_part[RW];
@@ -305,8 +305,14 @@ __global__ void __launch_bounds__(RW * 64) moe_router_kernel(MoeArgs a) {
   // each slot: its position among its expert's slots -> (entry, column)
   if (tid < nslot) {
     const int ee = s_sel[tid];
+    // earlier slots of the same expert, four per LDS read
     int pos = 0;
-    for (int q = 0; q < tid; ++q) pos += s_sel[q] == ee ? 1 : 0;
+    const int4 *s4 = (const int4 *)s_sel;
+    for (int q4 = 0; q4 < tid / 4; ++q4) {
+      const int4 v = s4[q4];
+      pos += (v.x == ee) + (v.y == ee) + (v.z == ee) + (v.w == ee);
+    }
+    for (int q = tid & ~3; q < tid; ++q) pos += s_sel[q] == ee ? 1 : 0;
     const int u = s_off[ee] + pos / NCAP, col = pos % NCAP;
     a.used_slot[u * TMAX + col] = tid;
     if (col == 0) {
