@@ -1,6 +1,7 @@
-// One work unit of the dot path (1..8 activation columns): a K segment of
-// WKT * RT row tiles of one or two matrices (gate and up), used by the GEMV
-// kernels and by the fused FFN kernel.
+// One work unit of the product kernels: W row tiles (one per wave, of one
+// matrix or of gate and up together) over one K segment, used by the GEMV
+// (1..8 columns), gate/up, LM head and 16-column GEMM kernels, the fused
+// FFN and the MoE expert kernels.
 //
 // What is computed ("Engine and kernels", Kernel families): y = W x over
 // Q4_0 / Q8_0 blocks dequantised in registers with f32 sums, with the
@@ -8,25 +9,28 @@
 // the per-row values an argmax needs).
 //
 // How (MI355X):
-//  * The workgroup stages the segment's activations once in LDS as f16,
-//    [block][column][32], read with broadcast by every wave.
-//  * One wave streams one row tile (of each matrix) across the segment, PF
-//    tile columns ahead; each 16-byte load of a wave reads a contiguous
-//    1 KiB stripe.  The stream is a bounded buffer range, so loads past the
-//    segment return zeros without touching memory and the loop has no
-//    branch around its loads.
-//  * Weights become exact f16 pairs and meet the activations in
-//    v_dot2_f32_f16; each block's partial is scaled by its f16 scale in f32.
-//  * Reduction order: tile columns in order within a wave, a 2-step lane
-//    butterfly, then the S segment partials in segment order (the last
-//    workgroup of the row group to finish adds them).  The order depends on
-//    the shape only, so each activation column of a batched call is bitwise
-//    equal to a 1-column call ("Architecture", Speculative decoding).
+//  * The workgroup stages its activations once in LDS as f16,
+//    [block][column][32] (16 columns: in double-buffered chunks).
+//  * One wave streams one row tile across its segment, PF tile columns
+//    ahead; each 16-byte load of a wave reads a contiguous 1 KiB stripe.
+//    The stream is a bounded buffer range, so loads past it return zeros
+//    without touching memory and the loop has no branch around its loads.
+//  * Weights become exact f16 values; per block, one matrix-core product
+//    (activation columns x the block's 16 rows) gives each lane its columns,
+//    scaled by the block's f16 scale into f32 accumulators.
+//  * Segments: S of them, contiguous K ranges or interleaved tile columns
+//    (segment q takes q, q + S, ...), chosen by the shape; summed in
+//    segment order, either by the last workgroup of the row group (from
+//    partials in memory) or, with the segments as waves of one workgroup,
+//    through LDS.  The order depends on the shape only, so each activation
+//    column of a batched call is bitwise equal to a 1-column call
+//    ("Architecture", Speculative decoding).
 //
 // Phases, for the fused FFN: a producer unit (gate/up) publishes the h rows
 // of its row group with coherent stores and then raises that group's ready
 // flag; a consumer unit (down) issues its first weight loads, waits until
-// the flags of its K segment are raised, and reads h with coherent loads.
+// the flags of the h rows it reads are raised, and reads h with coherent
+// loads.
 #pragma once
 #include "common.h"
 #include "internal.h"
@@ -79,16 +83,11 @@ struct DotArgs {
   int64_t xspan;      // bytes of X the columns may read (0: the ncols columns)
 };
 
-// Returns true when this workgroup emitted the outputs of row group g (its
-// only segment, or the last of its segments to finish).  For the argmax
-// epilogue, (bv, bi) then hold each lane's best (value, row).
+// The default `staged` hook of dot_unit: nothing.
 struct NoHook {
   __device__ void operator()() const {}
 };
 
-// `staged` runs once the activations are in LDS and the first weight loads
-// are in flight (the fused FFN takes its next work unit there, so that
-// round trip overlaps the stream).
 // Register fence after a matrix-core product and the FMAs that read its
 // result.  The matrix core reads A and B and writes all four result
 // registers over several passes after the instruction issues; a register it
@@ -116,6 +115,13 @@ __device__ __forceinline__ void mfma_fence(float (&acc)[NI], const h8 &A, const 
     __asm__ volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]) : "v"(A), "v"(B), "v"(D));
 }
 
+// The unit (row group g, segment s) of the launch `a`.  Returns true when
+// this workgroup emitted the outputs of row group g (its only segment, or
+// the last of its segments to finish).  For the argmax epilogue, (bv, bi)
+// then hold each lane's best (value, row).  `staged` runs once the
+// activations are in LDS and the first weight loads are in flight (the
+// fused FFN takes its next work unit there, so that round trip overlaps the
+// stream).
 template <int QT, int NC, int NMAT, int EPI, int RT, int PF, int WKT, int PH, bool MF = false,
           class Hook = NoHook>
 __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t *smem, uint32_t *flag,
