@@ -89,8 +89,17 @@ __device__ __forceinline__ u2 ld_stream2(const uint8_t *p) { return __builtin_no
 // buffer range check of gfx9), so a prefetch loop can run past the end of
 // its range without a branch around its loads.  Offsets go in the VGPR
 // offset, which is what the range check covers.
+// A range belongs to the wave: every lane passes the same base and size.
+// The descriptor lives in scalar registers; taking both from the first lane
+// says so to the compiler, which otherwise, where it cannot prove the values
+// uniform (e.g. an expert chosen at run time), wraps each load in a loop
+// over the distinct per-lane descriptors.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_range(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+  const uint64_t b = (uint64_t)base;
+  const uint64_t ub = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  return __builtin_amdgcn_make_buffer_rsrc((void *)ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                           0x00020000);
 }
 // nontemporal (aux bit 1): streamed once, no cache allocation
 __device__ __forceinline__ u4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {

@@ -115,6 +115,19 @@ __device__ __forceinline__ void mfma_fence(float (&acc)[NI], const h8 &A, const 
     __asm__ volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]) : "v"(A), "v"(B), "v"(D));
 }
 
+// The same, one fence over the four block products of a tile.
+#define QG_FENCE_IN "v"(A[0]), "v"(A[1]), "v"(A[2]), "v"(A[3]), "v"(B[0]), "v"(B[1]), "v"(B[2]), "v"(B[3]), \
+                    "v"(D[0]), "v"(D[1]), "v"(D[2]), "v"(D[3])
+template <int NI>
+__device__ __forceinline__ void mfma_fence(float (&acc)[NI], const h8 (&A)[4], const h8 (&B)[4], const f4 (&D)[4]) {
+  static_assert(NI >= 1 && NI <= 4, "columns per lane");
+  if constexpr (NI == 1) __asm__ volatile("" : "+v"(acc[0]) : QG_FENCE_IN);
+  else if constexpr (NI == 2) __asm__ volatile("" : "+v"(acc[0]), "+v"(acc[1]) : QG_FENCE_IN);
+  else if constexpr (NI == 3) __asm__ volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]) : QG_FENCE_IN);
+  else __asm__ volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]) : QG_FENCE_IN);
+}
+#undef QG_FENCE_IN
+
 // The unit (row group g, segment s) of the launch `a`.  Returns true when
 // this workgroup emitted the outputs of row group g (its only segment, or
 // the last of its segments to finish).  For the argmax epilogue, (bv, bi)
@@ -172,18 +185,25 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   const int nvec = nkt * TILE_BLOCKS * NC * 4;  // 8-value pieces of the segment
   const __amdgpu_buffer_rsrc_t rx =
       buf_range(a.X, (uint32_t)(a.xspan ? a.xspan : ((int64_t)(a.ncols - 1) * a.ldx + a.cols) * 4));
+  // the X column piece v reads (through the column map, if any); a piece's
+  // column does not change from chunk to chunk, so streamed staging looks
+  // it up once, not inside the weight stream (a map load there would make
+  // every chunk wait for all weight loads in flight)
+  auto x_col = [&](int v) -> int64_t {
+    const int c = (v >> 2) % NC;
+    return c < a.ncols && a.xmap ? a.xmap[c] : c;
+  };
   // piece v of the `span` pieces from tile column rel0 on: (block, column,
-  // 8 k) -> byte offset in X, or past any range (reads zeros) when it lies
-  // outside the span, the segment or the matrix
-  auto x_off = [&](int v, int rel0, int span) -> uint32_t {
+  // 8 k) -> byte offset in X column xc, or past any range (reads zeros) when
+  // it lies outside the span, the segment or the matrix
+  auto x_off = [&](int v, int rel0, int span, int64_t xc) -> uint32_t {
     const int qq = v & 3, c = (v >> 2) % NC, bl = (v >> 2) / NC;
     const int64_t k = ((int64_t)(kt0 + rel0) * TILE_BLOCKS + bl) * 32 + qq * 8;
     const bool ok = v < span && rel0 * TILE_BLOCKS + bl < nkt * TILE_BLOCKS && k < a.cols && c < a.ncols;
-    const int64_t xc = ok && a.xmap ? a.xmap[c] : c;
     return ok ? (uint32_t)((xc * a.ldx + k) * 4) : 0xFFFFFFC0u;
   };
-  auto x_ld = [&](int v, int rel0, int span, u4 &lo, u4 &hi) {
-    const uint32_t o = x_off(v, rel0, span);
+  auto x_ld = [&](int v, int rel0, int span, int64_t xc, u4 &lo, u4 &hi) {
+    const uint32_t o = x_off(v, rel0, span, xc);
     lo = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, XAUX);
     hi = __builtin_amdgcn_raw_buffer_load_b128(rx, o + 16u, 0, XAUX);
   };
@@ -231,9 +251,12 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   constexpr int X0 = XS ? XR : 1;
   const int span0 = XS ? CHV : nvec;
   u4 xl[X0], xh[X0];
+  int64_t xcs[X0];
+#pragma unroll
+  for (int i = 0; i < X0; ++i) xcs[i] = x_col(tid + i * NTHR);
   if constexpr (PH != PH_CONSUME) {
 #pragma unroll
-    for (int i = 0; i < X0; ++i) x_ld(tid + i * NTHR, 0, span0, xl[i], xh[i]);
+    for (int i = 0; i < X0; ++i) x_ld(tid + i * NTHR, 0, span0, xcs[i], xl[i], xh[i]);
   }
 #pragma unroll
   for (int p = 0; p < PF; ++p) load(p, p);
@@ -255,7 +278,7 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < X0; ++i) x_ld(tid + i * NTHR, 0, span0, xl[i], xh[i]);
+    for (int i = 0; i < X0; ++i) x_ld(tid + i * NTHR, 0, span0, xcs[i], xl[i], xh[i]);
   }
 
   // ---- 2. staging: f16 in LDS, [block][column][32] (XS: chunk 0 into
@@ -268,7 +291,7 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
     for (int v0 = tid + NTHR; v0 < nvec; v0 += XB * NTHR) {
       u4 lo[XB], hi[XB];
 #pragma unroll
-      for (int b = 0; b < XB; ++b) x_ld(v0 + b * NTHR, 0, nvec, lo[b], hi[b]);
+      for (int b = 0; b < XB; ++b) x_ld(v0 + b * NTHR, 0, nvec, x_col(v0 + b * NTHR), lo[b], hi[b]);
 #pragma unroll
       for (int b = 0; b < XB; ++b) x_put(v0 + b * NTHR, nvec, xs, lo[b], hi[b]);
     }
@@ -286,10 +309,20 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
       for (int c = 0; c < NI; ++c) acc[m][t][c] = 0.0f;
 
   const Q4Magic mg = q4_magic();
-  // matrix-core A operand: lane (r, sl) holds column r, k 8 sl .. 8 sl + 7.
-  // Lanes of columns past NC keep zeros: they never load (exec-masked), so
-  // the register set to zero here stays zero.
-  h8 A = {0, 0, 0, 0, 0, 0, 0, 0};
+  // matrix-core A operands of a tile's four blocks: lane (r, sl) holds
+  // column r, k 8 sl .. 8 sl + 7.  Lanes of columns past NC keep zeros: they
+  // never load (exec-masked), so the registers set to zero here stay zero.
+  // 16 columns issue the four blocks' reads and products together (the
+  // products of a tile overlap the LDS reads); narrower batches, whose
+  // streams are bound by memory, keep one block at a time (fewer registers:
+  // the fused FFN keeps two workgroups per CU).
+#ifndef DOT_GA_MIN
+#define DOT_GA_MIN 16
+#endif
+  constexpr bool GA = NC >= DOT_GA_MIN;
+  h8 A[TILE_BLOCKS];
+#pragma unroll
+  for (int j = 0; j < TILE_BLOCKS; ++j) A[j] = h8{0, 0, 0, 0, 0, 0, 0, 0};
   auto compute = [&](int slot, int rel) {
     // block index in LDS: the staged range's own (this wave's stream starts
     // wkt0 tile columns in), or, streaming, the slot of tile column rel in
@@ -298,25 +331,53 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
     if constexpr (MF) {
       // per block: D (16 columns x 16 rows) = X_blk^T W_blk^T on the matrix
       // cores from the exact f16 weights, then each lane's 4 D values get
-      // the block scale of its row
+      // the block scale of its row, blocks in order
+      if constexpr (!GA) {
 #pragma unroll
-      for (int j = 0; j < TILE_BLOCKS; ++j) {
-        if (NC == 16 || r < NC) A = *(const h8 *)(xs + ((size_t)(bl0 + j) * XC + r) * 32 + sl * 8);
+        for (int j = 0; j < TILE_BLOCKS; ++j) {
+          if (NC == 16 || r < NC) A[0] = *(const h8 *)(xs + ((size_t)(bl0 + j) * XC + r) * 32 + sl * 8);
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m)
+          for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-          for (int t = 0; t < RT; ++t) {
+            for (int t = 0; t < RT; ++t) {
+              h2 w[4];
+              if constexpr (QT == Q4) unpack_q4(wq[slot][m][t][0][j], w, mg);
+              else unpack_q8(wq[slot][m][t][j >> 1][(j & 1) * 2], wq[slot][m][t][j >> 1][(j & 1) * 2 + 1], w);
+              const h8 B = {w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
+              const f4 D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], B, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+              const float dj = scale_of(wd[slot][m][t], j);
+#pragma unroll
+              for (int i = 0; i < NI; ++i) acc[m][t][i] = __builtin_fmaf(dj, D[i], acc[m][t][i]);
+              mfma_fence(acc[m][t], A[0], B, D);
+            }
+        }
+        return;
+      }
+#pragma unroll
+      for (int j = 0; j < TILE_BLOCKS; ++j)
+        if (NC == 16 || r < NC) A[j] = *(const h8 *)(xs + ((size_t)(bl0 + j) * XC + r) * 32 + sl * 8);
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          h8 B[TILE_BLOCKS];
+          f4 D[TILE_BLOCKS];
+#pragma unroll
+          for (int j = 0; j < TILE_BLOCKS; ++j) {
             h2 w[4];
             if constexpr (QT == Q4) unpack_q4(wq[slot][m][t][0][j], w, mg);
             else unpack_q8(wq[slot][m][t][j >> 1][(j & 1) * 2], wq[slot][m][t][j >> 1][(j & 1) * 2 + 1], w);
-            const h8 B = {w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
-            const f4 D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            B[j] = h8{w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
+            D[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[j], B[j], f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          }
+#pragma unroll
+          for (int j = 0; j < TILE_BLOCKS; ++j) {
             const float dj = scale_of(wd[slot][m][t], j);
 #pragma unroll
-            for (int i = 0; i < NI; ++i) acc[m][t][i] = __builtin_fmaf(dj, D[i], acc[m][t][i]);
-            mfma_fence(acc[m][t], A, B, D);
+            for (int i = 0; i < NI; ++i) acc[m][t][i] = __builtin_fmaf(dj, D[j][i], acc[m][t][i]);
           }
-      }
+          mfma_fence(acc[m][t], A, B, D);
+        }
       return;
     }
 #pragma unroll
@@ -355,7 +416,7 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
     for (int k = 0; k < nkt; k += PF) {
       u4 nl[XR], nh[XR];
 #pragma unroll
-      for (int i = 0; i < XR; ++i) x_ld(tid + i * NTHR, k + PF, CHV, nl[i], nh[i]);
+      for (int i = 0; i < XR; ++i) x_ld(tid + i * NTHR, k + PF, CHV, xcs[i], nl[i], nh[i]);
 #pragma unroll
       for (int p = 0; p < PF; ++p) {
         if (live && k + p < nkt) compute(p, k + p);

@@ -332,7 +332,10 @@ template <bool GATEUP, int NC>
 __device__ __forceinline__ int moe_expert(const MoeArgs &a, int u, DotArgs &d, int32_t *s_x, int32_t *s_y,
                                           const int32_t *loc_e = nullptr, const int32_t *loc_slot = nullptr) {
   const int tid = threadIdx.x;
-  const int nused = loc_e ? a.k : (int)*a.nused;
+  // every value below is the same in all lanes (read from one address);
+  // readfirstlane lets the compiler see that, so the expert's weight
+  // ranges are scalar and its loads need no per-lane loop
+  const int nused = loc_e ? a.k : __builtin_amdgcn_readfirstlane((int)*a.nused);
   const int nsh = a.SF > 0 ? (a.T + NC - 1) / NC : 0;
   if (u >= nused + nsh) return 0;
   const bool shared = u >= nused;
@@ -352,8 +355,8 @@ __device__ __forceinline__ int moe_expert(const MoeArgs &a, int u, DotArgs &d, i
   } else {
     // the work-list entry, or (one token, selected locally) the expert of
     // index-order position u and its slot
-    const int e = loc_e ? loc_e[u] : a.used_e[u];
-    nc = loc_e ? 1 : a.used_cnt[u];
+    const int e = __builtin_amdgcn_readfirstlane(loc_e ? loc_e[u] : a.used_e[u]);
+    nc = loc_e ? 1 : __builtin_amdgcn_readfirstlane(a.used_cnt[u]);
     if (tid < nc) {
       const int q = loc_e ? loc_slot[u] : a.used_slot[u * TMAX + tid];
       s_x[tid] = GATEUP ? q / a.k : q;
