@@ -284,9 +284,28 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   // ---- 2. staging: f16 in LDS, [block][column][32] (XS: chunk 0 into
   // buffer 0).  Otherwise further pieces of the segment go in batches of XB
   // whose loads are all issued before any is used.
+  //
+  // A piece past the segment is loaded (it reads zeros) but not stored, so
+  // no store waits for its load; left pending, that load would be waited
+  // for wherever its register is next written, which can be inside the
+  // weight stream, at every tile.  So each staging step ends with a wait of
+  // its own: after each batch, for everything (the weight tiles were issued
+  // earlier and return first); after the first pieces, for everything with
+  // one matrix or when the activations came last, else for everything but
+  // the first weight tiles.  The wait at the loop's entry also shapes the
+  // waits the compiler places inside it: measured, one matrix streams best
+  // after the full wait (6-7 loads kept in flight per wave: decode down
+  // 14.0 -> 13.1 us), gate and up together after the partial one (the full
+  // wait keeps more in flight there and was 0.6 us slower).
+  constexpr int NWL = PF * NMAT * RT * (QW + 1);  // loads of the first PF tile columns
+  static_assert(NWL <= 63, "wait count");
+  constexpr int WAIT_ALL = 0x0F70;                // vmcnt(0), other counters untouched
+  constexpr int WAIT_X0 =
+      (PH == PH_CONSUME || NMAT == 1) ? WAIT_ALL : (WAIT_ALL | (NWL & 15) | ((NWL >> 4) << 14));
 #pragma unroll
   for (int i = 0; i < X0; ++i) x_put(tid + i * NTHR, span0, xs, xl[i], xh[i]);
   if constexpr (!XS) {
+    __builtin_amdgcn_s_waitcnt(WAIT_X0);
     constexpr int XB = 4;
     for (int v0 = tid + NTHR; v0 < nvec; v0 += XB * NTHR) {
       u4 lo[XB], hi[XB];
@@ -294,6 +313,7 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
       for (int b = 0; b < XB; ++b) x_ld(v0 + b * NTHR, 0, nvec, x_col(v0 + b * NTHR), lo[b], hi[b]);
 #pragma unroll
       for (int b = 0; b < XB; ++b) x_put(v0 + b * NTHR, nvec, xs, lo[b], hi[b]);
+      __builtin_amdgcn_s_waitcnt(WAIT_ALL);
     }
   }
   __syncthreads();

@@ -201,15 +201,9 @@ def test_no_register_reuse_under_matrix_core_products(assembly):
     assert total > 0
 
 
-# The MoE down kernel for expert FFNs too wide for the per-token form keeps
-# one full wait in its loop (the register of a tile's unpacked weights is the
-# target of a load still in flight); it runs only for those shapes.
-FULL_WAIT_ALLOWED = ("moe_down_kernel",)
-
-
 def test_no_full_wait_in_product_loops(assembly):
     for src, lines in assembly.items():
-        bad = [k for k in full_waits_in_product_loops(lines) if not any(a in k[0] for a in FULL_WAIT_ALLOWED)]
+        bad = full_waits_in_product_loops(lines)
         assert not bad, f"{src}: loops of products that wait for every load: {bad[:3]}"
 
 
