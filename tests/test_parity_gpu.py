@@ -133,8 +133,11 @@ def test_degenerate_weights(env):
 
 
 # ------------------------------------------------------------------ gemm16
+# (4352, 2048), (8200, 1664), (12300, 1152): several row tiles per CU with
+# 4, 3 and 2 K segments and ragged last row tiles.
 @pytest.mark.parametrize("qtype", [Q4, Q8])
-@pytest.mark.parametrize("rows,cols", [(40, 416), (64, 4096), (200, 2080), (16, 128)])
+@pytest.mark.parametrize("rows,cols", [(40, 416), (64, 4096), (200, 2080), (16, 128),
+                                       (4352, 2048), (8200, 1664), (12300, 1152)])
 @pytest.mark.parametrize("acc", [0, 1])
 def test_gemm16_parity(env, qtype, rows, cols, acc):
     torch, qg, dev = env
