@@ -27,10 +27,10 @@
 //    ("Architecture", Speculative decoding).
 //
 // Phases, for the fused FFN: a producer unit (gate/up) publishes the h rows
-// of its row group with coherent stores and then raises that group's ready
-// flag; a consumer unit (down) issues its first weight loads, waits until
-// the flags of the h rows it reads are raised, and reads h with coherent
-// loads.
+// of its row group with coherent stores and then raises the ready flag of
+// each of its row tiles; a consumer unit (down) issues its first weight
+// loads, waits until the flags of the h row tiles its K segment reads are
+// raised, and reads h with coherent loads.
 #pragma once
 #include "common.h"
 #include "internal.h"
@@ -77,8 +77,11 @@ struct DotArgs {
   int32_t *cand_i;
   int32_t *out_idx;
   float *out_val;
-  uint32_t *ready;    // fused FFN: producer sets ready[g]; consumer waits on ready[kt]
+  uint32_t *ready;    // fused FFN: one flag per h row tile, raised by its producer unit
+  int ready_n;        // fused FFN, consumer: h row tiles (flags) in all
   uint32_t *err;      // fused FFN: set when a wait gave up
+  int NWU;            // waves of the unit (<= 0: every wave of the workgroup); the
+                      // other waves only take part in its barriers
   const int32_t *xmap, *ymap;  // MoE: column c reads X column xmap[c], writes Y column ymap[c]
   int64_t xspan;      // bytes of X the columns may read (0: the ncols columns)
 };
@@ -167,8 +170,10 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   // segment q of nq takes tile columns q, q + nq, ... (wst = nq);
   // contiguous ones: its range [wkt0, wkt0 + wnkt) of the staged columns.
   const int SW = (!XS && a.SW > 1) ? a.SW : 1;
-  const int R = (NTHR >> 6) / SW;
-  const int wrt = wk % R, wsg = wk / R;
+  const int NWA = a.NWU > 0 ? a.NWU : (NTHR >> 6);  // waves of the unit
+  const bool idle = wk >= NWA;                      // stages, waits at barriers, streams nothing
+  const int R = NWA / SW;
+  const int wrt = idle ? 0 : wk % R, wsg = idle ? 0 : wk / R;
   const bool IL = !XS && a.IL;
   const int kt0 = IL ? 0 : seg_begin(s, a.KT, a.S);
   const int nkt = IL ? a.KT : seg_begin(s + 1, a.KT, a.S) - kt0;
@@ -176,7 +181,7 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   const int wkt0 = IL ? wq_i : seg_begin(wsg, nkt, SW);        // first tile column, relative to kt0
   const int wst = IL ? wq_n : 1;                               // step between its tile columns
   const int wnkt = IL ? (nkt - wq_i + wq_n - 1) / wq_n : seg_begin(wsg + 1, nkt, SW) - wkt0;
-  const int64_t rt_base = ((int64_t)g * R + wrt) * RT;
+  const int64_t rt_base = idle ? (int64_t)a.NT : ((int64_t)g * R + wrt) * RT;
   const int r = lane & 15, sl = lane >> 4;
   _Float16 *xs = (_Float16 *)smem;
 
@@ -263,11 +268,13 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
 
   if constexpr (PH == PH_CONSUME) {
     // the activations are h rows other workgroups produce: wait until the
-    // ready flags of this segment's tile columns are raised
+    // ready flags of the h row tiles of this segment's tile columns (8 row
+    // tiles of 16 to a column of 128) are raised
     if (wk == 0) {
+      const int f0 = kt0 * 8, nf = (nkt * 8 < a.ready_n - f0) ? nkt * 8 : a.ready_n - f0;
       for (int it = 0;; ++it) {
         bool ok = true;
-        for (int j = lane; j < nkt; j += 64) ok = ok && ld_agent_u32(a.ready + kt0 + j) != 0u;
+        for (int j = lane; j < nf; j += 64) ok = ok && ld_agent_u32(a.ready + f0 + j) != 0u;
         if (__all(ok)) break;
         if (it >= WAIT_POLLS) {
           if (lane == 0) st_agent_u32(a.err, 1u);
@@ -616,12 +623,13 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   }
 
   if constexpr (PH == PH_PRODUCE) {
-    // h rows of row group g are out: raise its flag once every wave's
-    // stores are acknowledged
+    // h rows of row group g are out: raise the flags of its row tiles once
+    // every wave's stores are acknowledged
     if (emitted && a.ready) {
       __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (tid == 0) st_agent_u32(a.ready + g, 1u);
+      const int64_t f = (int64_t)g * R * RT + tid;
+      if (tid < R * RT && f < a.NT) st_agent_u32(a.ready + f, 1u);
     }
   }
   return emitted;

@@ -254,7 +254,9 @@ static int launch_dot_t(const QmvCall &c, int S, int W = WKT, int SW = 1) {
   a.out_idx = c.out_idx;
   a.out_val = c.out_val;
   a.ready = nullptr;
+  a.ready_n = 0;
   a.err = nullptr;
+  a.NWU = 0;
   a.xmap = a.ymap = nullptr;
   a.xspan = 0;
   if (!ranges_fit(c, NT, KT, QTraits<QT>::tile_bytes)) return QG_EUNSUPPORTED;
