@@ -11,8 +11,9 @@ What it computes, in float64, from the canonical GGUF block bytes:
   dequantisation, and the byte image of the library's repacked layout
   written out from that layout's definition.
 * `ops`    - y = W x (and y += W x), the fused gate/up SiLU, LM-head argmax
-  with lowest-index ties, router top-k, softmax, the MoE FFN, and the
-  tolerances and argmax / top-k certification used by the parity tests.
+  and LM-head top-k candidates with lowest-index ties, router top-k,
+  softmax, the MoE FFN, and the tolerances and argmax / top-k certification
+  used by the parity tests.
 
 Pins (tests/test_oracle.py) tie every function to something other than
 itself: hand-worked blocks, exact rational brute force, closed forms,

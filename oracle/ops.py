@@ -187,6 +187,25 @@ def topk_certified(logits: np.ndarray, a: np.ndarray, k: int, k_terms: int,
 
 
 # --------------------------------------------------------------------------
+# LM head + top-k candidates.  "Architecture", one token end to end (greedy
+# and top-k sampling on the GPU, a few bytes read back instead of the 1 MB
+# logits); "Engine and kernels", Sampling and Fewer passes (GPU top-k, the
+# CPU loop's lowest-index ties); "Running LLMs in the browser with Three.js",
+# Reduce sampling on the GPU (a small top-k reduction on the GPU, the host
+# finishes the draw from the candidates).  Reading: the candidates are the k
+# largest logits over rows < n_rows, ordered by (value descending, index
+# ascending); k is small (the Three.js example asks for 10).
+# --------------------------------------------------------------------------
+def lmhead_topk(qtype: int, raw: np.ndarray, x: np.ndarray, n_rows: int, k: int):
+    """raw: uint8 [R, K/32, B]; x: [K].  Returns (idx int64 [k], val float64
+    [k], logits float64 [n_rows], a [n_rows]) with a = |W| |x| the scale of the
+    logits' rounding error."""
+    logits, a = gemv(qtype, raw[:n_rows], x)
+    idx = topk_lowest_index(logits, k)
+    return idx, logits[idx], logits, a
+
+
+# --------------------------------------------------------------------------
 # MoE FFN.  "Engine and kernels": the MoE model's FFN is 256 experts (8 active
 # per token) plus a shared expert; router, top-k, expert gate/up and down and
 # the weighted combine on the GPU.  "A 235B model in a browser window": each

@@ -235,6 +235,37 @@ def test_topk_matches_sorted_and_ties():
     assert list(ops.topk_lowest_index(np.zeros(12), 8)) == list(range(8))
 
 
+def test_lmhead_topk_by_brute_force():
+    """The LM-head candidates: each one's logit is its row's exact product
+    (rational brute force over the decoded block), the list is what a full
+    sort of all rows by (value desc, index asc) starts with, k = 1 is the
+    greedy argmax, and rows at or past n_rows never appear."""
+    from fractions import Fraction
+    g = np.random.default_rng(15)
+    for qtype in (Q4, Q8):
+        rows, cols, n_rows = 23, 64, 19
+        raw = synth.gen_weights(qtype, rows, cols, 0.02, g)
+        x = (g.integers(-8, 9, cols) / 8.0).astype(np.float64)
+        w = quant.dequantize(qtype, raw)
+        exact = [sum(Fraction(float(w[r, j])) * Fraction(float(x[j])) for j in range(cols)) for r in range(n_rows)]
+        for k in (1, 4, n_rows):
+            idx, val, logits, _ = ops.lmhead_topk(qtype, raw, x, n_rows, k)
+            want = sorted(range(n_rows), key=lambda r: (-exact[r], r))[:k]
+            assert list(idx) == want
+            assert all(float(exact[r]) == v for r, v in zip(idx, val))
+            assert max(idx) < n_rows
+        idx1, _, logits, _ = ops.lmhead_topk(qtype, raw, x, n_rows, 1)
+        assert idx1[0] == ops.argmax_first(logits)
+    # planted ties: duplicated rows give equal logits, the lower row first
+    raw = synth.gen_weights(Q8, 6, 32, 0.02, g)
+    raw[4] = raw[1]
+    raw[5] = raw[1]
+    x = np.ones(32)
+    idx, val, logits, _ = ops.lmhead_topk(Q8, raw, x, 6, 6)
+    pos = {int(r): i for i, r in enumerate(idx)}
+    assert pos[1] < pos[4] < pos[5] and pos[5] == pos[1] + 2
+
+
 def test_softmax_properties():
     g = np.random.default_rng(14)
     v = g.standard_normal(8)
