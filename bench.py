@@ -182,6 +182,12 @@ def run_extras(B, kernels):
     ov = torch.empty(1, dtype=torch.float32, device=B.dev)
     t, _ = B.graph_time([lambda m=m: qg.lmhead_argmax(m, x, None, oi, ov) for m in p], 20)
     kernels["lmhead_argmax_q8_0_5120to248320"] = kernel_entry(qbytes(Q8, N, K) + 4 * K + 8, t)
+    # the same head returning the 10 best (value, row) pairs (the Three.js
+    # page's example asks for top-k 10)
+    ti = torch.empty(10, dtype=torch.int32, device=B.dev)
+    tv = torch.empty(10, dtype=torch.float32, device=B.dev)
+    t, _ = B.graph_time([lambda m=m: qg.lmhead_topk(m, x, 10, None, ti, tv) for m in p], 20)
+    kernels["lmhead_topk10_q8_0_5120to248320"] = kernel_entry(qbytes(Q8, N, K) + 4 * K + 80, t)
     del p, w
     log("  lmhead done")
 

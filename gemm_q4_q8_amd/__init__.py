@@ -69,6 +69,9 @@ _SIGS = {
     "gateup_silu": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _i32,
                                    _vp, _i64, _vp, _sz, _vp]),
     "qg_lmhead_ws_bytes": (_sz, [_i64, _i64]),
+    "qg_lmhead_topk_ws_bytes": (_sz, [_i64, _i64, _i32]),
+    "lmhead_topk": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp,
+                                   _vp, _sz, _vp]),
     "lmhead_argmax": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp,
                                      _vp, _sz, _vp]),
     "qg_moe_ws_bytes": (_sz, [ctypes.POINTER(qg_moe), _i32]),
@@ -285,6 +288,23 @@ def lmhead_argmax(w: QMatrix, x, n_rows: Optional[int] = None, out_idx=None, out
                              w.rows if n_rows is None else n_rows, x.data_ptr(),
                              out_idx.data_ptr(), out_val.data_ptr(), ws.data_ptr(), ws.numel(),
                              _stream(x.device)), "lmhead_argmax")
+    return out_idx, out_val
+
+
+def lmhead_topk(w: QMatrix, x, k: int, n_rows: Optional[int] = None, out_idx=None, out_val=None):
+    """The k largest logits of W x over rows < n_rows, value descending then
+    row ascending: (idx int32 [k], val f32 [k]) on the GPU (no host sync)."""
+    torch = _torch()
+    _check_dev(x)
+    if out_idx is None:
+        out_idx = torch.empty(k, dtype=torch.int32, device=x.device)
+    if out_val is None:
+        out_val = torch.empty(k, dtype=torch.float32, device=x.device)
+    ws = workspace(lib.qg_lmhead_topk_ws_bytes(w.rows, w.cols, k), x.device, "lmhead_topk")
+    _check(lib.lmhead_topk(w.qtype, w.qs.data_ptr(), w.d.data_ptr(), w.rows, w.cols,
+                           w.rows if n_rows is None else n_rows, x.data_ptr(), k,
+                           out_idx.data_ptr(), out_val.data_ptr(), ws.data_ptr(), ws.numel(),
+                           _stream(x.device)), "lmhead_topk")
     return out_idx, out_val
 
 

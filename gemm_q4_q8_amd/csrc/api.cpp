@@ -156,6 +156,11 @@ size_t qg_lmhead_ws_bytes(int64_t rows, int64_t cols) {
   return qmv_ws_bytes(rows, cols, gemv_segments(rows, cols, 1, 1), 1, 1, true);
 }
 
+size_t qg_lmhead_topk_ws_bytes(int64_t rows, int64_t cols, int32_t k) {
+  if (rows <= 0 || cols <= 0 || cols % 32 || k < 1 || k > QG_TOPK_MAX) return 0;
+  return qmv_ws_bytes(rows, cols, gemv_segments(rows, cols, 1, 1), 1, 1, false, k);
+}
+
 int qgemv_q4_0(const void *qs, const void *d, int64_t rows, int64_t cols, const float *X, int64_t ldx,
                int32_t ncols, float *Y, int64_t ldy, int32_t accumulate, void *ws, size_t ws_bytes,
                void *stream) {
@@ -241,6 +246,43 @@ int lmhead_argmax(int qtype, const void *qs, const void *d, int64_t rows, int64_
   c.epi = EPI_ARGMAX;
   c.out_idx = out_idx;
   c.out_val = out_val;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  c.stream = (hipStream_t)stream;
+  return launch_qmv(c);
+}
+
+int lmhead_topk(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols, int64_t n_rows,
+                const float *x, int32_t k, int32_t *out_idx, float *out_val, void *ws, size_t ws_bytes,
+                void *stream) {
+  if (!qtype_ok(qtype)) return QG_EINVAL;
+  int st = check_matrix(qs, d, rows, cols);
+  if (st) return st;
+  if (n_rows < 1 || n_rows > rows) return QG_ESHAPE;
+  if (k < 1 || k > QG_TOPK_MAX || k > n_rows) return QG_ESHAPE;
+  if ((st = check_act(x, cols, cols, 1))) return st;
+  if (!out_idx) return QG_EINVAL;
+  if (!aligned(out_idx, 4) || (out_val && !aligned(out_val, 4))) return QG_EALIGN;
+  if (!ws || ws_bytes < qg_lmhead_topk_ws_bytes(rows, cols, k)) return QG_EWORKSPACE;
+  if (!aligned(ws, 256)) return QG_EALIGN;
+  QmvCall c;
+  memset(&c, 0, sizeof(c));
+  c.qtype = qtype;
+  c.nmat = 1;
+  c.qs[0] = c.qs[1] = qs;
+  c.d[0] = c.d[1] = d;
+  c.rows = rows;
+  c.cols = cols;
+  c.n_rows = n_rows;
+  c.X = x;
+  c.ldx = cols;
+  c.ncols = 1;
+  c.Y = nullptr;
+  c.ldy = 0;
+  c.epi = EPI_TOPK;
+  c.out_idx = out_idx;
+  c.out_val = out_val;
+  c.topk = k;
   c.ws = ws;
   c.ws_bytes = ws_bytes;
   c.stream = (hipStream_t)stream;

@@ -75,6 +75,8 @@ struct DotArgs {
   uint32_t *gcnt;     // argmax: one counter
   float *cand_v;      // argmax: [G]
   int32_t *cand_i;
+  uint64_t *cand_k;   // top-k: [G][topk] rank keys of each row group's best rows
+  int topk;
   int32_t *out_idx;
   float *out_val;
   uint32_t *ready;    // fused FFN: one flag per h row tile, raised by its producer unit
@@ -495,7 +497,7 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   auto emit = [&](int t, int c, const float (&v)[NMAT]) {
     const int64_t row = (rt_base + t) * 16 + r;
     if (rt_base + t >= a.NT || row >= a.rows || c >= a.ncols) return;
-    if constexpr (EPI == EPI_ARGMAX) {
+    if constexpr (EPI == EPI_ARGMAX || EPI == EPI_TOPK) {
       if (ranks_before(v[0], (int32_t)row, bv, bi)) { bv = v[0]; bi = (int32_t)row; }
     } else {
       float *yp = a.Y + (int64_t)(a.ymap ? a.ymap[c] : c) * a.ldy + row;

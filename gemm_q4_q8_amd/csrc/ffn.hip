@@ -47,8 +47,11 @@ struct FfnArgs {
 
 // Waves per workgroup: 16 (Q4_0), 12 (Q8_0, whose units need more than the
 // 128 registers a wave of a 16-wave workgroup may hold).
+#ifndef FFN_WQ4
+#define FFN_WQ4 16
+#endif
 template <int QT>
-constexpr int ffn_waves() { return QT == Q4 ? 16 : 12; }
+constexpr int ffn_waves() { return QT == Q4 ? FFN_WQ4 : 12; }
 
 template <int QT, int PFA, int PFB>
 __global__ void __launch_bounds__(ffn_waves<QT>() * 64) ffn_kernel(FfnArgs f) {

@@ -9,7 +9,7 @@
 
 namespace qg {
 
-enum Epi { EPI_STORE = 0, EPI_ACC = 1, EPI_SILU = 2, EPI_ARGMAX = 3 };
+enum Epi { EPI_STORE = 0, EPI_ACC = 1, EPI_SILU = 2, EPI_ARGMAX = 3, EPI_TOPK = 4 };
 
 // One launch of the tiled product kernel.
 struct QmvCall {
@@ -25,8 +25,9 @@ struct QmvCall {
   float *Y;
   int64_t ldy;
   int epi;
-  int32_t *out_idx;         // argmax
+  int32_t *out_idx;         // argmax (1), top-k (topk)
   float *out_val;
+  int topk;                 // top-k: candidates wanted, 1..QG_TOPK_MAX
   void *ws;
   size_t ws_bytes;
   hipStream_t stream;
@@ -50,7 +51,7 @@ int gemm16_splits(int64_t rows, int64_t cols);
 // workspace can serve calls of any shape in stream order.
 constexpr size_t WS_SYNC_WORDS = QG_WS_SYNC_BYTES / 4;
 
-size_t qmv_ws_bytes(int64_t rows, int64_t cols, int slots, int nmat, int ncols_max, bool argmax);
+size_t qmv_ws_bytes(int64_t rows, int64_t cols, int slots, int nmat, int ncols_max, bool argmax, int topk = 0);
 
 int launch_qmv(const QmvCall &c);  // returns 0 or a QG_ status
 int launch_repack(int qtype, int64_t n_mat, int64_t rows, int64_t cols, const void *blocks,

@@ -45,6 +45,110 @@ __global__ void __launch_bounds__(WMAX * 64) dot_kernel(DotArgs a) {
   int32_t bi = 0x7fffffff;
   const bool emitted = dot_unit<QT, NC, NMAT, EPI, RT, PF, WKT, PH_PLAIN, MF>(a, g, s, smem, &flag, bv, bi);
 
+  if constexpr (EPI == EPI_TOPK) {
+    if (!emitted) return;
+    // ---- the k best rows of this row group: each emitting lane holds one
+    // row (bv, bi), the others none; rank keys (value descending, index
+    // ascending; 0 = none), k rounds of a wave maximum in wave 0
+    __shared__ uint64_t s_key[WMAX * 64];
+    const int k = a.topk;
+    s_key[tid] = bi != 0x7fffffff ? rank_key(bv, bi) : 0;
+    __syncthreads();
+    if (wk == 0) {
+      uint64_t key[WMAX];
+      uint64_t loc = 0;
+#pragma unroll
+      for (int j = 0; j < WMAX; ++j) {
+        key[j] = j < NW ? s_key[lane + 64 * j] : 0;
+        loc = key[j] > loc ? key[j] : loc;
+      }
+      uint64_t mine = 0;  // lane kk: the key of rank kk
+      for (int kk = 0; kk < k; ++kk) {
+        const uint64_t w = wave_max_u64(loc);
+        if (lane == kk) mine = w;
+        if (w != 0 && loc == w) {  // the owner drops the winner
+          loc = 0;
+#pragma unroll
+          for (int j = 0; j < WMAX; ++j) {
+            if (key[j] == w) key[j] = 0;
+            loc = key[j] > loc ? key[j] : loc;
+          }
+        }
+      }
+      if (lane < k) st_agent_u64(a.cand_k + (int64_t)g * k + lane, mine);
+    }
+    if (!arrive_last(a.gcnt, (uint32_t)a.G, &flag)) return;
+    // ---- merge of the G * k candidates.  Each thread keeps the best
+    // QG_TOPK_MAX of its share, sorted (an exchange chain per candidate;
+    // candidates loaded 8 at a time with coherent loads over a bounded
+    // range, slots past the end read 0 = none) ...
+    const int64_t nc = (int64_t)a.G * k;
+    uint64_t top[QG_TOPK_MAX];
+#pragma unroll
+    for (int j = 0; j < QG_TOPK_MAX; ++j) top[j] = 0;
+    const __amdgpu_buffer_rsrc_t rk = buf_range(a.cand_k, (uint32_t)(nc * 8));
+    for (int64_t q0 = tid; q0 < nc; q0 += 8 * NTHR) {
+      uint64_t v[8];
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const int64_t q = q0 + (int64_t)b * NTHR;
+        const u2 p = __builtin_amdgcn_raw_buffer_load_b64(rk, q < nc ? (uint32_t)(q * 8) : 0xFFFFFFC0u, 0, 16);
+        v[b] = ((uint64_t)p[1] << 32) | p[0];
+      }
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        uint64_t c = v[b];
+#pragma unroll
+        for (int j = 0; j < QG_TOPK_MAX; ++j) {
+          const uint64_t hi = c > top[j] ? c : top[j];
+          c = c > top[j] ? top[j] : c;
+          top[j] = hi;
+        }
+      }
+    }
+    // ... each wave takes its k best heads (the owner of a head pops it) ...
+    __syncthreads();  // s_key is reused
+    for (int kk = 0; kk < k; ++kk) {
+      const uint64_t w = wave_max_u64(top[0]);
+      if (lane == 0) s_key[wk * QG_TOPK_MAX + kk] = w;
+      if (w != 0 && top[0] == w) {
+#pragma unroll
+        for (int j = 0; j < QG_TOPK_MAX - 1; ++j) top[j] = top[j + 1];
+        top[QG_TOPK_MAX - 1] = 0;
+      }
+    }
+    __syncthreads();
+    // ... and wave 0 merges the waves' lists
+    if (wk == 0) {
+      constexpr int NJ = (WMAX * QG_TOPK_MAX + 63) / 64;
+      uint64_t key[NJ];
+      uint64_t loc = 0;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int e = lane + 64 * j;
+        key[j] = (e / QG_TOPK_MAX < NW && e % QG_TOPK_MAX < k) ? s_key[e] : 0;
+        loc = key[j] > loc ? key[j] : loc;
+      }
+      uint64_t mine = 0;
+      for (int kk = 0; kk < k; ++kk) {
+        const uint64_t w = wave_max_u64(loc);
+        if (lane == kk) mine = w;
+        if (w != 0 && loc == w) {
+          loc = 0;
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            if (key[j] == w) key[j] = 0;
+            loc = key[j] > loc ? key[j] : loc;
+          }
+        }
+      }
+      if (lane < k) {
+        a.out_idx[lane] = rank_key_index(mine);
+        if (a.out_val) a.out_val[lane] = rank_key_value(mine);
+      }
+    }
+  }
+
   if constexpr (EPI == EPI_ARGMAX) {
     if (!emitted) return;
     // ---- argmax of this row group, then of all row groups
@@ -178,11 +282,12 @@ int gemm16_splits(int64_t rows, int64_t cols) {
   return (int)s;
 }
 
-size_t qmv_ws_bytes(int64_t rows, int64_t cols, int slots, int nmat, int ncols_max, bool argmax) {
+size_t qmv_ws_bytes(int64_t rows, int64_t cols, int slots, int nmat, int ncols_max, bool argmax, int topk) {
   const int64_t NT = cdiv(rows, 16);
   (void)cols;
   size_t b = QG_WS_SYNC_BYTES;                      // counters
   if (argmax) b += 2 * align256((size_t)NT * 4);    // candidates
+  if (topk > 0) b += align256((size_t)NT * topk * 8);  // top-k candidates (row groups <= row tiles)
   if (slots > 1) b += (size_t)slots * nmat * NT * dot_part_floats(ncols_max) * 4;
   return b;
 }
@@ -244,6 +349,13 @@ static int launch_dot_t(const QmvCall &c, int S, int W = WKT, int SW = 1) {
   size_t off = QG_WS_SYNC_BYTES;
   a.cand_v = nullptr;
   a.cand_i = nullptr;
+  a.cand_k = nullptr;
+  a.topk = c.topk;
+  if (EPI == EPI_TOPK) {
+    if (c.topk < 1 || c.topk > QG_TOPK_MAX) return QG_ESHAPE;
+    a.cand_k = (uint64_t *)(ws + off);
+    off += align256((size_t)NT * c.topk * 8);
+  }
   if (EPI == EPI_ARGMAX) {
     a.cand_v = (float *)(ws + off);
     off += align256((size_t)NT * 4);
@@ -397,6 +509,9 @@ static int dispatch_qt(const QmvCall &c) {
     case EPI_ARGMAX:
       if (c.ncols != 1) return QG_ESHAPE;
       return launch_dot<QT, 1, 1, EPI_ARGMAX>(c, gemv_segments(c.rows, c.cols, 1, 1));
+    case EPI_TOPK:
+      if (c.ncols != 1) return QG_ESHAPE;
+      return launch_dot<QT, 1, 1, EPI_TOPK>(c, gemv_segments(c.rows, c.cols, 1, 1));
   }
   return QG_EINVAL;
 }

@@ -63,6 +63,9 @@ extern "C" {
 /* Bytes of counters at the start of every workspace (see Conventions). */
 #define QG_WS_SYNC_BYTES 262144u
 
+/* Largest k of lmhead_topk. */
+#define QG_TOPK_MAX 16
+
 /* GGUF tensor type ids, so a GGUF reader can pass them through. */
 enum { QG_Q4_0 = 2, QG_Q8_0 = 8 };
 
@@ -217,6 +220,26 @@ size_t qg_lmhead_ws_bytes(int64_t rows, int64_t cols);
 int lmhead_argmax(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols,
                   int64_t n_rows, const float *x, int32_t *out_idx, float *out_val,
                   void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * LM head + top-k candidates  [ARCH One token, end to end: greedy and top-k
+ * sampling on the GPU, a few bytes read back instead of the 1 MB logits;
+ * ENG Sampling, Fewer passes: GPU top-k, lowest-index ties; TJS Reduce
+ * sampling on the GPU: a small top-k on the GPU, the host finishes the
+ * draw from the candidates]
+ *
+ *   out_idx[j], out_val[j] (j < k): the k largest logits (W x)[r] over
+ *   r < n_rows, ordered by value descending, then row ascending.  Rows are
+ *   read as for lmhead_argmax; the logits never reach memory (each row
+ *   group keeps its k best, the last workgroup to finish merges them).
+ *   1 <= k <= min(QG_TOPK_MAX, n_rows), else QG_ESHAPE.  out_idx: k int32,
+ *   out_val: k floats or NULL, both device memory, 4-byte aligned.
+ * ------------------------------------------------------------------------ */
+size_t qg_lmhead_topk_ws_bytes(int64_t rows, int64_t cols, int32_t k);
+
+int lmhead_topk(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols,
+                int64_t n_rows, const float *x, int32_t k, int32_t *out_idx, float *out_val,
+                void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * MoE FFN  [ENG What it runs: 256 experts, 8 active per token, plus a shared

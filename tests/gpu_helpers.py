@@ -46,3 +46,22 @@ def check_routing(idx_gpu, w_gpu, res, top_k, hidden):
             assert np.array_equal(gi[sg], oi[so]), (t, gi, oi)
             assert np.all(np.abs(gw[sg] - ow[so]) <= 1e-5), (t, gw, ow)
     return int(np.sum(ordered))
+
+
+def check_topk_order(idx, val, want, ref, a, k_terms):
+    """GPU top-k against the oracle's when the error bound forces the set:
+    the same rows; values within the bound; the GPU's own list ordered by
+    its values (then rows); and the oracle's order wherever the bound
+    separates two of its rows."""
+    got = np.asarray(idx).astype(np.int64)
+    v = np.asarray(val).astype(np.float64)
+    assert sorted(got) == sorted(want)
+    assert np.all(np.abs(v - ref[got]) <= ops.tol_dot(a[got]))
+    assert all(v[i] > v[i + 1] or (v[i] == v[i + 1] and got[i] < got[i + 1]) for i in range(len(got) - 1))
+    gam = k_terms * ops.U32 / (1 - k_terms * ops.U32)
+    bound = (gam + ops.U16 * (1 + gam)) * a
+    pos = {int(r): i for i, r in enumerate(got)}
+    for i, ri in enumerate(want):
+        for rj in want[i + 1:]:
+            if ref[ri] - bound[ri] > ref[rj] + bound[rj]:
+                assert pos[int(ri)] < pos[int(rj)], (ri, rj)

@@ -25,7 +25,7 @@ def _declared():
 def test_every_declared_symbol_is_exported():
     names = _declared()
     assert {"qgemv_q4_0", "qgemv_q8_0", "qgemm16", "gateup_silu", "moe_ffn",
-            "lmhead_argmax", "qg_repack", "qg_packed_bytes"} <= set(names)
+            "lmhead_argmax", "lmhead_topk", "qg_repack", "qg_packed_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -125,6 +125,25 @@ def test_lmhead_checks():
     assert L.lmhead_argmax(2, FAKE, FAKE, 64, 128, 64, x, None, None, ws, 1 << 20, None) == EINVAL
     assert L.lmhead_argmax(2, FAKE, FAKE, 64, 128, 64, x, o + 2, None, ws, 1 << 20, None) == EALIGN
     assert L.lmhead_argmax(2, FAKE, FAKE, 64, 128, 64, x, o, None, ws, 4, None) == EWS
+
+
+def test_lmhead_topk_checks():
+    assert L.qg_lmhead_topk_ws_bytes(248320, 5120, 10) > 0
+    assert L.qg_lmhead_topk_ws_bytes(248320, 5120, 16) > L.qg_lmhead_topk_ws_bytes(248320, 5120, 10)
+    assert L.qg_lmhead_topk_ws_bytes(248320, 5120, 0) == 0
+    assert L.qg_lmhead_topk_ws_bytes(248320, 5120, 17) == 0
+    ws = FAKE + (3 << 20)
+    x, o = FAKE + (1 << 20), FAKE + (2 << 20)
+    big = 1 << 20
+    assert L.lmhead_topk(2, FAKE, FAKE, 64, 128, 64, x, 0, o, None, ws, big, None) == ESHAPE
+    assert L.lmhead_topk(2, FAKE, FAKE, 64, 128, 64, x, 17, o, None, ws, big, None) == ESHAPE
+    assert L.lmhead_topk(2, FAKE, FAKE, 64, 128, 8, x, 9, o, None, ws, big, None) == ESHAPE
+    assert L.lmhead_topk(2, FAKE, FAKE, 64, 128, 65, x, 4, o, None, ws, big, None) == ESHAPE
+    assert L.lmhead_topk(2, FAKE, FAKE, 64, 128, 64, x, 4, None, None, ws, big, None) == EINVAL
+    assert L.lmhead_topk(2, FAKE, FAKE, 64, 128, 64, x, 4, o + 2, None, ws, big, None) == EALIGN
+    assert L.lmhead_topk(2, FAKE, FAKE, 64, 128, 64, x, 4, o, o + 6, ws, big, None) == EALIGN
+    assert L.lmhead_topk(2, FAKE, FAKE, 64, 128, 64, x, 4, o, None, ws, 4, None) == EWS
+    assert L.lmhead_topk(5, FAKE, FAKE, 64, 128, 64, x, 4, o, None, ws, big, None) == EINVAL
 
 
 def test_ffn_fused_checks():

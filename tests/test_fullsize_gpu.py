@@ -19,7 +19,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import assert_tol, check_routing, host, say, up
+from gpu_helpers import assert_tol, check_routing, check_topk_order, host, say, up
 from oracle import ops
 
 pytestmark = pytest.mark.gpu
@@ -114,6 +114,55 @@ def test_lmhead_argmax_full_vocabulary(env):
             assert int(idx.item()) == ops.argmax_first(ref[:n, j]), (j, "prefix")
             checked_prefix += 1
     assert checked_prefix, "no certified draft prefix"
+
+
+def test_lmhead_topk_full_vocabulary(env):
+    """The full LM head.  Natural inputs: the largest k of 10 (the size the
+    Three.js page's example asks for), 8, 4 whose set the error bound forces
+    on one of 24 input columns.  Planted: the best row copied to 20 rows
+    spread over the vocabulary, each copy's block scales multiplied by 3,
+    3.25, 3.5, ..., so that k = 10 and k = 16 candidates come from many row
+    groups in a forced order."""
+    torch, qg, dev = env
+    N, K = 248320, 5120
+    say(f"LM head top-k Q8_0 {K}->{N}")
+    raw, W = matrix(env, Q8, N, K, 51)
+    X = np.concatenate([synth.gen_x(K, 8, cfg_id=synth.CFG_PREFILL), synth.gen_x(K, 16, cfg_id=61)], axis=1)
+    ref, a = ops.gemv(Q8, raw, X)
+    found = None
+    for k in (10, 8, 4):
+        for j in range(X.shape[1]):
+            if ops.topk_certified(ref[:, j], a[:, j], k, K + 64, ops.U16):
+                found = (k, j)
+                break
+        if found:
+            break
+    assert found, "no certified column"
+    k, j = found
+    say(f"  natural inputs: k = {k}, column {j}")
+    idx, val = qg.lmhead_topk(W, up(env, X[:, j]), k)
+    torch.cuda.synchronize()
+    check_topk_order(host(idx), host(val), ops.topk_lowest_index(ref[:, j], k), ref[:, j], a[:, j], K + 64)
+    del W
+    x = X[:, 0]
+    best = ops.argmax_first(ref[:, 0])
+    rows = np.linspace(3, N - 1, 20).astype(np.int64)
+    src = raw[best].copy()
+    for i, r in enumerate(rows):
+        blk = src.copy()
+        d = blk[:, 0:2].copy().view(np.float16)
+        blk[:, 0:2] = (d.astype(np.float32) * np.float32(3.0 + 0.25 * i)).astype(np.float16).view(np.uint8)
+        raw[r] = blk
+    W = qg.qg_repack(Q8, up(env, raw.reshape(-1)), N, K)
+    ref, a = ops.gemv(Q8, raw, x)
+    for k in (10, 16):
+        assert ops.topk_certified(ref, a, k, K + 64, ops.U16, order=True)
+        idx, val = qg.lmhead_topk(W, up(env, x), k)
+        torch.cuda.synchronize()
+        want = ops.topk_lowest_index(ref, k)
+        assert set(int(r) for r in want) <= set(int(r) for r in rows)
+        check_topk_order(host(idx), host(val), want, ref, a, K + 64)
+        assert list(host(idx).astype(np.int64)) == list(want)
 
 
 @pytest.fixture(scope="module")

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import assert_tol, check_routing, host, say, up
+from gpu_helpers import assert_tol, check_routing, check_topk_order, host, say, up
 from oracle import ops, quant
 
 pytestmark = pytest.mark.gpu
@@ -231,6 +231,87 @@ def test_lmhead_argmax_certified(env, qtype, rows, cols):
     i = int(idx.item())
     assert i == ops.argmax_first(ref)
     assert abs(val.item() - ref[i]) <= ops.tol_dot(a[i])
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("rows,cols,k", [(40, 416, 1), (40, 416, 16), (16, 128, 16), (1000, 512, 10),
+                                         (70000, 1024, 16)])
+def test_lmhead_topk_certified(env, qtype, rows, cols, k):
+    """The k candidates, in order, against the oracle on inputs whose order
+    the error bound forces (k = 1 is the argmax; k = rows sorts them all)."""
+    torch, qg, dev = env
+    say(f"lmhead topk qtype={qtype} {rows}x{cols} k={k}")
+    raw, W = _lm_case(env, qtype, rows, cols, seed=rows + k)
+    for s in range(40):
+        x = synth.gen_x(cols, 1, cfg_id=2000 + s)[:, 0]
+        want, _, ref, a = ops.lmhead_topk(qtype, raw, x, rows, k)
+        if ops.topk_certified(ref, a, k, cols + 64, ops.U16):
+            break
+    else:
+        pytest.fail("no certified seed")
+    idx, val = qg.lmhead_topk(W, up(env, x), k)
+    torch.cuda.synchronize()
+    check_topk_order(host(idx), host(val), want, ref, a, cols + 64)
+    if k == 1:
+        i, _ = qg.lmhead_argmax(W, up(env, x))
+        assert int(i.item()) == int(host(idx)[0])
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+def test_lmhead_topk_ties_and_prefix(env, qtype):
+    """Copies of a top row in other tiles and row groups tie exactly: they
+    follow in row order.  Row prefixes (rows < n_rows only) and k = n_rows."""
+    torch, qg, dev = env
+    rows, cols, k = 5000, 512, 6
+    raw = synth.gen_weights(qtype, rows, cols, SIG[qtype], np.random.default_rng(6))
+    plant = (17, 4099, rows - 1)
+    for s in range(40):
+        x = synth.gen_x(cols, 1, cfg_id=75 + s)[:, 0]
+        ref, a = ops.gemv(qtype, raw, x)
+        top = int(ops.topk_lowest_index(ref, 2)[1])   # the second best row gets the copies
+        if top not in plant and ops.topk_certified(ref, a, k, cols + 64, ops.U16, order=True):
+            break
+    else:
+        pytest.fail("no certified seed")
+    for where in plant:
+        raw[where] = raw[top]
+        ref[where], a[where] = ref[top], a[top]
+    W = qg.qg_repack(qtype, up(env, raw.reshape(-1)), rows, cols)
+    xd = up(env, x)
+    copies = np.array(sorted(set(plant + (top,))))
+
+    def check(n_rows, kk):
+        want = ops.topk_lowest_index(ref[:n_rows], kk)
+        # certify with each group of bitwise-identical rows counted once
+        keep = np.ones(n_rows, bool)
+        c = copies[copies < n_rows]
+        if len(c):
+            keep[c] = False
+            keep[c[0]] = True
+        sub = np.flatnonzero(keep)
+        kk_sub = len(set(want) - set(c[1:]))
+        if not ops.topk_certified(ref[sub], a[sub], min(kk_sub, len(sub)), cols + 64, ops.U16, order=True):
+            return False
+        idx, _ = qg.lmhead_topk(W, xd, kk, n_rows=n_rows)
+        assert list(host(idx).astype(np.int64)) == list(want), (n_rows, kk)
+        return True
+
+    assert check(rows, k)
+    got = list(host(qg.lmhead_topk(W, xd, k)[0]))
+    pos = [got.index(r) for r in copies if r in got]
+    assert pos == sorted(pos) and len(pos) == len(copies)
+    checked = sum(check(n, k) for n in (k, 17, 18, 4099, 4100, rows - 1)) + check(12, 12)
+    assert checked >= 3
+
+
+def test_lmhead_topk_rejects(env):
+    torch, qg, dev = env
+    raw, W = _lm_case(env, Q8, 40, 416, seed=3)
+    xd = up(env, synth.gen_x(416, 1, cfg_id=9)[:, 0])
+    for k, n_rows in ((0, 40), (17, 40), (8, 7)):
+        with pytest.raises(qg.QGError) as e:
+            qg.lmhead_topk(W, xd, k, n_rows=n_rows)
+        assert e.value.status == -2
 
 
 @pytest.mark.parametrize("qtype", [Q4, Q8])
