@@ -80,23 +80,27 @@ __global__ void __launch_bounds__(WMAX * 64) dot_kernel(DotArgs a) {
     if (!arrive_last(a.gcnt, (uint32_t)a.G, &flag)) return;
     // ---- merge of the G * k candidates.  Each thread keeps the best
     // QG_TOPK_MAX of its share, sorted (an exchange chain per candidate;
-    // candidates loaded 8 at a time with coherent loads over a bounded
+    // candidates loaded TKB at a time with coherent loads over a bounded
     // range, slots past the end read 0 = none) ...
     const int64_t nc = (int64_t)a.G * k;
     uint64_t top[QG_TOPK_MAX];
 #pragma unroll
     for (int j = 0; j < QG_TOPK_MAX; ++j) top[j] = 0;
     const __amdgpu_buffer_rsrc_t rk = buf_range(a.cand_k, (uint32_t)(nc * 8));
-    for (int64_t q0 = tid; q0 < nc; q0 += 8 * NTHR) {
-      uint64_t v[8];
+#ifndef TOPK_BATCH
+#define TOPK_BATCH 16
+#endif
+    constexpr int TKB = TOPK_BATCH;
+    for (int64_t q0 = tid; q0 < nc; q0 += TKB * NTHR) {
+      uint64_t v[TKB];
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
+      for (int b = 0; b < TKB; ++b) {
         const int64_t q = q0 + (int64_t)b * NTHR;
         const u2 p = __builtin_amdgcn_raw_buffer_load_b64(rk, q < nc ? (uint32_t)(q * 8) : 0xFFFFFFC0u, 0, 16);
         v[b] = ((uint64_t)p[1] << 32) | p[0];
       }
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
+      for (int b = 0; b < TKB; ++b) {
         uint64_t c = v[b];
 #pragma unroll
         for (int j = 0; j < QG_TOPK_MAX; ++j) {
