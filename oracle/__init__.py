@@ -10,7 +10,7 @@ What it computes, in float64, from the canonical GGUF block bytes:
 * `quant`  - Q4_0 / Q8_0 block decoding by the block definition, dense
   dequantisation, and the byte image of the library's repacked layout
   written out from that layout's definition.
-* `ops`    - y = W x (and y += W x), the fused gate/up SiLU, LM-head argmax
+* `ops`    - y = W x (and y += W x), RMSNorm, the fused gate/up SiLU, LM-head argmax
   and LM-head top-k candidates with lowest-index ties, router top-k,
   softmax, the MoE FFN, and the tolerances and argmax / top-k certification
   used by the parity tests.

@@ -93,6 +93,23 @@ def silu(g: np.ndarray) -> np.ndarray:
     return out
 
 
+# --------------------------------------------------------------------------
+# RMSNorm.  "Running LLMs in the browser with Three.js", the Llama-style
+# differences (RMSNorm: the root mean square, no mean subtracted) and
+# "Architecture", one token end to end (the final RMSNorm before the head);
+# "Engine and kernels", the norm fused into the router (kept) and into the
+# GEMV (measured slower on Metal).  Reading: n(x)[k] = x[k] * gamma[k] /
+# sqrt(mean_k x[k]^2 + eps) per column, eps given by the caller.
+# --------------------------------------------------------------------------
+def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """x: [K] or [K, C]; gamma: [K].  float64."""
+    x = np.asarray(x, dtype=np.float64)
+    g = np.asarray(gamma, dtype=np.float64)
+    ms = np.mean(x * x, axis=0)
+    inv = 1.0 / np.sqrt(ms + float(eps))
+    return (x * inv) * (g if x.ndim == 1 else g[:, None])
+
+
 def gateup_silu(qtype: int, g_raw: np.ndarray, u_raw: np.ndarray, x: np.ndarray):
     """Returns (h, tol_h, g, u) float64, shapes [F] or [F, C]."""
     g, ag = gemv(qtype, g_raw, x)

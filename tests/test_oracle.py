@@ -266,6 +266,36 @@ def test_lmhead_topk_by_brute_force():
     assert pos[1] < pos[4] < pos[5] and pos[5] == pos[1] + 2
 
 
+def test_rmsnorm_by_definition_and_closed_forms():
+    """n(x) = x * gamma / sqrt(mean(x^2) + eps): an explicit loop with exact
+    rational arithmetic before the one square root; a constant column c gives
+    gamma * c / sqrt(c^2 + eps); with eps = 0 the result does not change when
+    x is scaled by any a > 0 and has root mean square 1 for gamma = 1; columns
+    are independent."""
+    from fractions import Fraction
+    import math
+    g = np.random.default_rng(16)
+    K = 48
+    x = (g.integers(-64, 65, K) / 16.0).astype(np.float64)
+    gam = (g.integers(1, 9, K) / 4.0).astype(np.float64)
+    eps = 2.0 ** -10
+    ms = sum(Fraction(float(v)) ** 2 for v in x) / K + Fraction(eps)
+    inv = 1.0 / math.sqrt(float(ms))
+    want = [float(Fraction(float(v)) * Fraction(float(gg))) * inv for v, gg in zip(x, gam)]
+    assert np.allclose(ops.rmsnorm(x, gam, eps), want, rtol=4e-16, atol=0)
+    c = 3.0
+    assert np.allclose(ops.rmsnorm(np.full(K, c), gam, eps), gam * c / np.sqrt(c * c + eps), rtol=1e-15)
+    assert np.allclose(ops.rmsnorm(-np.full(K, c), gam, eps), -gam * c / np.sqrt(c * c + eps), rtol=1e-15)
+    one = np.ones(K)
+    n0 = ops.rmsnorm(x, one, 0.0)
+    assert np.allclose(ops.rmsnorm(7.5 * x, one, 0.0), n0, rtol=1e-14)
+    assert abs(np.sqrt(np.mean(n0 * n0)) - 1.0) < 1e-14
+    X = np.stack([x, 2 * x[::-1], np.full(K, -0.5)], axis=1)
+    N = ops.rmsnorm(X, gam, eps)
+    for j in range(3):
+        assert np.array_equal(N[:, j], ops.rmsnorm(X[:, j], gam, eps))
+
+
 def test_softmax_properties():
     g = np.random.default_rng(14)
     v = g.standard_normal(8)
