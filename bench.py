@@ -126,9 +126,23 @@ def run_ffn(B, steps, warmup):
     t_fused, _ = B.graph_time([lambda i=i: qg.ffn_fused(pg[i], pu[i], pd[i], xv, yv, hv) for i in range(n)], 4 * n)
     t_gu, _ = B.graph_time([lambda i=i: qg.gateup_silu(pg[i], pu[i], x, h) for i in range(n)], 4 * n)
     t_dn, _ = B.graph_time([lambda i=i: qg.qgemv(pd[i], h, y, accumulate=True) for i in range(n)], 4 * n)
+    # RMSNorm ahead of gate/up: folded into the call, and as its own launch
+    # first (the same algorithmic bytes: weights, x, gamma, h)
+    gam = B.up(synth.rng(3, K).uniform(0.5, 1.5, K).astype(np.float32))
+    xn = torch.empty_like(x)
+    t_gun, _ = B.graph_time([lambda i=i: qg.gateup_silu_rmsnorm(pg[i], pu[i], x, gam, 1e-6, h) for i in range(n)],
+                            4 * n)
+
+    def norm_then_gu(i):
+        qg.rmsnorm(x, gam, 1e-6, xn)
+        qg.gateup_silu(pg[i], pu[i], xn, h)
+
+    t_ngu, _ = B.graph_time([lambda i=i: norm_then_gu(i) for i in range(n)], 4 * n)
+    norm = {"gateup_rmsnorm_fused_q4_0_5120to2x17408": (gu_bytes + 4 * K, t_gun),
+            "rmsnorm_then_gateup_q4_0_5120to2x17408": (gu_bytes + 4 * K, t_ngu)}
     raws = (graw, uraw, draw)
     del pg, pu, pd
-    return step_bytes, t_step, gu_bytes, t_gu, dn_bytes, t_dn, raws, t_fused
+    return step_bytes, t_step, gu_bytes, t_gu, dn_bytes, t_dn, raws, t_fused, norm
 
 
 def run_extras(B, kernels):
@@ -346,13 +360,15 @@ def main():
         return
 
     log("bench: decode FFN step")
-    step_bytes, t_step, gu_bytes, t_gu, dn_bytes, t_dn, raws, t_fused = run_ffn(B, args.steps, args.warmup)
+    step_bytes, t_step, gu_bytes, t_gu, dn_bytes, t_dn, raws, t_fused, norm = run_ffn(B, args.steps, args.warmup)
     value = step_bytes / t_step / 1e9
     kernels = {
         "gateup_silu_q4_0_5120to2x17408": kernel_entry(gu_bytes, t_gu),
         "qgemv_q4_0_17408to5120_acc": kernel_entry(dn_bytes, t_dn),
         "ffn_fused_q4_0_5120x17408": kernel_entry(step_bytes, t_fused),
     }
+    for nm, (nb, tt) in norm.items():
+        kernels[nm] = kernel_entry(nb, tt)
     copy_gbs, read_gbs, read100_gbs = ceilings(B)
     if args.suite == "all":
         log("bench: other workloads")

@@ -68,6 +68,9 @@ _SIGS = {
                                  _vp, _sz, _vp]),
     "gateup_silu": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _i32,
                                    _vp, _i64, _vp, _sz, _vp]),
+    "gateup_silu_rmsnorm": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _i32,
+                                           _vp, ctypes.c_float, _vp, _i64, _vp, _sz, _vp]),
+    "qg_rmsnorm": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, ctypes.c_float, _vp, _i64, _vp]),
     "qg_lmhead_ws_bytes": (_sz, [_i64, _i64]),
     "qg_lmhead_topk_ws_bytes": (_sz, [_i64, _i64, _i32]),
     "lmhead_topk": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp,
@@ -238,6 +241,37 @@ def gateup_silu(wg: QMatrix, wu: QMatrix, X, H=None):
                            H2.data_ptr(), _ld(H2), ws.data_ptr(), ws.numel(),
                            _stream(X.device)), "gateup_silu")
     return H
+
+
+def gateup_silu_rmsnorm(wg: QMatrix, wu: QMatrix, X, gamma, eps: float, H=None):
+    """H[j] = silu(Wg n(X[j])) * (Wu n(X[j])), n = RMSNorm with weights gamma
+    (cols floats) and eps, folded into the gate/up call."""
+    torch = _torch()
+    _check_dev(X, gamma)
+    X2 = X if X.dim() == 2 else X.view(1, -1)
+    ncols = X2.shape[0]
+    if H is None:
+        H = torch.empty((ncols, wg.rows), dtype=torch.float32, device=X.device)
+    H2 = H if H.dim() == 2 else H.view(1, -1)
+    ws = workspace(lib.qg_gateup_ws_bytes(wg.rows, wg.cols), X.device)
+    _check(lib.gateup_silu_rmsnorm(wg.qtype, wg.qs.data_ptr(), wg.d.data_ptr(), wu.qs.data_ptr(),
+                                   wu.d.data_ptr(), wg.rows, wg.cols, X2.data_ptr(), _ld(X2), ncols,
+                                   gamma.data_ptr(), float(eps), H2.data_ptr(), _ld(H2), ws.data_ptr(),
+                                   ws.numel(), _stream(X.device)), "gateup_silu_rmsnorm")
+    return H
+
+
+def rmsnorm(X, gamma, eps: float, Y=None):
+    """Y[j] = X[j] * gamma / sqrt(mean(X[j]^2) + eps); X: [ncols, cols]; Y may be X."""
+    torch = _torch()
+    _check_dev(X, gamma)
+    X2 = X if X.dim() == 2 else X.view(1, -1)
+    if Y is None:
+        Y = torch.empty_like(X2)
+    Y2 = Y if Y.dim() == 2 else Y.view(1, -1)
+    _check(lib.qg_rmsnorm(X2.data_ptr(), _ld(X2), X2.shape[1], X2.shape[0], gamma.data_ptr(), float(eps),
+                          Y2.data_ptr(), _ld(Y2), _stream(X.device)), "qg_rmsnorm")
+    return Y
 
 
 def ffn_fused(wg: QMatrix, wu: QMatrix, wd: QMatrix, x, y, h=None):

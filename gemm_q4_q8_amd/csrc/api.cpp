@@ -181,9 +181,45 @@ int qgemm16(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols
   return qmv_common(qtype, qs, d, rows, cols, X, ldx, 16, Y, ldy, accumulate, ws, ws_bytes, stream, true);
 }
 
+static int gateup_common(int qtype, const void *g_qs, const void *g_d, const void *u_qs, const void *u_d,
+                         int64_t rows, int64_t cols, const float *X, int64_t ldx, int32_t ncols,
+                         const float *gamma, float eps, float *H, int64_t ldh, void *ws, size_t ws_bytes,
+                         void *stream);
+
 int gateup_silu(int qtype, const void *g_qs, const void *g_d, const void *u_qs, const void *u_d,
                 int64_t rows, int64_t cols, const float *X, int64_t ldx, int32_t ncols, float *H,
                 int64_t ldh, void *ws, size_t ws_bytes, void *stream) {
+  return gateup_common(qtype, g_qs, g_d, u_qs, u_d, rows, cols, X, ldx, ncols, nullptr, 0.0f, H, ldh, ws,
+                       ws_bytes, stream);
+}
+
+int gateup_silu_rmsnorm(int qtype, const void *g_qs, const void *g_d, const void *u_qs, const void *u_d,
+                        int64_t rows, int64_t cols, const float *X, int64_t ldx, int32_t ncols,
+                        const float *gamma, float eps, float *H, int64_t ldh, void *ws, size_t ws_bytes,
+                        void *stream) {
+  if (!gamma) return QG_EINVAL;
+  if (!aligned(gamma, 16)) return QG_EALIGN;
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return QG_EINVAL;  // also rejects NaN
+  return gateup_common(qtype, g_qs, g_d, u_qs, u_d, rows, cols, X, ldx, ncols, gamma, eps, H, ldh, ws,
+                       ws_bytes, stream);
+}
+
+int qg_rmsnorm(const float *X, int64_t ldx, int64_t cols, int32_t ncols, const float *gamma, float eps, float *Y,
+               int64_t ldy, void *stream) {
+  if (!X || !Y || !gamma) return QG_EINVAL;
+  if (cols < 1 || ncols < 1 || ldx < cols || ldy < cols) return QG_ESHAPE;
+  if (!aligned(X, 4) || !aligned(Y, 4) || !aligned(gamma, 4)) return QG_EALIGN;
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return QG_EINVAL;
+  // y may be x itself (same columns), not a shifted copy of it
+  if (Y != X && overlap(span(X, ldx, cols, ncols), span(Y, ldy, cols, ncols))) return QG_EINVAL;
+  if (Y == X && ldy != ldx) return QG_EINVAL;
+  return launch_rmsnorm(X, ldx, cols, ncols, gamma, eps, Y, ldy, stream);
+}
+
+static int gateup_common(int qtype, const void *g_qs, const void *g_d, const void *u_qs, const void *u_d,
+                         int64_t rows, int64_t cols, const float *X, int64_t ldx, int32_t ncols,
+                         const float *gamma, float eps, float *H, int64_t ldh, void *ws, size_t ws_bytes,
+                         void *stream) {
   if (!qtype_ok(qtype)) return QG_EINVAL;
   int st = check_matrix(g_qs, g_d, rows, cols);
   if (st) return st;
@@ -211,6 +247,8 @@ int gateup_silu(int qtype, const void *g_qs, const void *g_d, const void *u_qs, 
   c.Y = H;
   c.ldy = ldh;
   c.epi = EPI_SILU;
+  c.gamma = gamma;
+  c.norm_eps = eps;
   c.ws = ws;
   c.ws_bytes = ws_bytes;
   c.stream = (hipStream_t)stream;

@@ -84,6 +84,8 @@ struct DotArgs {
   uint32_t *err;      // fused FFN: set when a wait gave up
   int NWU;            // waves of the unit (<= 0: every wave of the workgroup); the
                       // other waves only take part in its barriers
+  const float *gamma; // RMSNorm prologue: the weights (cols), and eps
+  float norm_eps;
   const int32_t *xmap, *ymap;  // MoE: column c reads X column xmap[c], writes Y column ymap[c]
   int64_t xspan;      // bytes of X the columns may read (0: the ncols columns)
 };
@@ -133,7 +135,11 @@ __device__ __forceinline__ void mfma_fence(float (&acc)[NI], const h8 (&A)[4], c
 }
 #undef QG_FENCE_IN
 
-// The unit (row group g, segment s) of the launch `a`.  Returns true when
+// The unit (row group g, segment s) of the launch `a`.  RMSN (gate/up,
+// units that stage all of K): the activations are RMS-normalised first, as
+// x * gamma staged, times 1 / sqrt(mean(x^2) + eps) per column applied to
+// the two products (the same value, since the products are linear in x).
+// Returns true when
 // this workgroup emitted the outputs of row group g (its only segment, or
 // the last of its segments to finish).  For the argmax epilogue, (bv, bi)
 // then hold each lane's best (value, row).  `staged` runs once the
@@ -141,7 +147,7 @@ __device__ __forceinline__ void mfma_fence(float (&acc)[NI], const h8 (&A)[4], c
 // fused FFN takes its next work unit there, so that round trip overlaps the
 // stream).
 template <int QT, int NC, int NMAT, int EPI, int RT, int PF, int WKT, int PH, bool MF = false,
-          class Hook = NoHook>
+          class Hook = NoHook, bool RMSN = false>
 __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t *smem, uint32_t *flag,
                                           float &bv, int32_t &bi, Hook staged = Hook()) {
   // WKT == 0: one row tile per wave of the workgroup as launched (at least
@@ -209,16 +215,54 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
     const bool ok = v < span && rel0 * TILE_BLOCKS + bl < nkt * TILE_BLOCKS && k < a.cols && c < a.ncols;
     return ok ? (uint32_t)((xc * a.ldx + k) * 4) : 0xFFFFFFC0u;
   };
-  auto x_ld = [&](int v, int rel0, int span, int64_t xc, u4 &lo, u4 &hi) {
-    const uint32_t o = x_off(v, rel0, span, xc);
-    lo = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, XAUX);
-    hi = __builtin_amdgcn_raw_buffer_load_b128(rx, o + 16u, 0, XAUX);
+  // RMSNorm: gamma over the same 8 k of a piece (its range: cols floats;
+  // a piece outside reads zeros), and per staged piece the sum of its 8
+  // squares, [column][piece along K], past the staged activations and the
+  // in-workgroup sums; then 1 / rms per column
+  static_assert(!RMSN || (!XS && EPI == EPI_SILU), "RMSNorm prologue: gate/up, staged whole");
+  const __amdgpu_buffer_rsrc_t rg = buf_range(a.gamma, RMSN ? (uint32_t)(a.cols * 4) : 0u);
+  const int npc = nkt * TILE_BLOCKS * 4;  // pieces of one column
+  float *ssq = (float *)(smem + (size_t)nkt * TILE_BLOCKS * NC * 64 +
+                         (SW > 1 ? (size_t)(SW - 1) * R * NMAT * RT * NI * 64 * 4 : 0));
+  float *inv_rms = ssq + (size_t)NC * npc;
+  struct XPiece {
+    u4 lo, hi, glo, ghi;
   };
-  auto x_put = [&](int v, int span, _Float16 *dst, const u4 &lo, const u4 &hi) {
+  auto x_ld = [&](int v, int rel0, int span, int64_t xc, XPiece &pc) {
+    const uint32_t o = x_off(v, rel0, span, xc);
+    pc.lo = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, XAUX);
+    pc.hi = __builtin_amdgcn_raw_buffer_load_b128(rx, o + 16u, 0, XAUX);
+    if constexpr (RMSN) {
+      const int qq = v & 3, bl = (v >> 2) / NC;
+      const int64_t k = ((int64_t)(kt0 + rel0) * TILE_BLOCKS + bl) * 32 + qq * 8;
+      const uint32_t og = o != 0xFFFFFFC0u ? (uint32_t)(k * 4) : 0xFFFFFFC0u;
+      pc.glo = __builtin_amdgcn_raw_buffer_load_b128(rg, og, 0, 0);
+      pc.ghi = __builtin_amdgcn_raw_buffer_load_b128(rg, og + 16u, 0, 0);
+    }
+  };
+  auto x_put = [&](int v, int span, _Float16 *dst, const XPiece &pc) {
     if (v < span) {
       const int qq = v & 3, c = (v >> 2) % NC, bl = (v >> 2) / NC;
-      *(h8 *)(dst + ((size_t)bl * XC + c) * 32 + qq * 8) =
-          cvt8(__builtin_bit_cast(float4, lo), __builtin_bit_cast(float4, hi));
+      float4 lo = __builtin_bit_cast(float4, pc.lo), hi = __builtin_bit_cast(float4, pc.hi);
+      if constexpr (RMSN) {
+        // the piece's squares in k order, then x * gamma
+        float q = lo[0] * lo[0];
+        q = __builtin_fmaf(lo[1], lo[1], q);
+        q = __builtin_fmaf(lo[2], lo[2], q);
+        q = __builtin_fmaf(lo[3], lo[3], q);
+        q = __builtin_fmaf(hi[0], hi[0], q);
+        q = __builtin_fmaf(hi[1], hi[1], q);
+        q = __builtin_fmaf(hi[2], hi[2], q);
+        q = __builtin_fmaf(hi[3], hi[3], q);
+        ssq[(size_t)c * npc + bl * 4 + qq] = q;
+        const float4 glo = __builtin_bit_cast(float4, pc.glo), ghi = __builtin_bit_cast(float4, pc.ghi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo[e] *= glo[e];
+          hi[e] *= ghi[e];
+        }
+      }
+      *(h8 *)(dst + ((size_t)bl * XC + c) * 32 + qq * 8) = cvt8(lo, hi);
     }
   };
 
@@ -257,13 +301,13 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   // ---- 1. start the weight stream, and (first round) the activations
   constexpr int X0 = XS ? XR : 1;
   const int span0 = XS ? CHV : nvec;
-  u4 xl[X0], xh[X0];
+  XPiece xp[X0];
   int64_t xcs[X0];
 #pragma unroll
   for (int i = 0; i < X0; ++i) xcs[i] = x_col(tid + i * NTHR);
   if constexpr (PH != PH_CONSUME) {
 #pragma unroll
-    for (int i = 0; i < X0; ++i) x_ld(tid + i * NTHR, 0, span0, xcs[i], xl[i], xh[i]);
+    for (int i = 0; i < X0; ++i) x_ld(tid + i * NTHR, 0, span0, xcs[i], xp[i]);
   }
 #pragma unroll
   for (int p = 0; p < PF; ++p) load(p, p);
@@ -287,7 +331,7 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < X0; ++i) x_ld(tid + i * NTHR, 0, span0, xcs[i], xl[i], xh[i]);
+    for (int i = 0; i < X0; ++i) x_ld(tid + i * NTHR, 0, span0, xcs[i], xp[i]);
   }
 
   // ---- 2. staging: f16 in LDS, [block][column][32] (XS: chunk 0 into
@@ -312,20 +356,32 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   constexpr int WAIT_X0 =
       (PH == PH_CONSUME || NMAT == 1) ? WAIT_ALL : (WAIT_ALL | (NWL & 15) | ((NWL >> 4) << 14));
 #pragma unroll
-  for (int i = 0; i < X0; ++i) x_put(tid + i * NTHR, span0, xs, xl[i], xh[i]);
+  for (int i = 0; i < X0; ++i) x_put(tid + i * NTHR, span0, xs, xp[i]);
   if constexpr (!XS) {
     __builtin_amdgcn_s_waitcnt(WAIT_X0);
     constexpr int XB = 4;
     for (int v0 = tid + NTHR; v0 < nvec; v0 += XB * NTHR) {
-      u4 lo[XB], hi[XB];
+      XPiece pc[XB];
 #pragma unroll
-      for (int b = 0; b < XB; ++b) x_ld(v0 + b * NTHR, 0, nvec, x_col(v0 + b * NTHR), lo[b], hi[b]);
+      for (int b = 0; b < XB; ++b) x_ld(v0 + b * NTHR, 0, nvec, x_col(v0 + b * NTHR), pc[b]);
 #pragma unroll
-      for (int b = 0; b < XB; ++b) x_put(v0 + b * NTHR, nvec, xs, lo[b], hi[b]);
+      for (int b = 0; b < XB; ++b) x_put(v0 + b * NTHR, nvec, xs, pc[b]);
       __builtin_amdgcn_s_waitcnt(WAIT_ALL);
     }
   }
   __syncthreads();
+  if constexpr (RMSN) {
+    // 1 / rms per column: lane l adds the column's pieces l, l + 64, ... in
+    // order, then a fixed wave tree, so every workgroup (and every column
+    // count) gets the same bits
+    for (int c = wk; c < NC; c += NTHR >> 6) {
+      float t = 0.0f;
+      for (int p = lane; p < npc; p += 64) t += ssq[(size_t)c * npc + p];
+      t = wave_sum(t);
+      if (lane == 0) inv_rms[c] = 1.0f / __builtin_sqrtf(t / (float)a.cols + a.norm_eps);
+    }
+    __syncthreads();
+  }
   staged();
 
   // ---- 3. stream the weight tiles of the segment
@@ -443,9 +499,9 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
     // every wave runs the same trip count: the chunk hand-over is a barrier
     const bool live = rt_base < a.NT;
     for (int k = 0; k < nkt; k += PF) {
-      u4 nl[XR], nh[XR];
+      XPiece np[XR];
 #pragma unroll
-      for (int i = 0; i < XR; ++i) x_ld(tid + i * NTHR, k + PF, CHV, xcs[i], nl[i], nh[i]);
+      for (int i = 0; i < XR; ++i) x_ld(tid + i * NTHR, k + PF, CHV, xcs[i], np[i]);
 #pragma unroll
       for (int p = 0; p < PF; ++p) {
         if (live && k + p < nkt) compute(p, k + p);
@@ -453,7 +509,7 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
       }
       _Float16 *nb = xs + (((k / PF) + 1) & 1) * CHH;
 #pragma unroll
-      for (int i = 0; i < XR; ++i) x_put(tid + i * NTHR, CHV, nb, nl[i], nh[i]);
+      for (int i = 0; i < XR; ++i) x_put(tid + i * NTHR, CHV, nb, np[i]);
       __syncthreads();
     }
   } else {
@@ -507,9 +563,13 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
       } else if constexpr (EPI == EPI_ACC) {
         out = *yp + v[0];
       } else {
-        const float gg = v[0];
+        float gg = v[0], uu = v[NMAT - 1];
+        if constexpr (RMSN) {
+          gg *= inv_rms[c];
+          uu *= inv_rms[c];
+        }
         const float sg = gg / (1.0f + expf(-gg));
-        out = sg * v[NMAT - 1];
+        out = sg * uu;
       }
       if constexpr (PH == PH_PRODUCE) st_agent(yp, out);
       else *yp = out;

@@ -28,6 +28,8 @@ struct QmvCall {
   int32_t *out_idx;         // argmax (1), top-k (topk)
   float *out_val;
   int topk;                 // top-k: candidates wanted, 1..QG_TOPK_MAX
+  const float *gamma;       // gate/up with an RMSNorm prologue: weights (cols), eps
+  float norm_eps;
   void *ws;
   size_t ws_bytes;
   hipStream_t stream;
@@ -72,6 +74,8 @@ size_t ffn_ws_bytes(int64_t hidden, int64_t ffn);
 int launch_ffn(const FfnCall &c);
 
 // Streaming-read probe (the bench's measured read ceiling).
+int launch_rmsnorm(const float *X, int64_t ldx, int64_t cols, int ncols, const float *gamma, float eps, float *Y,
+                   int64_t ldy, void *stream);
 int launch_read_probe(const void *p, size_t bytes, uint32_t *sink, void *stream);
 
 struct MoeCall {

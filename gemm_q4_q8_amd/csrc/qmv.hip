@@ -26,7 +26,7 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // --------------------------------------------------------------- dot path
 // WKT > 0: workgroups of WKT waves; WKT == 0: as many waves as launched, at
 // most WMAX (the launch planner picks the size per shape).
-template <int QT, int NC, int NMAT, int EPI, int RT, int PF, int WKT, bool MF, int WMAX>
+template <int QT, int NC, int NMAT, int EPI, int RT, int PF, int WKT, bool MF, int WMAX, bool RMSN = false>
 __global__ void __launch_bounds__(WMAX * 64) dot_kernel(DotArgs a) {
   static_assert(WKT <= WMAX, "workgroup size");
   const int NTHR = WKT > 0 ? WKT * 64 : (int)blockDim.x;
@@ -43,7 +43,8 @@ __global__ void __launch_bounds__(WMAX * 64) dot_kernel(DotArgs a) {
   const int g = (int)(u / a.S), s = (int)(u % a.S);
   float bv = __builtin_nanf("");  // argmax: this lane's best (value, row)
   int32_t bi = 0x7fffffff;
-  const bool emitted = dot_unit<QT, NC, NMAT, EPI, RT, PF, WKT, PH_PLAIN, MF>(a, g, s, smem, &flag, bv, bi);
+  const bool emitted =
+      dot_unit<QT, NC, NMAT, EPI, RT, PF, WKT, PH_PLAIN, MF, NoHook, RMSN>(a, g, s, smem, &flag, bv, bi);
 
   if constexpr (EPI == EPI_TOPK) {
     if (!emitted) return;
@@ -318,7 +319,7 @@ static int grant_lds(const void *kern, size_t lds, size_t &granted) {
 
 // S segments across workgroups; SW > 1: segments inside each workgroup
 // instead (S must then be 1), W = R * SW waves for R row tiles.
-template <int QT, int NC, int NMAT, int EPI, int RT, int PF, int WKT, bool MF, int WMAX = WKT>
+template <int QT, int NC, int NMAT, int EPI, int RT, int PF, int WKT, bool MF, int WMAX = WKT, bool RMSN = false>
 static int launch_dot_t(const QmvCall &c, int S, int W = WKT, int SW = 1) {
   const int64_t NT = cdiv(c.rows, 16), KT = cdiv(c.cols / 32, 4);
   const int64_t NTu = cdiv(c.n_rows, 16);  // row tiles actually produced
@@ -373,6 +374,10 @@ static int launch_dot_t(const QmvCall &c, int S, int W = WKT, int SW = 1) {
   a.ready_n = 0;
   a.err = nullptr;
   a.NWU = 0;
+  a.gamma = RMSN ? c.gamma : nullptr;
+  a.norm_eps = c.norm_eps;
+  // the RMSNorm prologue needs every unit to stage all of K
+  if (RMSN && !(a.IL || S == 1)) return QG_EUNSUPPORTED;
   a.xmap = a.ymap = nullptr;
   a.xspan = 0;
   if (!ranges_fit(c, NT, KT, QTraits<QT>::tile_bytes)) return QG_EUNSUPPORTED;
@@ -387,8 +392,9 @@ static int launch_dot_t(const QmvCall &c, int S, int W = WKT, int SW = 1) {
   size_t lds = NC >= 16 ? (size_t)2 * PF * TILE_BLOCKS * NC * 64
                         : (size_t)(a.IL ? KT : cdiv(KT, S)) * TILE_BLOCKS * NC * 64;
   lds += (size_t)(SW - 1) * (W / SW) * NMAT * RT * (MF ? (NC < 4 ? NC : 4) : NC) * 64 * 4;
+  if (RMSN) lds += (size_t)NC * KT * TILE_BLOCKS * 4 * 4 + (size_t)NC * 4;  // squares per piece, 1/rms
   if (lds > LDS_HARD - 1024) return QG_EUNSUPPORTED;
-  auto kern = dot_kernel<QT, NC, NMAT, EPI, RT, PF, WKT, MF, WMAX>;
+  auto kern = dot_kernel<QT, NC, NMAT, EPI, RT, PF, WKT, MF, WMAX, RMSN>;
   static size_t granted = 65536;  // per instantiation; only ever raised
   int st = grant_lds((const void *)kern, lds, granted);
   if (st) return st;
@@ -414,7 +420,7 @@ static int dot_waves(int64_t NTu, int S) {
 
 // One row tile per wave, about 4 KiB of weights in flight per wave (PF tile
 // columns).
-template <int QT, int NC, int NMAT, int EPI>
+template <int QT, int NC, int NMAT, int EPI, bool RMSN = false>
 static int launch_dot(const QmvCall &c, int S) {
   constexpr int QW = QT == Q4 ? 1 : 2;
   constexpr int PF0 = 4 / (NMAT * QW);
@@ -443,10 +449,10 @@ static int launch_dot(const QmvCall &c, int S) {
     const int64_t cu_bytes = (int64_t)NMAT * R * KT * (QTraits<QT>::tile_bytes + TILE_D_BYTES);
     bool sw = R * S <= 16 && lds <= DOT_SW_LDS &&
               (dot_interleaved(c.cols) || 10 * u_sw >= 9 * u_cross || cu_bytes <= 196608);
-    if (sw) return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 16>(c, 1, (int)(R * S), S);
+    if (sw) return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 16, RMSN>(c, 1, (int)(R * S), S);
   }
-  if (W <= 8) return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 8>(c, S, W);
-  return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 16>(c, S, W);
+  if (W <= 8) return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 8, RMSN>(c, S, W);
+  return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 16, RMSN>(c, S, W);
 }
 
 template <int QT, int EPI>
@@ -464,19 +470,24 @@ static int dispatch_dot(const QmvCall &c, int S) {
   return QG_ESHAPE;
 }
 
-template <int QT>
-static int dispatch_silu(const QmvCall &c, int S) {
+template <int QT, bool RMSN>
+static int dispatch_silu_t(const QmvCall &c, int S) {
   switch (c.ncols) {
-    case 1: return launch_dot<QT, 1, 2, EPI_SILU>(c, S);
-    case 2: return launch_dot<QT, 2, 2, EPI_SILU>(c, S);
-    case 3: return launch_dot<QT, 3, 2, EPI_SILU>(c, S);
-    case 4: return launch_dot<QT, 4, 2, EPI_SILU>(c, S);
-    case 5: return launch_dot<QT, 5, 2, EPI_SILU>(c, S);
-    case 6: return launch_dot<QT, 6, 2, EPI_SILU>(c, S);
-    case 7: return launch_dot<QT, 7, 2, EPI_SILU>(c, S);
-    case 8: return launch_dot<QT, 8, 2, EPI_SILU>(c, S);
+    case 1: return launch_dot<QT, 1, 2, EPI_SILU, RMSN>(c, S);
+    case 2: return launch_dot<QT, 2, 2, EPI_SILU, RMSN>(c, S);
+    case 3: return launch_dot<QT, 3, 2, EPI_SILU, RMSN>(c, S);
+    case 4: return launch_dot<QT, 4, 2, EPI_SILU, RMSN>(c, S);
+    case 5: return launch_dot<QT, 5, 2, EPI_SILU, RMSN>(c, S);
+    case 6: return launch_dot<QT, 6, 2, EPI_SILU, RMSN>(c, S);
+    case 7: return launch_dot<QT, 7, 2, EPI_SILU, RMSN>(c, S);
+    case 8: return launch_dot<QT, 8, 2, EPI_SILU, RMSN>(c, S);
   }
   return QG_ESHAPE;
+}
+
+template <int QT>
+static int dispatch_silu(const QmvCall &c, int S) {
+  return c.gamma ? dispatch_silu_t<QT, true>(c, S) : dispatch_silu_t<QT, false>(c, S);
 }
 
 // 16 columns: the shared dot unit on the matrix cores (one row tile per

@@ -181,6 +181,33 @@ int gateup_silu(int qtype, const void *g_qs, const void *g_d, const void *u_qs,
                 void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * RMSNorm prologue  [TJS Llama-style differences: RMSNorm takes the root
+ * mean square, no mean subtracted; ENG: the norm fused ahead of the router
+ * (kept, +4-5% decode) and into the GEMV (0.91x on Metal: to be measured)]
+ *
+ *   n(X)[k, j] = X[k, j] * gamma[k] / sqrt(mean_k X[k, j]^2 + eps)
+ *
+ * gateup_silu_rmsnorm: H = gateup_silu of n(X), with the norm folded into
+ * the call: each workgroup stages X * gamma and multiplies both products of
+ * a column by that column's 1 / rms (the products are linear in X).  gamma:
+ * cols floats, device, 16-byte aligned; eps >= 0 and finite, else QG_EINVAL.
+ * Shapes whose K segments do not each stage all of K (cols > 5120 with more
+ * than one segment) return QG_EUNSUPPORTED.  Workspace: qg_gateup_ws_bytes.
+ * Column j is bitwise equal to a 1-column call on column j.
+ *
+ * qg_rmsnorm: Y = n(X) on its own (a workgroup per column); Y may be X itself
+ * (same ld), not a shifted overlap.  Its 1 / rms has the same bits as the
+ * fused form's (the squares are summed in the same order).
+ * ------------------------------------------------------------------------ */
+int gateup_silu_rmsnorm(int qtype, const void *g_qs, const void *g_d, const void *u_qs,
+                        const void *u_d, int64_t rows, int64_t cols, const float *X,
+                        int64_t ldx, int32_t ncols, const float *gamma, float eps, float *H,
+                        int64_t ldh, void *ws, size_t ws_bytes, void *stream);
+
+int qg_rmsnorm(const float *X, int64_t ldx, int64_t cols, int32_t ncols, const float *gamma,
+               float eps, float *Y, int64_t ldy, void *stream);
+
+/* ------------------------------------------------------------------------
  * Fused decode FFN, one token  [ENG Kernel families: fused gate/up with SiLU
  * applied before writing, and the residual epilogue y += W x]
  *

@@ -25,7 +25,8 @@ def _declared():
 def test_every_declared_symbol_is_exported():
     names = _declared()
     assert {"qgemv_q4_0", "qgemv_q8_0", "qgemm16", "gateup_silu", "moe_ffn",
-            "lmhead_argmax", "lmhead_topk", "qg_repack", "qg_packed_bytes"} <= set(names)
+            "lmhead_argmax", "lmhead_topk", "gateup_silu_rmsnorm", "qg_rmsnorm", "qg_repack",
+            "qg_packed_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -144,6 +145,34 @@ def test_lmhead_topk_checks():
     assert L.lmhead_topk(2, FAKE, FAKE, 64, 128, 64, x, 4, o, o + 6, ws, big, None) == EALIGN
     assert L.lmhead_topk(2, FAKE, FAKE, 64, 128, 64, x, 4, o, None, ws, 4, None) == EWS
     assert L.lmhead_topk(5, FAKE, FAKE, 64, 128, 64, x, 4, o, None, ws, big, None) == EINVAL
+
+
+def test_rmsnorm_checks():
+    X, Y, G = FAKE, FAKE + (1 << 20), FAKE + (2 << 20)
+    ws = FAKE + (3 << 20)
+    big = 1 << 22
+    gu = lambda gamma, eps, qt=2: L.gateup_silu_rmsnorm(qt, FAKE, FAKE, FAKE, FAKE, 64, 128, X, 128, 1, gamma, eps,
+                                                       Y, 64, ws, big, None)
+    assert gu(None, 1e-6) == EINVAL
+    assert gu(G + 4, 1e-6) == EALIGN
+    assert gu(G, -1.0) == EINVAL
+    assert gu(G, float("nan")) == EINVAL
+    assert gu(G, float("inf")) == EINVAL
+    assert gu(G, 1e-6, qt=5) == EINVAL
+    assert L.gateup_silu_rmsnorm(2, FAKE, FAKE, FAKE, FAKE, 64, 128, X, 128, 9, G, 1e-6, Y, 64, ws, big,
+                                 None) == ESHAPE
+    assert L.gateup_silu_rmsnorm(2, FAKE, FAKE, FAKE, FAKE, 64, 128, X, 128, 1, G, 1e-6, Y, 64, ws, 8,
+                                 None) == EWS
+    rn = L.qg_rmsnorm
+    assert rn(None, 128, 128, 1, G, 1e-6, Y, 128, None) == EINVAL
+    assert rn(X, 128, 128, 1, None, 1e-6, Y, 128, None) == EINVAL
+    assert rn(X, 128, 0, 1, G, 1e-6, Y, 128, None) == ESHAPE
+    assert rn(X, 100, 128, 1, G, 1e-6, Y, 128, None) == ESHAPE
+    assert rn(X, 128, 128, 0, G, 1e-6, Y, 128, None) == ESHAPE
+    assert rn(X + 2, 128, 128, 1, G, 1e-6, Y, 128, None) == EALIGN
+    assert rn(X, 128, 128, 1, G, -1e-6, Y, 128, None) == EINVAL
+    assert rn(X, 128, 128, 2, G, 1e-6, X + 64, 128, None) == EINVAL      # shifted overlap
+    assert rn(X, 128, 128, 2, G, 1e-6, X, 256, None) == EINVAL           # in place with another ld
 
 
 def test_ffn_fused_checks():

@@ -168,6 +168,65 @@ def test_gateup_parity(env, qtype, rows, cols, ncols):
     assert_tol(host(H).T, h, th, "gateup")
 
 
+# ------------------------------------------------------- RMSNorm prologue
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("rows,cols", [(40, 416), (64, 4096), (512, 2048), (300, 5120)])
+@pytest.mark.parametrize("ncols", [1, 3, 8])
+def test_gateup_rmsnorm_parity(env, qtype, rows, cols, ncols):
+    """gate/up of RMSNorm(X): against the oracle (norm in f64, then the
+    products), each column bitwise equal to a 1-column call, and the
+    stand-alone norm followed by gateup_silu within the same bound."""
+    torch, qg, dev = env
+    say(f"gateup rmsnorm qtype={qtype} {rows}x{cols} ncols={ncols}")
+    graw, G = make(env, qtype, rows, cols, seed=31 + cols)
+    uraw, U = make(env, qtype, rows, cols, seed=32 + cols)
+    X = synth.gen_x(cols, ncols, cfg_id=60 + ncols) * 3.0
+    gam = synth.rng(61, cols).uniform(-2.0, 2.0, cols).astype(np.float32)
+    eps = 1e-5
+    n = ops.rmsnorm(X.astype(np.float64), gam.astype(np.float64), eps)
+    hr, th, _, _ = ops.gateup_silu(qtype, graw, uraw, n)
+    gd = up(env, gam)
+    H = qg.gateup_silu_rmsnorm(G, U, up(env, X.T), gd, eps)
+    torch.cuda.synchronize()
+    assert_tol(host(H).T, hr, th, "h")
+    for j in range(ncols):
+        h1 = qg.gateup_silu_rmsnorm(G, U, up(env, X[:, j:j + 1].T), gd, eps)
+        assert torch.equal(h1[0], H[j]), j
+    Xn = qg.rmsnorm(up(env, X.T), gd, eps)
+    H2 = qg.gateup_silu(G, U, Xn)
+    assert_tol(host(H2).T, hr, th, "h via rmsnorm")
+
+
+@pytest.mark.parametrize("cols,ncols", [(128, 1), (416, 3), (5120, 8), (100, 2)])
+def test_rmsnorm_parity(env, cols, ncols):
+    """The stand-alone norm against the oracle (f32 bound: the squares' sum,
+    the square root and two products), in place as well."""
+    torch, qg, dev = env
+    X = synth.gen_x(cols, ncols, cfg_id=70 + cols) * 5.0
+    gam = synth.rng(71, cols).uniform(-2.0, 2.0, cols).astype(np.float32)
+    eps = 1e-6
+    ref = ops.rmsnorm(X.astype(np.float64), gam.astype(np.float64), eps)
+    Y = host(qg.rmsnorm(up(env, X.T), up(env, gam), eps)).T.astype(np.float64)
+    tol = (cols + 16) * 2.0 ** -24 * np.abs(ref) + 1e-30
+    assert np.all(np.abs(Y - ref) <= tol)
+    Xd = up(env, X.T)
+    qg.rmsnorm(Xd, up(env, gam), eps, Y=Xd)
+    assert np.array_equal(host(Xd).T.astype(np.float64), Y)
+
+
+def test_gateup_rmsnorm_unsupported_split(env):
+    """cols > 5120 with K split into contiguous segments across workgroups
+    (600 x 11264: 22 segments, too many for one workgroup): no unit stages
+    all of K, so the fused form refuses (QG_EUNSUPPORTED)."""
+    torch, qg, dev = env
+    _, G = make(env, Q4, 600, 11264, seed=5)
+    _, U = make(env, Q4, 600, 11264, seed=6)
+    with pytest.raises(qg.QGError) as e:
+        qg.gateup_silu_rmsnorm(G, U, up(env, synth.gen_x(11264, 1, cfg_id=3).T),
+                               up(env, np.ones(11264, np.float32)), 1e-6)
+    assert e.value.status == -4
+
+
 # --------------------------------------------------------------- fused FFN
 @pytest.mark.parametrize("qtype", [Q4, Q8])
 @pytest.mark.parametrize("H,F", [(256, 384), (416, 224), (512, 2048), (2048, 1024)])
