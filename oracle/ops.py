@@ -254,9 +254,13 @@ def moe_ffn(x: np.ndarray, router: np.ndarray, qtype: int,
             top_k: int, normalize: bool = True,
             sh_gate: Optional[np.ndarray] = None, sh_up: Optional[np.ndarray] = None,
             sh_down: Optional[np.ndarray] = None,
-            y_in: Optional[np.ndarray] = None):
+            y_in: Optional[np.ndarray] = None,
+            norm_w: Optional[np.ndarray] = None, norm_eps: float = 0.0):
     """x: [H, T]; router: [E, H] f32; gate/up raw: [E, F, H/32, B];
-    down raw: [E, H, F/32, B]; y_in: [H, T] or None.
+    down raw: [E, H, F/32, B]; y_in: [H, T] or None.  norm_w: with it, the
+    router and every expert read RMSNorm(x) (weights norm_w, eps norm_eps)
+    instead of x ("Engine and kernels": the norm fused ahead of the router);
+    the residual y is not normalised.
 
     Returns dict with y [H, T], tol [H, T], idx [T, k], p [T, k],
     logits [E, T], logit_a [E, T]."""
@@ -264,8 +268,14 @@ def moe_ffn(x: np.ndarray, router: np.ndarray, qtype: int,
     if x.ndim == 1:
         x = x[:, None]
     H, T = x.shape
+    if norm_w is not None:
+        x = rmsnorm(x, norm_w, norm_eps)
     logits, la = router_logits(x, router)       # [E, T]
     gam = (H + 2) * U32 / (1 - (H + 2) * U32)
+    if norm_w is not None:
+        # the norm's 1 / rms in f32 (sum of H squares, square root, division)
+        # scales every logit of a token: relative error (H + 8) u32 more
+        la = la + (H + 8) * U32 / gam * np.abs(logits)
     y = np.zeros((H, T)) if y_in is None else np.asarray(y_in, dtype=np.float64).reshape(H, T).copy()
     tol = np.full((H, T), ABS_TOL)
     idx = np.zeros((T, top_k), dtype=np.int64)

@@ -296,6 +296,33 @@ def test_rmsnorm_by_definition_and_closed_forms():
         assert np.array_equal(N[:, j], ops.rmsnorm(X[:, j], gam, eps))
 
 
+def test_moe_with_norm_invariants():
+    """The norm ahead of the MoE: with unit weights and eps = 0, scaling x by
+    any a > 0 changes nothing (router and experts both read the normalised
+    x); with unit weights the experts chosen are those of the plain layer
+    (1 / rms is one positive factor per token); and the result is the plain
+    layer applied to the normalised x, whose RMS is 1."""
+    g = np.random.default_rng(17)
+    E, H, F, k = 6, 64, 32, 2
+    router = (g.standard_normal((E, H)) * 0.1).astype(np.float32)
+    gate = np.stack([synth.gen_weights(Q4, F, H, 0.05, g) for _ in range(E)])
+    upw = np.stack([synth.gen_weights(Q4, F, H, 0.05, g) for _ in range(E)])
+    down = np.stack([synth.gen_weights(Q4, H, F, 0.05, g) for _ in range(E)])
+    x = g.standard_normal((H, 3)) * 4.0
+    one = np.ones(H)
+    r1 = ops.moe_ffn(x, router, Q4, gate, upw, down, top_k=k, norm_w=one, norm_eps=0.0)
+    r2 = ops.moe_ffn(2.5 * x, router, Q4, gate, upw, down, top_k=k, norm_w=one, norm_eps=0.0)
+    assert np.array_equal(r1["idx"], r2["idx"])
+    assert np.allclose(r1["y"], r2["y"], rtol=1e-12, atol=1e-14)
+    plain = ops.moe_ffn(x, router, Q4, gate, upw, down, top_k=k)
+    assert np.array_equal(r1["idx"], plain["idx"])
+    xn = x / np.sqrt(np.mean(x * x, axis=0))
+    assert np.allclose(np.sqrt(np.mean(xn * xn, axis=0)), 1.0, rtol=1e-14)
+    r3 = ops.moe_ffn(xn, router, Q4, gate, upw, down, top_k=k)
+    assert np.allclose(r1["y"], r3["y"], rtol=1e-12, atol=1e-14)
+    assert np.all(r1["logit_a"] >= ops.router_logits(xn, router)[1])
+
+
 def test_softmax_properties():
     g = np.random.default_rng(14)
     v = g.standard_normal(8)
