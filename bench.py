@@ -234,6 +234,23 @@ def run_extras(B, kernels):
         t, _ = B.graph_time([lambda m=m: qg.moe_ffn(m, X, Y) for m in moes], 4 * copies)
         kernels[f"moe_ffn_{T}tok"] = kernel_entry(nbytes, t, {"distinct_experts": U,
                                                              "tokens_per_s": round(T / t, 1)})
+        # the RMSNorm ahead of router and experts: folded into the layer, and
+        # as its own launch first (the same algorithmic bytes plus the weights)
+        gam = B.up(synth.rng(63, H).uniform(0.5, 1.5, H).astype(np.float32))
+        for m in moes:
+            m.norm_weight, m.norm_eps = gam, 1e-6
+        t_nf, _ = B.graph_time([lambda m=m: qg.moe_ffn(m, X, Y) for m in moes], 4 * copies)
+        for m in moes:
+            m.norm_weight = None
+        Xn = torch.empty_like(X)
+
+        def norm_then_moe(m):
+            qg.rmsnorm(X, gam, 1e-6, Xn)
+            qg.moe_ffn(m, Xn, Y)
+
+        t_nu, _ = B.graph_time([lambda m=m: norm_then_moe(m) for m in moes], 4 * copies)
+        kernels[f"moe_ffn_rmsnorm_fused_{T}tok"] = kernel_entry(nbytes + 4 * H, t_nf)
+        kernels[f"rmsnorm_then_moe_ffn_{T}tok"] = kernel_entry(nbytes + 4 * H, t_nu)
     del moes, gate, upm, down
     log("  moe done")
 

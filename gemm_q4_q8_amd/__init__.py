@@ -45,6 +45,7 @@ class qg_moe(ctypes.Structure):
         ("sh_ffn", _i64),
         ("sh_gate_qs", _vp), ("sh_up_qs", _vp), ("sh_down_qs", _vp),
         ("sh_gate_d", _vp), ("sh_up_d", _vp), ("sh_down_d", _vp),
+        ("norm_weight", _vp), ("norm_eps", ctypes.c_float),
     ]
 
 
@@ -357,6 +358,8 @@ class MoE:
     sh_up: Optional[QMatrix] = None
     sh_down: Optional[QMatrix] = None
     normalize_topk: bool = True
+    norm_weight: object = None  # f32 [hidden]: RMSNorm ahead of router and experts
+    norm_eps: float = 0.0
 
     def struct(self) -> qg_moe:
         s = qg_moe()
@@ -374,6 +377,8 @@ class MoE:
                 m.d.data_ptr() for m in (self.sh_gate, self.sh_up, self.sh_down))
         else:
             s.sh_ffn = 0
+        s.norm_weight = self.norm_weight.data_ptr() if self.norm_weight is not None else None
+        s.norm_eps = float(self.norm_eps)
         return s
 
 

@@ -385,6 +385,11 @@ static int check_moe(const qg_moe *m, int32_t ntok) {
   const void *d[3] = {m->gate_d, m->up_d, m->down_d};
   for (int i = 0; i < 3; ++i)
     if (!aligned(q[i], 16) || !aligned(d[i], 8)) return QG_EALIGN;
+  if (m->norm_weight) {
+    if (!aligned(m->norm_weight, 16)) return QG_EALIGN;
+    if (!(m->norm_eps >= 0.0f) || m->norm_eps > 3.0e38f) return QG_EINVAL;
+    if (!dot_interleaved(m->hidden)) return QG_EUNSUPPORTED;
+  }
   if (m->sh_ffn > 0) {
     const void *sq[3] = {m->sh_gate_qs, m->sh_up_qs, m->sh_down_qs};
     const void *sd[3] = {m->sh_gate_d, m->sh_up_d, m->sh_down_d};

@@ -61,6 +61,8 @@ struct MoeArgs {
   int sel_local;          // one token: each gate/up workgroup selects the experts itself
   int il_gu;              // gate/up: interleaved K segments
   int nsh;                // shared-expert entries (tokens in groups of the unit width)
+  const float *rms_w;     // RMSNorm ahead of router and experts (NULL: none), and eps
+  float rms_eps;
   int64_t gpart_per;      // gate/up partial floats per listed expert
 };
 
@@ -212,7 +214,7 @@ __global__ void __launch_bounds__(RW * 64) moe_router_kernel(MoeArgs a) {
   __shared__ __attribute__((aligned(16))) int32_t s_sel[TMAX * 8];
   __shared__ int32_t s_cnt[1024], s_off[1024];  // per expert (n_expert <= 1024)
   __shared__ int32_t s_wtot[RW];
-  __shared__ float s_part[RW];
+  __shared__ float s_part[RW], s_sq[RW];
   const int tid = threadIdx.x, lane = tid & 63, wk = tid >> 6;
   {
     // wave -> (expert, token, part of the hidden range); the P parts of a
@@ -221,7 +223,10 @@ __global__ void __launch_bounds__(RW * 64) moe_router_kernel(MoeArgs a) {
     const int64_t item = ((int64_t)blockIdx.x * RW + wk) / P;
     const int p = wk % P;
     const int e = (int)(item / a.T), t = (int)(item % a.T);
-    float v = 0.0f;
+    // with the RMSNorm: R (x * w) here, the same pass summing x^2; every
+    // logit of token t is then scaled by its 1 / rms (one positive factor
+    // per token, so it changes no ranking, only the softmax weights)
+    float v = 0.0f, sq = 0.0f;
     if (e < a.E) {
       const int64_t hb = (int64_t)p * hp, he = hb + hp < a.H ? hb + hp : a.H;
       for (int64_t h0 = hb; h0 < he; h0 += 2048) {
@@ -232,6 +237,21 @@ __global__ void __launch_bounds__(RW * 64) moe_router_kernel(MoeArgs a) {
           rv[j] = h < he ? *(const float4 *)(a.R + (int64_t)e * a.H + h) : float4{0, 0, 0, 0};
           xv[j] = h < he ? *(const float4 *)(a.X + (int64_t)t * a.ldx + h) : float4{0, 0, 0, 0};
         }
+        if (a.rms_w) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int64_t h = h0 + ((int64_t)j * 64 + lane) * 4;
+            const float4 w = h < he ? *(const float4 *)(a.rms_w + h) : float4{0, 0, 0, 0};
+            sq = __builtin_fmaf(xv[j].x, xv[j].x, sq);
+            sq = __builtin_fmaf(xv[j].y, xv[j].y, sq);
+            sq = __builtin_fmaf(xv[j].z, xv[j].z, sq);
+            sq = __builtin_fmaf(xv[j].w, xv[j].w, sq);
+            xv[j].x *= w.x;
+            xv[j].y *= w.y;
+            xv[j].z *= w.z;
+            xv[j].w *= w.w;
+          }
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           v = __builtin_fmaf(rv[j].x, xv[j].x, v);
@@ -241,14 +261,23 @@ __global__ void __launch_bounds__(RW * 64) moe_router_kernel(MoeArgs a) {
         }
       }
       v = wave_sum(v);
+      if (a.rms_w) sq = wave_sum(sq);
     }
-    if (lane == 0) s_part[wk] = v;
+    if (lane == 0) {
+      s_part[wk] = v;
+      s_sq[wk] = sq;
+    }
     __syncthreads();
     if (tid < RW / P) {
       const int64_t it = (int64_t)blockIdx.x * (RW / P) + tid;
       if (it < (int64_t)a.E * a.T) {
         float l = s_part[tid * P];
         for (int q = 1; q < P; ++q) l += s_part[tid * P + q];
+        if (a.rms_w) {
+          float ss = s_sq[tid * P];
+          for (int q = 1; q < P; ++q) ss += s_sq[tid * P + q];
+          l *= 1.0f / __builtin_sqrtf(ss / (float)a.H + a.rms_eps);
+        }
         st_agent(a.logits + (it % a.T) * a.E + it / a.T, l);
       }
     }
@@ -381,7 +410,7 @@ __device__ __forceinline__ int moe_expert(const MoeArgs &a, int u, DotArgs &d, i
   return nc;
 }
 
-template <int QT, int NC, int PF>
+template <int QT, int NC, int PF, bool RMSN>
 __global__ void __launch_bounds__(MOE_WMAX * 64) moe_gateup_kernel(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ uint32_t flag;
@@ -429,10 +458,12 @@ __global__ void __launch_bounds__(MOE_WMAX * 64) moe_gateup_kernel(MoeArgs a) {
   d.ldy = a.Fmax;
   d.part = a.gpart + (int64_t)u * a.gpart_per;
   d.cnt = a.gcnt + (int64_t)u * a.G_gu;
+  d.gamma = a.rms_w;
+  d.norm_eps = a.rms_eps;
   __syncthreads();  // the column maps
   float bv = 0.0f;
   int32_t bi = 0;
-  dot_unit<QT, NC, 2, EPI_SILU, 1, PF, 0, PH_PLAIN, true>(d, g, s, smem, &flag, bv, bi);
+  dot_unit<QT, NC, 2, EPI_SILU, 1, PF, 0, PH_PLAIN, true, NoHook, RMSN>(d, g, s, smem, &flag, bv, bi);
 }
 
 template <int QT, int NC, int PF>
@@ -634,16 +665,20 @@ static int launch_moe_t(const MoeCall &c, MoeArgs &a) {
     hipLaunchKernelGGL((moe_router_kernel<NC, 16>), rgrid, dim3(RW * 64), 0, c.stream, a);
   if (launch_status() != QG_OK) return QG_EHIP;
 
-  auto kg = moe_gateup_kernel<QT, NC, PFG>;
+  // with the RMSNorm, every unit stages all of K (interleaved segments)
+  if (a.rms_w && !(a.il_gu || a.sw_gu)) return QG_EUNSUPPORTED;
+  auto kg = a.rms_w ? moe_gateup_kernel<QT, NC, PFG, true> : moe_gateup_kernel<QT, NC, PFG, false>;
   // in-workgroup or interleaved segments: all of K staged (plus, in the
-  // workgroup, the segment sums)
-  const size_t lds_g = (a.sw_gu || a.il_gu) ? unit_lds<NC, PFG>(a.H / 128, 1) + (a.sw_gu ? (size_t)(a.S_gu - 1) * a.W_gu * 2 *
-                                                                      (NC < 4 ? NC : 4) * 64 * 4 : 0)
-                               : unit_lds<NC, PFG>(a.H / 128, a.S_gu);
+  // workgroup, the segment sums; with the norm, the squares per piece and
+  // 1 / rms per column)
+  size_t lds_g = (a.sw_gu || a.il_gu) ? unit_lds<NC, PFG>(a.H / 128, 1) + (a.sw_gu ? (size_t)(a.S_gu - 1) * a.W_gu * 2 *
+                                                                (NC < 4 ? NC : 4) * 64 * 4 : 0)
+                         : unit_lds<NC, PFG>(a.H / 128, a.S_gu);
+  if (a.rms_w) lds_g += (size_t)NC * (a.H / 128) * TILE_BLOCKS * 4 * 4 + (size_t)NC * 4;
   const int sx = a.sw_gu ? 1 : a.S_gu;
   const int wg_threads = a.W_gu * (a.sw_gu ? a.S_gu : 1) * 64;
-  static size_t granted_g = 65536;
-  st = grant((const void *)kg, lds_g, granted_g);
+  static size_t granted_g[2] = {65536, 65536};  // per kernel: without, with the norm
+  st = grant((const void *)kg, lds_g, granted_g[a.rms_w ? 1 : 0]);
   if (st) return st;
   clear_hip_error();
   hipLaunchKernelGGL(kg, dim3((unsigned)((int64_t)(a.Umax + a.nsh) * a.G_gu * sx)), dim3(wg_threads), lds_g,
@@ -689,6 +724,8 @@ int launch_moe(const MoeCall &c) {
   a.E = m->n_expert;
   a.k = m->top_k;
   a.norm = m->normalize_topk ? 1 : 0;
+  a.rms_w = m->norm_weight;
+  a.rms_eps = m->norm_eps;
   a.T = c.ntok;
   a.Umax = (int)L.umax;
   // enough router waves to spread the router matrix over the device, each

@@ -301,6 +301,13 @@ typedef struct {
   int64_t sh_ffn; /* 0 = no shared expert */
   const void *sh_gate_qs, *sh_up_qs, *sh_down_qs;
   const void *sh_gate_d, *sh_up_d, *sh_down_d;
+  /* RMSNorm ahead of router and experts (ENG: norm fused with the router);
+   * NULL = none.  hidden floats, 16-byte aligned; the router and every
+   * expert read X * norm_weight / sqrt(mean(X^2) + norm_eps), the residual
+   * Y is not normalised.  hidden <= 5120 (every expert unit stages all of
+   * the hidden range), else QG_EUNSUPPORTED; norm_eps >= 0 and finite. */
+  const float *norm_weight;
+  float norm_eps;
 } qg_moe;
 
 size_t qg_moe_ws_bytes(const qg_moe *m, int32_t ntok);

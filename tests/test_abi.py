@@ -238,6 +238,15 @@ def test_moe_checks():
     assert call(_moe(router=FAKE + 4)) == EALIGN
     assert call(_moe(sh_ffn=128)) == EINVAL          # shared expert pointers missing
     assert call(_moe(), wsb=8) == EWS
+    # the RMSNorm ahead of router and experts
+    G = FAKE + (5 << 28)
+    assert call(_moe(norm_weight=G + 4, norm_eps=1e-6)) == EALIGN
+    assert call(_moe(norm_weight=G, norm_eps=-1.0)) == EINVAL
+    assert call(_moe(norm_weight=G, norm_eps=float("nan"))) == EINVAL
+    X2 = FAKE + (6 << 28)
+    wide = _moe(norm_weight=G, norm_eps=1e-6, hidden=8192)
+    assert L.moe_ffn(ctypes.byref(wide), X2, 8192, 1, X2 + (1 << 20), 8192, None, None, ws, 1 << 26,
+                     None) == EUNSUP
 
 
 def test_read_probe_checks():

@@ -437,16 +437,18 @@ def _moe_build(env, E, H, F, k, seed, shared=True, normalize=True):
     return m, (gate, upw, down, router, sh)
 
 
-def _moe_check(env, m, host_w, T, k, cfg, normalize=True, tries=40):
+def _moe_check(env, m, host_w, T, k, cfg, normalize=True, tries=40, norm=None, xscale=1.0):
     torch, qg, dev = env
     gate, upw, down, router, sh = host_w
     H = m.hidden
     for s in range(tries):
-        X = synth.gen_x(H, T, cfg_id=cfg + 1000 * s)
+        X = (synth.gen_x(H, T, cfg_id=cfg + 1000 * s) * xscale).astype(np.float32)
         res = ops.moe_ffn(X, router, Q4, gate, upw, down, top_k=k, normalize=normalize,
                           sh_gate=None if sh is None else sh[0], sh_up=None if sh is None else sh[1],
                           sh_down=None if sh is None else sh[2],
-                          y_in=synth.rng(cfg, 90).standard_normal((H, T)).astype(np.float32))
+                          y_in=synth.rng(cfg, 90).standard_normal((H, T)).astype(np.float32),
+                          norm_w=None if norm is None else norm[0].astype(np.float64),
+                          norm_eps=0.0 if norm is None else norm[1])
         if ops.moe_routing_certified(res, k, H):
             break
     else:
@@ -475,6 +477,18 @@ def test_moe_wide_experts(env):
     say("moe wide experts (ffn 11008)")
     m, hw = _moe_build(env, E=6, H=128, F=11008, k=5, seed=85)
     _moe_check(env, m, hw, 3, 5, cfg=86)
+
+
+@pytest.mark.parametrize("T", [1, 3, 16])
+def test_moe_rmsnorm(env, T):
+    """The RMSNorm ahead of router and experts (the residual not normalised):
+    routing and output against the oracle, on inputs far from unit RMS."""
+    torch, qg, dev = env
+    say(f"moe rmsnorm T={T}")
+    m, hw = _moe_build(env, E=16, H=256, F=128, k=4, seed=95 + T)
+    gam = synth.rng(96, 256).uniform(0.5, 1.5, 256).astype(np.float32)
+    m.norm_weight, m.norm_eps = up(env, gam), 1e-5
+    _moe_check(env, m, hw, T, 4, cfg=97 + T, norm=(gam, 1e-5), xscale=7.0)
 
 
 def test_moe_unnormalized(env):
