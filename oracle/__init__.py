@@ -10,6 +10,8 @@ What it computes, in float64, from the canonical GGUF block bytes:
 * `quant`  - Q4_0 / Q8_0 block decoding by the block definition, dense
   dequantisation, and the byte image of the library's repacked layout
   written out from that layout's definition.
+* `requant` - Q4_1 / Q5_0 / Q5_1 blocks decoded by the public GGUF layouts
+  and requantised to Q8_0 in float32 steps (byte-exact reference).
 * `ops`    - y = W x (and y += W x), RMSNorm, the fused gate/up SiLU, LM-head argmax
   and LM-head top-k candidates with lowest-index ties, router top-k,
   softmax, the MoE FFN, and the tolerances and argmax / top-k certification
@@ -19,4 +21,4 @@ Pins (tests/test_oracle.py) tie every function to something other than
 itself: hand-worked blocks, exact rational brute force, closed forms,
 library special cases and invariants.  Parity unpinned: none.
 """
-from . import quant, ops  # noqa: F401
+from . import quant, ops, requant  # noqa: F401

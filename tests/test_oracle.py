@@ -323,6 +323,59 @@ def test_moe_with_norm_invariants():
     assert np.all(r1["logit_a"] >= ops.router_logits(xn, router)[1])
 
 
+def test_requant_decoding_by_hand():
+    """Hand-built source blocks with known values: Q4_1 weight j at nibble
+    j (low) or j - 16 (high), value w * d + m; Q5_0 / Q5_1 with single qh
+    bits set (bit j adds 16 to weight j, bit j + 16 to weight j + 16)."""
+    from oracle import requant as rq
+    d_one, m_neg2 = np.array([1.0], np.float16).view(np.uint8), np.array([-2.0], np.float16).view(np.uint8)
+    b = np.zeros((1, 20), np.uint8)
+    b[0, 0:2], b[0, 2:4] = d_one, m_neg2
+    b[0, 4:20] = np.arange(16, dtype=np.uint8) | ((15 - np.arange(16, dtype=np.uint8)) << 4)
+    v = rq.decode_values_f32(rq.Q4_1, b)[0]
+    assert list(v[:16]) == [j - 2.0 for j in range(16)] and list(v[16:]) == [13.0 - j for j in range(16)]
+    half = np.array([0.5], np.float16).view(np.uint8)
+    for t, qh_off, qs_off in ((rq.Q5_0, 2, 6), (rq.Q5_1, 4, 8)):
+        b = np.zeros((1, rq.SRC_BLOCK_BYTES[t]), np.uint8)
+        b[0, 0:2] = half
+        if t == rq.Q5_1:
+            b[0, 2:4] = m_neg2
+        b[0, qs_off:qs_off + 16] = 0x31            # low nibble 1, high nibble 3
+        b[0, qh_off:qh_off + 4] = np.array([(1 << 5) | (1 << 20)], "<u4").view(np.uint8)
+        v = rq.decode_values_f32(t, b)[0]
+        w = np.array([1] * 16 + [3] * 16)
+        w[5] += 16
+        w[20] += 16
+        want = (w - 16) * 0.5 if t == rq.Q5_0 else w * 0.5 - 2.0
+        assert np.array_equal(v, want.astype(np.float32)), t
+
+
+def test_requant_rounding_rules():
+    """Q8_0 requantisation: all-zero blocks stay zero with scale 0; the
+    largest magnitude maps to +-127; halves round away from zero (checked
+    against the definition on exact float32 halves); the reconstruction
+    error stays within half a step plus the f16 rounding of the scale; and
+    negating the values negates the weights."""
+    from oracle import requant as rq
+    assert list(rq.round_half_away(np.array([0.5, -0.5, 1.5, -2.5, 0.49999997, 2.4999998]))) == \
+        [1.0, -1.0, 2.0, -3.0, 0.0, 2.0]
+    z = rq.quantize_q8_0(np.zeros((1, 32), np.float32))
+    assert not z.any()
+    g = np.random.default_rng(18)
+    v = (g.standard_normal((200, 32)) * g.uniform(1e-3, 50.0, (200, 1))).astype(np.float32)
+    out = rq.quantize_q8_0(v)
+    w, d = quant.decode_blocks(quant.Q8_0, out)
+    top = np.argmax(np.abs(v), axis=1)
+    assert np.all(np.abs(w[np.arange(200), top]) == 127)
+    amax = np.max(np.abs(v), axis=1).astype(np.float64)
+    step = amax / 127.0
+    err = np.abs(w * d[:, None] - v.astype(np.float64))
+    assert np.all(err <= 0.5 * step[:, None] * (1 + 1e-6) + 127 * np.abs(d - step)[:, None] + 1e-12)
+    neg = rq.quantize_q8_0(-v)
+    wn, dn = quant.decode_blocks(quant.Q8_0, neg)
+    assert np.array_equal(wn, -w) and np.array_equal(dn, d)
+
+
 def test_softmax_properties():
     g = np.random.default_rng(14)
     v = g.standard_normal(8)
