@@ -205,6 +205,18 @@ def run_extras(B, kernels):
     del p, w
     log("  lmhead done")
 
+    # load-time requantisation of a Q4_1 17408 x 5120 matrix to Q8_0 (bytes
+    # read + written)
+    nbk = 17408 * 5120 // 32
+    src = torch.randint(0, 256, (nbk * 20,), dtype=torch.uint8, device=B.dev)
+    src.view(nbk, 20)[:, 1] = 0x3C        # finite scales near 1 (f16 high byte)
+    src.view(nbk, 20)[:, 3] = 0xBC        # offsets near -1
+    dst = torch.empty(nbk * 34, dtype=torch.uint8, device=B.dev)
+    t, _ = B.graph_time([lambda: qg.requant_q8_0(qg.Q4_1, src, nbk, dst)], 20)
+    kernels["requant_q4_1_to_q8_0_17408x5120"] = kernel_entry(nbk * (20 + 34), t)
+    del src, dst
+    log("  requant done")
+
     # MoE FFN, 256 experts (8 active) + shared, hidden 2048, ffn 512
     E, H, F, k = 256, 2048, 512, 8
     g = np.random.default_rng(61)

@@ -72,6 +72,7 @@ _SIGS = {
     "gateup_silu_rmsnorm": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _i32,
                                            _vp, ctypes.c_float, _vp, _i64, _vp, _sz, _vp]),
     "qg_rmsnorm": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, ctypes.c_float, _vp, _i64, _vp]),
+    "qg_requant_q8_0": (ctypes.c_int, [ctypes.c_int, _i64, _vp, _vp, _vp]),
     "qg_lmhead_ws_bytes": (_sz, [_i64, _i64]),
     "qg_lmhead_topk_ws_bytes": (_sz, [_i64, _i64, _i32]),
     "lmhead_topk": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp,
@@ -242,6 +243,21 @@ def gateup_silu(wg: QMatrix, wu: QMatrix, X, H=None):
                            H2.data_ptr(), _ld(H2), ws.data_ptr(), ws.numel(),
                            _stream(X.device)), "gateup_silu")
     return H
+
+
+Q4_1, Q5_0, Q5_1 = 3, 6, 7
+
+
+def requant_q8_0(src_type: int, blocks, n_blocks: int, out=None):
+    """Q4_1 / Q5_0 / Q5_1 blocks (device uint8) -> canonical Q8_0 blocks
+    (device uint8, n_blocks * 34 bytes), on the GPU."""
+    torch = _torch()
+    _check_dev(blocks)
+    if out is None:
+        out = torch.empty(n_blocks * 34, dtype=torch.uint8, device=blocks.device)
+    _check(lib.qg_requant_q8_0(src_type, n_blocks, blocks.data_ptr(), out.data_ptr(), _stream(blocks.device)),
+           "qg_requant_q8_0")
+    return out
 
 
 def gateup_silu_rmsnorm(wg: QMatrix, wu: QMatrix, X, gamma, eps: float, H=None):

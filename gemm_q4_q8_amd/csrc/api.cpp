@@ -136,6 +136,23 @@ int qg_repack(int qtype, int64_t n_mat, int64_t rows, int64_t cols, const void *
   return launch_repack(qtype, n_mat, rows, cols, blocks, qs, d, (hipStream_t)stream);
 }
 
+int qg_requant_q8_0(int src_type, int64_t n_blocks, const void *src, void *dst, void *stream) {
+  int bs;
+  switch (src_type) {
+    case QG_Q4_1: bs = 20; break;
+    case QG_Q5_0: bs = 22; break;
+    case QG_Q5_1: bs = 24; break;
+    default: return QG_EINVAL;
+  }
+  if (n_blocks < 1 || n_blocks > ((int64_t)1 << 40)) return QG_ESHAPE;
+  if (!src || !dst) return QG_EINVAL;
+  if (!aligned(src, 2) || !aligned(dst, 2)) return QG_EALIGN;
+  const Range in{(uintptr_t)src, (uintptr_t)src + (uintptr_t)(n_blocks * bs)};
+  const Range out{(uintptr_t)dst, (uintptr_t)dst + (uintptr_t)(n_blocks * 34)};
+  if (overlap(in, out)) return QG_EINVAL;
+  return launch_requant_q8_0(src_type, n_blocks, src, dst, stream);
+}
+
 size_t qg_gemv_ws_bytes(int64_t rows, int64_t cols) {
   if (rows <= 0 || cols <= 0 || cols % 32) return 0;
   return qmv_ws_bytes(rows, cols, gemv_segments(rows, cols, 1, 8), 1, 8, false);

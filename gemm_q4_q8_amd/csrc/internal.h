@@ -74,6 +74,7 @@ size_t ffn_ws_bytes(int64_t hidden, int64_t ffn);
 int launch_ffn(const FfnCall &c);
 
 // Streaming-read probe (the bench's measured read ceiling).
+int launch_requant_q8_0(int src_type, int64_t nb, const void *src, void *dst, void *stream);
 int launch_rmsnorm(const float *X, int64_t ldx, int64_t cols, int ncols, const float *gamma, float eps, float *Y,
                    int64_t ldy, void *stream);
 int launch_read_probe(const void *p, size_t bytes, uint32_t *sink, void *stream);

@@ -68,6 +68,8 @@ extern "C" {
 
 /* GGUF tensor type ids, so a GGUF reader can pass them through. */
 enum { QG_Q4_0 = 2, QG_Q8_0 = 8 };
+/* Source block types qg_requant_q8_0 converts (GGUF type ids). */
+enum { QG_Q4_1 = 3, QG_Q5_0 = 6, QG_Q5_1 = 7 };
 
 enum {
   QG_OK = 0,
@@ -179,6 +181,23 @@ int gateup_silu(int qtype, const void *g_qs, const void *g_d, const void *u_qs,
                 const void *u_d, int64_t rows, int64_t cols, const float *X,
                 int64_t ldx, int32_t ncols, float *H, int64_t ldh,
                 void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Requantisation to Q8_0 at load  [ENG What it runs: the Q4_1 / Q5_0 /
+ * K-quant tensors of the public MoE file are requantized to Q8_0 on the way
+ * to the GPU; ARCH where the weights live: converted once and kept]
+ *
+ *   dst[b] = Q8_0 block of the values of src[b] (b < n_blocks): d = max|v|
+ *   / 127 and q = v / d rounded half away from zero, in float32 steps,
+ *   d stored as binary16.  Source layouts: the public GGUF ones (Q4_1 20 B:
+ *   f16 d, f16 m, 16 nibble bytes, v = w d + m; Q5_0 22 B: f16 d, 32 high
+ *   bits, nibbles, v = (w - 16) d; Q5_1 24 B: d, m, high bits, nibbles,
+ *   v = w d + m).  K-quants are not covered.  src and dst: device memory,
+ *   2-byte aligned, not overlapping; dst receives n_blocks * 34 bytes of
+ *   canonical Q8_0 blocks, ready for qg_repack(QG_Q8_0, ...).  Asynchronous
+ *   on `stream`; the bytes are a function of the source bytes alone.
+ * ------------------------------------------------------------------------ */
+int qg_requant_q8_0(int src_type, int64_t n_blocks, const void *src, void *dst, void *stream);
 
 /* ------------------------------------------------------------------------
  * RMSNorm prologue  [TJS Llama-style differences: RMSNorm takes the root

@@ -25,8 +25,8 @@ def _declared():
 def test_every_declared_symbol_is_exported():
     names = _declared()
     assert {"qgemv_q4_0", "qgemv_q8_0", "qgemm16", "gateup_silu", "moe_ffn",
-            "lmhead_argmax", "lmhead_topk", "gateup_silu_rmsnorm", "qg_rmsnorm", "qg_repack",
-            "qg_packed_bytes"} <= set(names)
+            "lmhead_argmax", "lmhead_topk", "gateup_silu_rmsnorm", "qg_rmsnorm", "qg_requant_q8_0",
+            "qg_repack", "qg_packed_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -145,6 +145,18 @@ def test_lmhead_topk_checks():
     assert L.lmhead_topk(2, FAKE, FAKE, 64, 128, 64, x, 4, o, o + 6, ws, big, None) == EALIGN
     assert L.lmhead_topk(2, FAKE, FAKE, 64, 128, 64, x, 4, o, None, ws, 4, None) == EWS
     assert L.lmhead_topk(5, FAKE, FAKE, 64, 128, 64, x, 4, o, None, ws, big, None) == EINVAL
+
+
+def test_requant_checks():
+    src, dst = FAKE, FAKE + (1 << 30)
+    rq = L.qg_requant_q8_0
+    assert rq(2, 10, src, dst, None) == EINVAL          # Q4_0 is not a source type
+    assert rq(8, 10, src, dst, None) == EINVAL
+    assert rq(3, 0, src, dst, None) == ESHAPE
+    assert rq(3, 10, None, dst, None) == EINVAL
+    assert rq(6, 10, src + 1, dst, None) == EALIGN
+    assert rq(7, 10, src, dst + 1, None) == EALIGN
+    assert rq(3, 10, src, src + 100, None) == EINVAL   # 200 source bytes overlap the output
 
 
 def test_rmsnorm_checks():

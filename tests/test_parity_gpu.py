@@ -168,6 +168,56 @@ def test_gateup_parity(env, qtype, rows, cols, ncols):
     assert_tol(host(H).T, h, th, "gateup")
 
 
+# --------------------------------------------------- requantisation to Q8_0
+def _src_blocks(src_type, nb, seed):
+    """Random source blocks with finite scales of moderate size (the f16
+    exponent kept in 2^-14 .. 2^1) and random offsets for the types that
+    have one."""
+    from oracle import requant as rq
+    g = np.random.default_rng(seed)
+    raw = g.integers(0, 256, (nb, rq.SRC_BLOCK_BYTES[src_type]), dtype=np.uint8)
+    d = (g.uniform(-1.0, 1.0, nb) * 2.0 ** g.integers(-14, 2, nb)).astype(np.float16)
+    raw[:, 0:2] = d.view(np.uint8).reshape(-1, 2)
+    if src_type != rq.Q5_0:
+        m = (g.standard_normal(nb) * 2.0 ** g.integers(-12, 3, nb)).astype(np.float16)
+        raw[:, 2:4] = m.view(np.uint8).reshape(-1, 2)
+    return raw
+
+
+@pytest.mark.parametrize("src_type", [3, 6, 7])
+@pytest.mark.parametrize("nb", [1, 255, 257, 40000])
+def test_requant_bytes_exact(env, src_type, nb):
+    """Every output byte equal to the oracle's, including all-zero and
+    single-value blocks and a tail past a multiple of 256 blocks."""
+    torch, qg, dev = env
+    from oracle import requant as rq
+    raw = _src_blocks(src_type, nb, seed=nb + src_type)
+    if nb > 3:
+        raw[1, :] = 0                                  # all zero
+        raw[2, 4:] = 0                                 # scale only: every value the offset (or -16 d)
+    want = rq.requant_q8_0(src_type, raw)
+    got = host(qg.requant_q8_0(src_type, up(env, raw.reshape(-1)), nb)).reshape(nb, 34)
+    bad = np.flatnonzero(np.any(got != want, axis=1))
+    assert bad.size == 0, (bad[:5], got[bad[:1]], want[bad[:1]])
+
+
+def test_requant_then_product(env):
+    """The requantised blocks through repack and the GEMV: against the
+    oracle's product of the oracle's Q8_0 bytes."""
+    torch, qg, dev = env
+    from oracle import requant as rq
+    rows, cols = 300, 1024
+    raw = _src_blocks(3, rows * cols // 32, seed=9)
+    q8d = qg.requant_q8_0(3, up(env, raw.reshape(-1)), rows * cols // 32)
+    want = rq.requant_q8_0(3, raw)
+    assert np.array_equal(q8d.cpu().numpy().reshape(-1, 34), want)
+    W = qg.qg_repack(Q8, q8d, rows, cols)
+    x = synth.gen_x(cols, 2, cfg_id=11)
+    Y = qg.qgemv(W, up(env, x.T))
+    ref, a = ops.gemv(Q8, want.reshape(rows, cols // 32, 34), x)
+    assert_tol(host(Y).T, ref, ops.tol_dot(a), "requant gemv")
+
+
 # ------------------------------------------------------- RMSNorm prologue
 @pytest.mark.parametrize("qtype", [Q4, Q8])
 @pytest.mark.parametrize("rows,cols", [(40, 416), (64, 4096), (512, 2048), (300, 5120)])
