@@ -185,7 +185,7 @@ def _src_blocks(src_type, nb, seed):
 
 
 @pytest.mark.parametrize("src_type", [3, 6, 7])
-@pytest.mark.parametrize("nb", [1, 255, 257, 40000])
+@pytest.mark.parametrize("nb", [1, 255, 256, 257, 1024, 40000])
 def test_requant_bytes_exact(env, src_type, nb):
     """Every output byte equal to the oracle's, including all-zero and
     single-value blocks and a tail past a multiple of 256 blocks."""
@@ -199,6 +199,25 @@ def test_requant_bytes_exact(env, src_type, nb):
     got = host(qg.requant_q8_0(src_type, up(env, raw.reshape(-1)), nb)).reshape(nb, 34)
     bad = np.flatnonzero(np.any(got != want, axis=1))
     assert bad.size == 0, (bad[:5], got[bad[:1]], want[bad[:1]])
+
+
+@pytest.mark.parametrize("src_type", [3, 6, 7])
+def test_requant_unaligned(env, src_type):
+    """Source and destination 2 bytes past a 16-byte boundary (the 16-bit
+    word path) give the same bytes, and nothing outside the output is
+    written."""
+    torch, qg, dev = env
+    from oracle import requant as rq
+    nb = 1000
+    raw = _src_blocks(src_type, nb, seed=77 + src_type)
+    bs = rq.SRC_BLOCK_BYTES[src_type]
+    sbuf = torch.zeros(nb * bs + 16, dtype=torch.uint8, device=dev)
+    sbuf[2:2 + nb * bs] = up(env, raw.reshape(-1))
+    dbuf = torch.full((nb * 34 + 16,), 0xA5, dtype=torch.uint8, device=dev)
+    qg.requant_q8_0(src_type, sbuf[2:2 + nb * bs], nb, dbuf[2:2 + nb * 34])
+    got = dbuf.cpu().numpy()
+    assert np.all(got[:2] == 0xA5) and np.all(got[2 + nb * 34:] == 0xA5)
+    assert np.array_equal(got[2:2 + nb * 34].reshape(nb, 34), rq.requant_q8_0(src_type, raw))
 
 
 def test_requant_then_product(env):
