@@ -29,8 +29,9 @@ __device__ __forceinline__ float f16_bits(uint32_t b) {
 // one half, carrying x's sign, truncated toward zero.  The sum reaches the
 // next integer away from zero exactly when |x - trunc(x)| >= 1/2 (a sum that
 // is a tie rounds to the even neighbour, which is then that integer), so
-// this equals roundf(x) there; checked for every such float.  Three
-// instructions instead of roundf's six before the conversion.
+// this equals roundf(x) there; the host tests check it for every float of
+// magnitude up to 128, the range of the quotients here.  Three instructions
+// instead of roundf's six before the conversion.
 // x must be a rounded float: contraction stays off here and where x is
 // formed, or a product feeding x would be fused into the sum.
 __device__ __forceinline__ int round_half_away(float x) {
