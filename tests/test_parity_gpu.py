@@ -184,6 +184,39 @@ def _src_blocks(src_type, nb, seed):
     return raw
 
 
+def _tie_block(src_type):
+    """A block whose largest magnitude is 127, so the Q8_0 scale is 1 and
+    its reciprocal exact, with values on exact halves: Q4_1 / Q5_1 with
+    d = 8.5, m = -0.5 (8.5 n - 0.5, halves at every even n); Q5_0 with
+    d = 7.9375 ((w - 16) d, +-63.5 at w = 8 and 24)."""
+    from oracle import requant as rq
+    b = np.zeros(rq.SRC_BLOCK_BYTES[src_type], np.uint8)
+    if src_type == rq.Q5_0:
+        b[0:2] = np.array([7.9375], np.float16).view(np.uint8)
+        w = np.arange(32)
+        qh = 0
+        for j in range(32):
+            qh |= int(w[j] >> 4) << j
+        b[2:6] = np.array([qh], "<u4").view(np.uint8)
+        b[6:22] = (w[:16] & 15) | ((w[16:] & 15) << 4)
+    else:
+        b[0:2] = np.array([8.5], np.float16).view(np.uint8)
+        b[2:4] = np.array([-0.5], np.float16).view(np.uint8)
+        j = np.arange(16)
+        q0 = 4 if src_type == rq.Q4_1 else 8
+        b[q0:q0 + 16] = j | ((15 - j) << 4)
+    return b
+
+
+def test_tie_block_has_halves():
+    """The planted block does put quotients on exact halves (oracle)."""
+    from oracle import requant as rq
+    for t in (3, 6, 7):
+        v = rq.decode_values_f32(t, _tie_block(t)[None, :])[0]
+        assert np.max(np.abs(v)) == 127.0
+        assert np.any(np.abs(v - np.trunc(v)) == 0.5)
+
+
 @pytest.mark.parametrize("src_type", [3, 6, 7])
 @pytest.mark.parametrize("nb", [1, 255, 256, 257, 1024, 40000])
 def test_requant_bytes_exact(env, src_type, nb):
@@ -195,6 +228,7 @@ def test_requant_bytes_exact(env, src_type, nb):
     if nb > 3:
         raw[1, :] = 0                                  # all zero
         raw[2, 4:] = 0                                 # scale only: every value the offset (or -16 d)
+        raw[3] = _tie_block(src_type)
     want = rq.requant_q8_0(src_type, raw)
     got = host(qg.requant_q8_0(src_type, up(env, raw.reshape(-1)), nb)).reshape(nb, 34)
     bad = np.flatnonzero(np.any(got != want, axis=1))
