@@ -83,6 +83,15 @@ _SIGS = {
     "moe_ffn": (ctypes.c_int, [ctypes.POINTER(qg_moe), _vp, _i64, _i32, _vp, _i64, _vp, _vp,
                                _vp, _sz, _vp]),
     "qg_read_probe": (ctypes.c_int, [_vp, _sz, _vp, _vp]),
+    "qg_tune_gemv": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _i64, _i64, _vp, _i64, _i32, _vp, _i64,
+                                    _vp, _sz, _vp, _vp]),
+    "qg_tune_gateup": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _i32,
+                                      _vp, _i64, _vp, _sz, _vp, _vp]),
+    "qg_tune_lmhead": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp,
+                                      _vp, _sz, _vp, _vp]),
+    "qg_plan_set": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _i64, _i64, _i32, _i32]),
+    "qg_plan_get": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _i64, _i64, _i32, _vp]),
+    "qg_plan_reset": (None, []),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -357,6 +366,79 @@ def lmhead_topk(w: QMatrix, x, k: int, n_rows: Optional[int] = None, out_idx=Non
                            out_idx.data_ptr(), out_val.data_ptr(), ws.data_ptr(), ws.numel(),
                            _stream(x.device)), "lmhead_topk")
     return out_idx, out_val
+
+
+# ------------------------------------------------------------ launch plans
+OP_GEMV, OP_GATEUP, OP_LMHEAD = 0, 1, 2
+PLAN_SW = 0x100
+PLAN_STRICT = 0x200
+
+
+def tune_gemv(w: QMatrix, X, Y=None) -> int:
+    """Times the launch plans of qgemv (1..8 columns) or qgemm16 (16) on
+    these buffers, keeps the winner for this shape and column count, and
+    returns it; Y ends holding W X."""
+    torch = _torch()
+    _check_dev(X)
+    X2 = X if X.dim() == 2 else X.view(1, -1)
+    ncols = X2.shape[0]
+    if Y is None:
+        Y = torch.empty((ncols, w.rows), dtype=torch.float32, device=X.device)
+    Y2 = Y if Y.dim() == 2 else Y.view(1, -1)
+    ws_b = lib.qg_gemm16_ws_bytes(w.qtype, w.rows, w.cols) if ncols == 16 else lib.qg_gemv_ws_bytes(w.rows, w.cols)
+    ws = workspace(ws_b, X.device)
+    plan = ctypes.c_int32(-1)
+    _check(lib.qg_tune_gemv(w.qtype, w.qs.data_ptr(), w.d.data_ptr(), w.rows, w.cols, X2.data_ptr(), _ld(X2),
+                            ncols, Y2.data_ptr(), _ld(Y2), ws.data_ptr(), ws.numel(), _stream(X.device),
+                            ctypes.addressof(plan)), "qg_tune_gemv")
+    return plan.value
+
+
+def tune_gateup(wg: QMatrix, wu: QMatrix, X, H=None) -> int:
+    """As tune_gemv for gateup_silu; H ends holding the gated product."""
+    torch = _torch()
+    _check_dev(X)
+    X2 = X if X.dim() == 2 else X.view(1, -1)
+    ncols = X2.shape[0]
+    if H is None:
+        H = torch.empty((ncols, wg.rows), dtype=torch.float32, device=X.device)
+    H2 = H if H.dim() == 2 else H.view(1, -1)
+    ws = workspace(lib.qg_gateup_ws_bytes(wg.rows, wg.cols), X.device)
+    plan = ctypes.c_int32(-1)
+    _check(lib.qg_tune_gateup(wg.qtype, wg.qs.data_ptr(), wg.d.data_ptr(), wu.qs.data_ptr(), wu.d.data_ptr(),
+                              wg.rows, wg.cols, X2.data_ptr(), _ld(X2), ncols, H2.data_ptr(), _ld(H2),
+                              ws.data_ptr(), ws.numel(), _stream(X.device), ctypes.addressof(plan)),
+           "qg_tune_gateup")
+    return plan.value
+
+
+def tune_lmhead(w: QMatrix, x, n_rows: Optional[int] = None) -> int:
+    """As tune_gemv for lmhead_argmax (the entry serves lmhead_topk too)."""
+    torch = _torch()
+    _check_dev(x)
+    out_idx = torch.empty(1, dtype=torch.int32, device=x.device)
+    out_val = torch.empty(1, dtype=torch.float32, device=x.device)
+    ws = workspace(lib.qg_lmhead_ws_bytes(w.rows, w.cols), x.device, "lmhead")
+    plan = ctypes.c_int32(-1)
+    _check(lib.qg_tune_lmhead(w.qtype, w.qs.data_ptr(), w.d.data_ptr(), w.rows, w.cols,
+                              w.rows if n_rows is None else n_rows, x.data_ptr(), out_idx.data_ptr(),
+                              out_val.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x.device),
+                              ctypes.addressof(plan)), "qg_tune_lmhead")
+    return plan.value
+
+
+def plan_set(op: int, qtype: int, rows: int, cols: int, ncols: int, plan: int) -> None:
+    _check(lib.qg_plan_set(op, qtype, rows, cols, ncols, plan), "qg_plan_set")
+
+
+def plan_get(op: int, qtype: int, rows: int, cols: int, ncols: int) -> int:
+    plan = ctypes.c_int32(-1)
+    _check(lib.qg_plan_get(op, qtype, rows, cols, ncols, ctypes.addressof(plan)), "qg_plan_get")
+    return plan.value
+
+
+def plan_reset() -> None:
+    lib.qg_plan_reset()
 
 
 @dataclass

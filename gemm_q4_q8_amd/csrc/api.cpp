@@ -58,7 +58,7 @@ int check_out(const float *Y, int64_t ldy, int64_t len) {
 
 int qmv_common(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols, const float *X,
                int64_t ldx, int ncols, float *Y, int64_t ldy, int accumulate, void *ws, size_t ws_bytes,
-               void *stream, bool gemm16) {
+               void *stream, bool gemm16, bool tune = false, int32_t *plan = nullptr) {
   if (!qtype_ok(qtype)) return QG_EINVAL;
   int st = check_matrix(qs, d, rows, cols);
   if (st) return st;
@@ -88,7 +88,7 @@ int qmv_common(int qtype, const void *qs, const void *d, int64_t rows, int64_t c
   c.ws = ws;
   c.ws_bytes = ws_bytes;
   c.stream = (hipStream_t)stream;
-  return launch_qmv(c);
+  return tune ? tune_call(c, plan) : launch_qmv(c);
 }
 
 }  // namespace
@@ -201,7 +201,7 @@ int qgemm16(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols
 static int gateup_common(int qtype, const void *g_qs, const void *g_d, const void *u_qs, const void *u_d,
                          int64_t rows, int64_t cols, const float *X, int64_t ldx, int32_t ncols,
                          const float *gamma, float eps, float *H, int64_t ldh, void *ws, size_t ws_bytes,
-                         void *stream);
+                         void *stream, bool tune = false, int32_t *plan = nullptr);
 
 int gateup_silu(int qtype, const void *g_qs, const void *g_d, const void *u_qs, const void *u_d,
                 int64_t rows, int64_t cols, const float *X, int64_t ldx, int32_t ncols, float *H,
@@ -236,7 +236,7 @@ int qg_rmsnorm(const float *X, int64_t ldx, int64_t cols, int32_t ncols, const f
 static int gateup_common(int qtype, const void *g_qs, const void *g_d, const void *u_qs, const void *u_d,
                          int64_t rows, int64_t cols, const float *X, int64_t ldx, int32_t ncols,
                          const float *gamma, float eps, float *H, int64_t ldh, void *ws, size_t ws_bytes,
-                         void *stream) {
+                         void *stream, bool tune, int32_t *plan) {
   if (!qtype_ok(qtype)) return QG_EINVAL;
   int st = check_matrix(g_qs, g_d, rows, cols);
   if (st) return st;
@@ -269,12 +269,12 @@ static int gateup_common(int qtype, const void *g_qs, const void *g_d, const voi
   c.ws = ws;
   c.ws_bytes = ws_bytes;
   c.stream = (hipStream_t)stream;
-  return launch_qmv(c);
+  return tune ? tune_call(c, plan) : launch_qmv(c);
 }
 
-int lmhead_argmax(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols, int64_t n_rows,
-                  const float *x, int32_t *out_idx, float *out_val, void *ws, size_t ws_bytes,
-                  void *stream) {
+static int lmhead_argmax_common(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols,
+                                int64_t n_rows, const float *x, int32_t *out_idx, float *out_val, void *ws,
+                                size_t ws_bytes, void *stream, bool tune, int32_t *plan) {
   if (!qtype_ok(qtype)) return QG_EINVAL;
   int st = check_matrix(qs, d, rows, cols);
   if (st) return st;
@@ -304,7 +304,35 @@ int lmhead_argmax(int qtype, const void *qs, const void *d, int64_t rows, int64_
   c.ws = ws;
   c.ws_bytes = ws_bytes;
   c.stream = (hipStream_t)stream;
-  return launch_qmv(c);
+  return tune ? tune_call(c, plan) : launch_qmv(c);
+}
+
+int lmhead_argmax(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols, int64_t n_rows,
+                  const float *x, int32_t *out_idx, float *out_val, void *ws, size_t ws_bytes,
+                  void *stream) {
+  return lmhead_argmax_common(qtype, qs, d, rows, cols, n_rows, x, out_idx, out_val, ws, ws_bytes, stream,
+                              false, nullptr);
+}
+
+int qg_tune_lmhead(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols, int64_t n_rows,
+                   const float *x, int32_t *out_idx, float *out_val, void *ws, size_t ws_bytes, void *stream,
+                   int32_t *plan) {
+  return lmhead_argmax_common(qtype, qs, d, rows, cols, n_rows, x, out_idx, out_val, ws, ws_bytes, stream,
+                              true, plan);
+}
+
+int qg_tune_gemv(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols, const float *X,
+                 int64_t ldx, int32_t ncols, float *Y, int64_t ldy, void *ws, size_t ws_bytes, void *stream,
+                 int32_t *plan) {
+  return qmv_common(qtype, qs, d, rows, cols, X, ldx, ncols, Y, ldy, 0, ws, ws_bytes, stream, ncols == 16,
+                    true, plan);
+}
+
+int qg_tune_gateup(int qtype, const void *g_qs, const void *g_d, const void *u_qs, const void *u_d,
+                   int64_t rows, int64_t cols, const float *X, int64_t ldx, int32_t ncols, float *H,
+                   int64_t ldh, void *ws, size_t ws_bytes, void *stream, int32_t *plan) {
+  return gateup_common(qtype, g_qs, g_d, u_qs, u_d, rows, cols, X, ldx, ncols, nullptr, 0.0f, H, ldh, ws,
+                       ws_bytes, stream, true, plan);
 }
 
 int lmhead_topk(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols, int64_t n_rows,

@@ -33,7 +33,17 @@ struct QmvCall {
   void *ws;
   size_t ws_bytes;
   hipStream_t stream;
+  int plan;                 // 0: the plan table's entry (else the built-in choice)
 };
+
+// Launch plans of the product calls: 0 = the built-in choice; 1..16 = that
+// many waves per workgroup (segments across workgroups); QG_PLAN_SW = the
+// K segments inside one workgroup.  No plan changes a result bit (the
+// segments and their order are a function of the shape).  PLAN_FORCED
+// marks a plan fixed by the caller (the tuner), bypassing the table.
+constexpr int PLAN_W_MASK = 0x1F, PLAN_FORCED = 1 << 30;
+int plan_lookup(const QmvCall &c);                // tune.cpp
+int tune_call(QmvCall c, int32_t *plan_out);      // times the plans, stores the winner
 
 // K segments of the dot path: a function of the matrix shape (and of the
 // widest batch the entry point takes) only, so that every column count gives

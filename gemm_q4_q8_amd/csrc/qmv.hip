@@ -428,6 +428,9 @@ static int launch_dot(const QmvCall &c, int S) {
   const int64_t NTu = cdiv(c.n_rows, 16);
   constexpr bool MF = DOT_MF;
   const int W = dot_waves(NTu, S);
+  const int plan = c.plan & ~PLAN_FORCED;
+  bool sw_ok = false, sw = false;
+  int64_t R = 1;
   if (S > 1) {
     // The segments as waves of one workgroup, summed through LDS: no
     // partials in memory and no second round trip at the end (about 2-3 us
@@ -441,16 +444,30 @@ static int launch_dot(const QmvCall &c, int S) {
     // is then a large part of the time); the decode down projection stays
     // across workgroups (its waves would finish far apart).
     const int64_t ncu = device_cus();
-    const int64_t R = cdiv(NTu, ncu);
+    R = cdiv(NTu, ncu);
     const int64_t KT = cdiv(c.cols / 32, 4);
     constexpr int NI = MF ? (NC < 4 ? NC : 4) : NC;
     const size_t lds = (size_t)KT * TILE_BLOCKS * NC * 64 + (size_t)(S - 1) * R * NMAT * NI * 64 * 4;
     const int64_t u_sw = cdiv(NTu, R), u_cross = cdiv(NTu, (int64_t)W) * S;
     const int64_t cu_bytes = (int64_t)NMAT * R * KT * (QTraits<QT>::tile_bytes + TILE_D_BYTES);
-    bool sw = R * S <= 16 && lds <= DOT_SW_LDS &&
-              (dot_interleaved(c.cols) || 10 * u_sw >= 9 * u_cross || cu_bytes <= 196608);
-    if (sw) return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 16, RMSN>(c, 1, (int)(R * S), S);
+    sw_ok = R * S <= 16 && lds <= DOT_SW_LDS;
+    sw = sw_ok && (dot_interleaved(c.cols) || 10 * u_sw >= 9 * u_cross || cu_bytes <= 196608);
   }
+  // A plan from the plan table (or the tuner) replaces the choice above; it
+  // changes no sum (same segments, same order).
+  if (plan) {
+    if (plan & ~(PLAN_W_MASK | QG_PLAN_SW)) return QG_EUNSUPPORTED;
+    if (plan & QG_PLAN_SW) {
+      if (!sw_ok || (plan & PLAN_W_MASK)) return QG_EUNSUPPORTED;
+      sw = true;
+    } else {
+      const int Wp = plan & PLAN_W_MASK;
+      if (Wp > 16) return QG_EUNSUPPORTED;
+      if (Wp <= 8) return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 8, RMSN>(c, S, Wp);
+      return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 16, RMSN>(c, S, Wp);
+    }
+  }
+  if (sw) return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 16, RMSN>(c, 1, (int)(R * S), S);
   if (W <= 8) return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 8, RMSN>(c, S, W);
   return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 16, RMSN>(c, S, W);
 }
@@ -506,6 +523,11 @@ static int launch_gemm16(const QmvCall &c) {
       W = w;
       break;
     }
+  const int plan = c.plan & ~PLAN_FORCED;
+  if (plan) {
+    if (plan < 8 || plan > 16) return QG_EUNSUPPORTED;  // 8 to 16 waves, no in-workgroup segments
+    W = plan;
+  }
   if (W == 8) return launch_dot_t<QT, 16, 1, EPI, 1, 2, 8, true>(c, S);
   return launch_dot_t<QT, 16, 1, EPI, 1, 2, 0, true, 16>(c, S, W);
 }
@@ -531,10 +553,27 @@ static int dispatch_qt(const QmvCall &c) {
   return QG_EINVAL;
 }
 
-int launch_qmv(const QmvCall &c) {
+static int dispatch_qmv(const QmvCall &c) {
   if (c.qtype == QG_Q4_0) return dispatch_qt<Q4>(c);
   if (c.qtype == QG_Q8_0) return dispatch_qt<Q8>(c);
   return QG_EINVAL;
+}
+
+// The plan table's entry for this call, unless the caller fixed the plan;
+// an entry the call cannot use (refused before anything is launched) gives
+// way to the built-in choice, unless it is marked strict.
+int launch_qmv(const QmvCall &c0) {
+  QmvCall c = c0;
+  const bool forced = (c.plan & PLAN_FORCED) != 0;
+  if (!forced) c.plan = plan_lookup(c);
+  const bool strict = (c.plan & QG_PLAN_STRICT) != 0;
+  c.plan &= ~QG_PLAN_STRICT;
+  int st = dispatch_qmv(c);
+  if (st == QG_EUNSUPPORTED && !forced && !strict && c.plan) {
+    c.plan = 0;
+    st = dispatch_qmv(c);
+  }
+  return st;
 }
 
 }  // namespace qg

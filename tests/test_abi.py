@@ -19,7 +19,7 @@ FAKE = 1 << 40          # an aligned, never-dereferenced "device" address
 def _declared():
     src = open(os.path.join(ROOT, "include", "qgemm.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char)\s*\*?\s*(\w+)\s*\(", src, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char|void)\s*\*?\s*(\w+)\s*\(", src, re.M)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -268,3 +268,53 @@ def test_read_probe_checks():
     assert L.qg_read_probe(ctypes.c_void_p(4096), 0, sink, None) == ESHAPE
     assert L.qg_read_probe(ctypes.c_void_p(4096), 1000, sink, None) == ESHAPE
     assert L.qg_read_probe(ctypes.c_void_p(4104), 1024, sink, None) == EALIGN
+
+
+def test_plan_table():
+    """Plan entries: valid ops, shapes and plans only; set, get, reset."""
+    get = lambda *a: qg.plan_get(*a)
+    L.qg_plan_reset()
+    assert get(qg.OP_GEMV, 2, 64, 128, 1) == 0
+    for op, nc, plan in [(qg.OP_GEMV, 1, 4), (qg.OP_GEMV, 8, qg.PLAN_SW), (qg.OP_GEMV, 16, 12),
+                         (qg.OP_GATEUP, 3, 16), (qg.OP_LMHEAD, 1, 8 | qg.PLAN_STRICT)]:
+        assert L.qg_plan_set(op, 2, 64, 128, nc, plan) == OK
+        assert get(op, 2, 64, 128, nc) == plan
+    assert get(qg.OP_GEMV, 8, 64, 128, 1) == 0           # other qtype: no entry
+    bad = [(3, 2, 64, 128, 1, 0),                          # op
+           (qg.OP_GEMV, 3, 64, 128, 1, 0),                 # qtype
+           (qg.OP_GEMV, 2, 64, 100, 1, 0),                 # cols % 32
+           (qg.OP_GEMV, 2, 0, 128, 1, 0),                  # rows
+           (qg.OP_GEMV, 2, 64, 128, 9, 0),                 # ncols
+           (qg.OP_GATEUP, 2, 64, 128, 16, 0),
+           (qg.OP_LMHEAD, 2, 64, 128, 2, 0),
+           (qg.OP_GEMV, 2, 64, 128, 1, 17),                # plans
+           (qg.OP_GEMV, 2, 64, 128, 1, -1),
+           (qg.OP_GEMV, 2, 64, 128, 1, 0x400),
+           (qg.OP_GEMV, 2, 64, 128, 1, qg.PLAN_SW | 4),
+           (qg.OP_GEMV, 2, 64, 128, 1, qg.PLAN_STRICT),
+           (qg.OP_GEMV, 2, 64, 128, 16, 4),                # 16 columns: 8..16 waves
+           (qg.OP_GEMV, 2, 64, 128, 16, qg.PLAN_SW)]
+    for a in bad:
+        assert L.qg_plan_set(*a) == EINVAL, a
+    assert L.qg_plan_get(qg.OP_GEMV, 2, 64, 128, 1, None) == EINVAL
+    L.qg_plan_reset()
+    assert get(qg.OP_GEMV, 2, 64, 128, 1) == 0
+    assert get(qg.OP_GATEUP, 2, 64, 128, 3) == 0
+
+
+def test_tune_argument_checks():
+    """The tuning calls check their arguments as the calls they tune (before
+    any HIP call)."""
+    ws, X, Y = FAKE + (3 << 20), FAKE + (1 << 20), FAKE + (2 << 20)
+    tg = lambda **k: L.qg_tune_gemv(k.get("qt", 2), k.get("qs", FAKE), FAKE, 64, 128, X, 128, k.get("nc", 1),
+                                    k.get("Y", Y), 64, ws, 1 << 20, None, None)
+    assert tg(qs=None) == EINVAL
+    assert tg(qt=3) == EINVAL
+    assert tg(nc=9) == ESHAPE
+    assert tg(Y=X + 64) == EINVAL
+    assert L.qg_tune_gateup(2, FAKE, FAKE, None, FAKE, 64, 128, X, 128, 1, Y, 64, ws, 1 << 20, None,
+                            None) == EINVAL
+    assert L.qg_tune_gateup(2, FAKE, FAKE, FAKE, FAKE, 64, 128, X, 128, 1, Y, 64, ws, 16, None,
+                            None) == EWS
+    assert L.qg_tune_lmhead(2, FAKE, FAKE, 64, 128, 65, X, Y, None, ws, 1 << 20, None, None) == ESHAPE
+    assert L.qg_tune_lmhead(2, FAKE, FAKE, 64, 128, 64, X, None, None, ws, 1 << 20, None, None) == EINVAL

@@ -609,3 +609,153 @@ def test_moe_repeat_bitwise(env):
         Y = torch.zeros((16, 256), device=dev)
         qg.moe_ffn(m, X, Y)
         assert torch.equal(Y, Y0)
+
+
+# ------------------------------------------------------------ launch plans
+def _under_plans(env, op, qtype, rows, cols, nc, call, plans):
+    """call() (host arrays) with the built-in plan, then under each plan
+    pinned strict (None where the call refuses it)."""
+    torch, qg, dev = env
+    qg.plan_reset()
+    base = call()
+    out = {}
+    try:
+        for p in plans:
+            qg.plan_set(op, qtype, rows, cols, nc, p | qg.PLAN_STRICT)
+            try:
+                out[p] = call()
+            except qg.QGError as e:
+                assert e.status == -4, e            # QG_EUNSUPPORTED, refused before launching
+                out[p] = None
+    finally:
+        qg.plan_reset()
+    return base, out
+
+
+def _same_bits(base, out, may_refuse):
+    applied = [p for p, o in out.items() if o is not None]
+    say(f"  plans applied {applied}, refused {[p for p in out if p not in applied]}")
+    assert len(applied) >= len(out) - len(may_refuse)
+    for p, o in out.items():
+        if o is None:
+            assert p in may_refuse, p
+            continue
+        for a, b in zip(base, o):
+            assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                                  b.view(np.uint32) if b.dtype == np.float32 else b), p
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("rows,cols", [(300, 1024), (64, 8192), (2100, 2048), (600, 11264)])
+@pytest.mark.parametrize("ncols", [1, 5])
+def test_plans_gemv_same_bits(env, qtype, rows, cols, ncols):
+    """Every launch plan (4 / 8 / 12 / 16 waves, in-workgroup segments) gives
+    the built-in plan's bits, storing and accumulating; only in-workgroup
+    segments may be refused, and the result matches the oracle."""
+    torch, qg, dev = env
+    say(f"plans gemv qtype={qtype} {rows}x{cols} ncols={ncols}")
+    raw, W = make(env, qtype, rows, cols, seed=rows + cols + ncols)
+    X = synth.gen_x(cols, ncols, cfg_id=rows * 3 + cols)
+    Xd = up(env, X.T)
+    y0 = synth.rng(5, rows).standard_normal((ncols, rows)).astype(np.float32)
+
+    def call():
+        Y = qg.qgemv(W, Xd)
+        Ya = qg.qgemv(W, Xd, up(env, y0), accumulate=True)
+        return Y.cpu().numpy(), Ya.cpu().numpy()
+
+    plans = [4, 8, 12, 16, qg.PLAN_SW]
+    base, out = _under_plans(env, qg.OP_GEMV, qtype, rows, cols, ncols, call, plans)
+    _same_bits(base, out, {qg.PLAN_SW})
+    ref, a = ops.gemv(qtype, raw, X)
+    assert_tol(base[0].astype(np.float64).T, ref, ops.tol_dot(a), "gemv")
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("rows,cols", [(300, 1024), (2100, 2048)])
+def test_plans_gemm16_same_bits(env, qtype, rows, cols):
+    torch, qg, dev = env
+    say(f"plans gemm16 qtype={qtype} {rows}x{cols}")
+    raw, W = make(env, qtype, rows, cols, seed=rows + cols + 16)
+    X = synth.gen_x(cols, 16, cfg_id=rows + 5 * cols)
+    Xd = up(env, X.T)
+    base, out = _under_plans(env, qg.OP_GEMV, qtype, rows, cols, 16,
+                             lambda: (qg.qgemm16(W, Xd).cpu().numpy(),), [8, 12, 16])
+    _same_bits(base, out, set())
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("rows,cols,ncols", [(300, 1024, 1), (1000, 5120, 3), (700, 8192, 1)])
+def test_plans_gateup_same_bits(env, qtype, rows, cols, ncols):
+    torch, qg, dev = env
+    say(f"plans gateup qtype={qtype} {rows}x{cols} ncols={ncols}")
+    _, G = make(env, qtype, rows, cols, seed=rows + cols + 2)
+    _, U = make(env, qtype, rows, cols, seed=rows + cols + 3)
+    X = synth.gen_x(cols, ncols, cfg_id=rows + 7 * cols)
+    Xd = up(env, X.T)
+    base, out = _under_plans(env, qg.OP_GATEUP, qtype, rows, cols, ncols,
+                             lambda: (qg.gateup_silu(G, U, Xd).cpu().numpy(),), [4, 8, 12, 16, qg.PLAN_SW])
+    _same_bits(base, out, {qg.PLAN_SW})
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("rows,cols", [(5000, 1024), (300, 2048)])
+def test_plans_lmhead_same_bits(env, qtype, rows, cols):
+    """Argmax and top-k under every plan: the same rows and value bits."""
+    torch, qg, dev = env
+    say(f"plans lmhead qtype={qtype} {rows}x{cols}")
+    raw, W = _lm_case(env, qtype, rows, cols, seed=rows + cols)
+    x = up(env, synth.gen_x(cols, 1, cfg_id=rows)[:, 0])
+
+    def call():
+        i, v = qg.lmhead_argmax(W, x)
+        ti, tv = qg.lmhead_topk(W, x, 5)
+        return i.cpu().numpy(), v.cpu().numpy(), ti.cpu().numpy(), tv.cpu().numpy()
+
+    base, out = _under_plans(env, qg.OP_LMHEAD, qtype, rows, cols, 1, call, [4, 8, 12, 16, qg.PLAN_SW])
+    _same_bits(base, out, {qg.PLAN_SW})
+
+
+def test_tune_keeps_bits_and_fills_the_table(env):
+    """The tuners return a candidate plan, store it for the shape, leave the
+    built-in plan's outputs, and later calls keep those bits."""
+    torch, qg, dev = env
+    qg.plan_reset()
+    try:
+        rows, cols = 2100, 2048
+        raw, W = make(env, Q4, rows, cols, seed=31)
+        X = up(env, synth.gen_x(cols, 2, cfg_id=3).T)
+        base = qg.qgemv(W, X).cpu().numpy()
+        p = qg.tune_gemv(W, X)
+        say(f"  tuned gemv plan {p}")
+        assert p in (0, 4, 8, 12, 16, qg.PLAN_SW)
+        assert qg.plan_get(qg.OP_GEMV, Q4, rows, cols, 2) == p
+        Y = torch.full((2, rows), 7.0, device=dev)
+        qg.tune_gemv(W, X, Y)                         # stores, never accumulates
+        assert np.array_equal(Y.cpu().numpy().view(np.uint32), base.view(np.uint32))
+        assert np.array_equal(qg.qgemv(W, X).cpu().numpy().view(np.uint32), base.view(np.uint32))
+
+        X16 = up(env, synth.gen_x(cols, 16, cfg_id=4).T)
+        b16 = qg.qgemm16(W, X16).cpu().numpy()
+        p16 = qg.tune_gemv(W, X16)
+        assert p16 in (0, 8, 12, 16)
+        assert np.array_equal(qg.qgemm16(W, X16).cpu().numpy().view(np.uint32), b16.view(np.uint32))
+
+        _, G = make(env, Q8, 1000, 5120, seed=32)
+        _, U = make(env, Q8, 1000, 5120, seed=34)
+        x1 = up(env, synth.gen_x(5120, 1, cfg_id=5).T)
+        hb = qg.gateup_silu(G, U, x1).cpu().numpy()
+        pg = qg.tune_gateup(G, U, x1)
+        assert qg.plan_get(qg.OP_GATEUP, Q8, 1000, 5120, 1) == pg
+        assert np.array_equal(qg.gateup_silu(G, U, x1).cpu().numpy().view(np.uint32), hb.view(np.uint32))
+
+        raw3, W3 = _lm_case(env, Q8, 5000, 1024, seed=33)
+        x3 = up(env, synth.gen_x(1024, 1, cfg_id=6)[:, 0])
+        i0, v0 = (t.cpu().numpy() for t in qg.lmhead_argmax(W3, x3))
+        pl = qg.tune_lmhead(W3, x3)
+        assert qg.plan_get(qg.OP_LMHEAD, Q8, 5000, 1024, 1) == pl
+        i1, v1 = (t.cpu().numpy() for t in qg.lmhead_argmax(W3, x3))
+        assert i0[0] == i1[0] and v0.view(np.uint32)[0] == v1.view(np.uint32)[0]
+        say(f"  tuned plans: gemv {p}, gemm16 {p16}, gateup {pg}, lmhead {pl}")
+    finally:
+        qg.plan_reset()
