@@ -267,6 +267,59 @@ def run_extras(B, kernels):
     log("  moe done")
 
 
+def run_plans(B, kernels):
+    """Each launch plan timed at the benchmarked decode shapes (the built-in
+    choice, 4 / 8 / 12 / 16 waves per workgroup, K segments inside one
+    workgroup), and the plan the tuner keeps there."""
+    torch, qg = B.torch, B.qg
+    import synth
+    Q4 = qg.Q4_0
+    cands = [4, 8, 12, 16, qg.PLAN_SW]
+
+    def sweep(op, w, ncols, mk_fns, iters, plans):
+        us = {}
+        for pl in [0] + plans:
+            qg.plan_reset()
+            if pl:
+                qg.plan_set(op, w.qtype, w.rows, w.cols, ncols, pl | qg.PLAN_STRICT)
+            key = "builtin" if pl == 0 else ("sw" if pl == qg.PLAN_SW else str(pl))
+            try:
+                t, _ = B.graph_time(mk_fns(), iters)   # a refused plan raises in the eager warm-up
+                us[key] = round(t * 1e6, 2)
+            except qg.QGError:
+                us[key] = None
+        qg.plan_reset()
+        return us
+
+    N, K = 17408, 5120
+    for nm, rows, cols, ncols in (("gateup_silu_q4_0_5120to2x17408_1col", N, K, 1),
+                                  ("down_q4_0_17408to5120_1col", K, N, 1),
+                                  ("verify_q4_0_5120to17408_4col", N, K, 4),
+                                  ("verify_q4_0_5120to17408_8col", N, K, 8),
+                                  ("gemm16_q4_0_5120to17408", N, K, 16)):
+        w, _ = B.matrix(Q4, rows, cols, seed=61, sigma=0.02)
+        gate = nm.startswith("gateup")
+        p = B.pool(w, qbytes(Q4, rows, cols))     # gate/up: distinct pairs (2i, 2i + 1)
+        x = B.up(synth.gen_x(cols, ncols, cfg_id=6).T)
+        y = torch.empty((ncols, rows), device=B.dev)
+        if gate:
+            fns = lambda: [lambda i=i: qg.gateup_silu(p[2 * i], p[2 * i + 1], x, y) for i in range(len(p) // 2)]
+            us = sweep(qg.OP_GATEUP, w, ncols, fns, len(p), cands)
+            tuned = qg.tune_gateup(p[0], p[1], x, y)
+        elif ncols == 16:
+            fns = lambda: [lambda m=m: qg.qgemm16(m, x, y) for m in p]
+            us = sweep(qg.OP_GEMV, w, ncols, fns, 2 * len(p), [8, 12, 16])
+            tuned = qg.tune_gemv(p[0], x, y)
+        else:
+            fns = lambda: [lambda m=m: qg.qgemv(m, x, y) for m in p]
+            us = sweep(qg.OP_GEMV, w, ncols, fns, 2 * len(p), cands)
+            tuned = qg.tune_gemv(p[0], x, y)
+        qg.plan_reset()
+        kernels[f"plans_{nm}"] = {"us": us, "tuned_plan": tuned}
+        del p
+    log("  plans done")
+
+
 def ceilings(B):
     """Measured denominators beside the 8 TB/s spec, timed the same way:
     a plain device copy of 1 GiB (read + write), and the library's
@@ -402,6 +455,7 @@ def main():
     if args.suite == "all":
         log("bench: other workloads")
         run_extras(B, kernels)
+        run_plans(B, kernels)
     achieved = gu_bytes / t_gu / 1e9
     out = {
         "metric": "Q4_0/Q8_0 GEMV+GEMM achieved HBM GB/s and % of MI355X peak",
