@@ -84,11 +84,11 @@ _SIGS = {
                                _vp, _sz, _vp]),
     "qg_read_probe": (ctypes.c_int, [_vp, _sz, _vp, _vp]),
     "qg_tune_gemv": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _i64, _i64, _vp, _i64, _i32, _vp, _i64,
-                                    _vp, _sz, _vp, _vp]),
+                                    _vp, _sz, _vp, _i32, _vp]),
     "qg_tune_gateup": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _i32,
-                                      _vp, _i64, _vp, _sz, _vp, _vp]),
+                                      _vp, _i64, _vp, _sz, _vp, _i32, _vp]),
     "qg_tune_lmhead": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp,
-                                      _vp, _sz, _vp, _vp]),
+                                      _vp, _sz, _vp, _i32, _vp]),
     "qg_plan_set": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _i64, _i64, _i32, _i32]),
     "qg_plan_get": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _i64, _i64, _i32, _vp]),
     "qg_plan_reset": (None, []),
@@ -372,12 +372,18 @@ def lmhead_topk(w: QMatrix, x, k: int, n_rows: Optional[int] = None, out_idx=Non
 OP_GEMV, OP_GATEUP, OP_LMHEAD = 0, 1, 2
 PLAN_SW = 0x100
 PLAN_STRICT = 0x200
+TUNE_SPLIT = 1
 
 
-def tune_gemv(w: QMatrix, X, Y=None) -> int:
+def PLAN_SPLIT(s: int) -> int:
+    """Plan bits for s K segments instead of the shape's own."""
+    return s << 12
+
+
+def tune_gemv(w: QMatrix, X, Y=None, split: bool = False) -> int:
     """Times the launch plans of qgemv (1..8 columns) or qgemm16 (16) on
-    these buffers, keeps the winner for this shape and column count, and
-    returns it; Y ends holding W X."""
+    these buffers (with split: K splits too), keeps the winner for this
+    shape and column count, and returns it; Y ends holding W X."""
     torch = _torch()
     _check_dev(X)
     X2 = X if X.dim() == 2 else X.view(1, -1)
@@ -390,11 +396,11 @@ def tune_gemv(w: QMatrix, X, Y=None) -> int:
     plan = ctypes.c_int32(-1)
     _check(lib.qg_tune_gemv(w.qtype, w.qs.data_ptr(), w.d.data_ptr(), w.rows, w.cols, X2.data_ptr(), _ld(X2),
                             ncols, Y2.data_ptr(), _ld(Y2), ws.data_ptr(), ws.numel(), _stream(X.device),
-                            ctypes.addressof(plan)), "qg_tune_gemv")
+                            int(split), ctypes.addressof(plan)), "qg_tune_gemv")
     return plan.value
 
 
-def tune_gateup(wg: QMatrix, wu: QMatrix, X, H=None) -> int:
+def tune_gateup(wg: QMatrix, wu: QMatrix, X, H=None, split: bool = False) -> int:
     """As tune_gemv for gateup_silu; H ends holding the gated product."""
     torch = _torch()
     _check_dev(X)
@@ -407,12 +413,12 @@ def tune_gateup(wg: QMatrix, wu: QMatrix, X, H=None) -> int:
     plan = ctypes.c_int32(-1)
     _check(lib.qg_tune_gateup(wg.qtype, wg.qs.data_ptr(), wg.d.data_ptr(), wu.qs.data_ptr(), wu.d.data_ptr(),
                               wg.rows, wg.cols, X2.data_ptr(), _ld(X2), ncols, H2.data_ptr(), _ld(H2),
-                              ws.data_ptr(), ws.numel(), _stream(X.device), ctypes.addressof(plan)),
+                              ws.data_ptr(), ws.numel(), _stream(X.device), int(split), ctypes.addressof(plan)),
            "qg_tune_gateup")
     return plan.value
 
 
-def tune_lmhead(w: QMatrix, x, n_rows: Optional[int] = None) -> int:
+def tune_lmhead(w: QMatrix, x, n_rows: Optional[int] = None, split: bool = False) -> int:
     """As tune_gemv for lmhead_argmax (the entry serves lmhead_topk too)."""
     torch = _torch()
     _check_dev(x)
@@ -423,7 +429,7 @@ def tune_lmhead(w: QMatrix, x, n_rows: Optional[int] = None) -> int:
     _check(lib.qg_tune_lmhead(w.qtype, w.qs.data_ptr(), w.d.data_ptr(), w.rows, w.cols,
                               w.rows if n_rows is None else n_rows, x.data_ptr(), out_idx.data_ptr(),
                               out_val.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x.device),
-                              ctypes.addressof(plan)), "qg_tune_lmhead")
+                              int(split), ctypes.addressof(plan)), "qg_tune_lmhead")
     return plan.value
 
 

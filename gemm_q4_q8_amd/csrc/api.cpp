@@ -58,7 +58,7 @@ int check_out(const float *Y, int64_t ldy, int64_t len) {
 
 int qmv_common(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols, const float *X,
                int64_t ldx, int ncols, float *Y, int64_t ldy, int accumulate, void *ws, size_t ws_bytes,
-               void *stream, bool gemm16, bool tune = false, int32_t *plan = nullptr) {
+               void *stream, bool gemm16, bool tune = false, int32_t flags = 0, int32_t *plan = nullptr) {
   if (!qtype_ok(qtype)) return QG_EINVAL;
   int st = check_matrix(qs, d, rows, cols);
   if (st) return st;
@@ -88,7 +88,7 @@ int qmv_common(int qtype, const void *qs, const void *d, int64_t rows, int64_t c
   c.ws = ws;
   c.ws_bytes = ws_bytes;
   c.stream = (hipStream_t)stream;
-  return tune ? tune_call(c, plan) : launch_qmv(c);
+  return tune ? tune_call(c, flags, plan) : launch_qmv(c);
 }
 
 }  // namespace
@@ -153,29 +153,45 @@ int qg_requant_q8_0(int src_type, int64_t n_blocks, const void *src, void *dst, 
   return launch_requant_q8_0(src_type, n_blocks, src, dst, stream);
 }
 
+// Workspace queries leave room for a plan's K split of up to twice the
+// shape's own (the calls themselves need only the shape's own).
+static int split_room(int S, int64_t cols) {
+  const int64_t KT = (cols / 32 + 3) / 4;
+  const int64_t r = 2 * (int64_t)S;
+  return (int)(r < KT ? r : (KT > S ? KT : S));
+}
+
+// The least workspace each call takes (its shape's own split).
+static size_t gateup_ws_min(int64_t rows, int64_t cols) {
+  return qmv_ws_bytes(rows, cols, gemv_segments(rows, cols, 2, 8), 2, 8, false);
+}
+static size_t lmhead_ws_min(int64_t rows, int64_t cols, int32_t k) {
+  return qmv_ws_bytes(rows, cols, gemv_segments(rows, cols, 1, 1), 1, 1, k == 0, k);
+}
+
 size_t qg_gemv_ws_bytes(int64_t rows, int64_t cols) {
   if (rows <= 0 || cols <= 0 || cols % 32) return 0;
-  return qmv_ws_bytes(rows, cols, gemv_segments(rows, cols, 1, 8), 1, 8, false);
+  return qmv_ws_bytes(rows, cols, split_room(gemv_segments(rows, cols, 1, 8), cols), 1, 8, false);
 }
 
 size_t qg_gateup_ws_bytes(int64_t rows, int64_t cols) {
   if (rows <= 0 || cols <= 0 || cols % 32) return 0;
-  return qmv_ws_bytes(rows, cols, gemv_segments(rows, cols, 2, 8), 2, 8, false);
+  return qmv_ws_bytes(rows, cols, split_room(gemv_segments(rows, cols, 2, 8), cols), 2, 8, false);
 }
 
 size_t qg_gemm16_ws_bytes(int qtype, int64_t rows, int64_t cols) {
   if (!qtype_ok(qtype) || rows <= 0 || cols <= 0 || cols % 32) return 0;
-  return qmv_ws_bytes(rows, cols, gemm16_splits(rows, cols), 1, 16, false);
+  return qmv_ws_bytes(rows, cols, split_room(gemm16_splits(rows, cols), cols), 1, 16, false);
 }
 
 size_t qg_lmhead_ws_bytes(int64_t rows, int64_t cols) {
   if (rows <= 0 || cols <= 0 || cols % 32) return 0;
-  return qmv_ws_bytes(rows, cols, gemv_segments(rows, cols, 1, 1), 1, 1, true);
+  return qmv_ws_bytes(rows, cols, split_room(gemv_segments(rows, cols, 1, 1), cols), 1, 1, true);
 }
 
 size_t qg_lmhead_topk_ws_bytes(int64_t rows, int64_t cols, int32_t k) {
   if (rows <= 0 || cols <= 0 || cols % 32 || k < 1 || k > QG_TOPK_MAX) return 0;
-  return qmv_ws_bytes(rows, cols, gemv_segments(rows, cols, 1, 1), 1, 1, false, k);
+  return qmv_ws_bytes(rows, cols, split_room(gemv_segments(rows, cols, 1, 1), cols), 1, 1, false, k);
 }
 
 int qgemv_q4_0(const void *qs, const void *d, int64_t rows, int64_t cols, const float *X, int64_t ldx,
@@ -201,7 +217,7 @@ int qgemm16(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols
 static int gateup_common(int qtype, const void *g_qs, const void *g_d, const void *u_qs, const void *u_d,
                          int64_t rows, int64_t cols, const float *X, int64_t ldx, int32_t ncols,
                          const float *gamma, float eps, float *H, int64_t ldh, void *ws, size_t ws_bytes,
-                         void *stream, bool tune = false, int32_t *plan = nullptr);
+                         void *stream, bool tune = false, int32_t flags = 0, int32_t *plan = nullptr);
 
 int gateup_silu(int qtype, const void *g_qs, const void *g_d, const void *u_qs, const void *u_d,
                 int64_t rows, int64_t cols, const float *X, int64_t ldx, int32_t ncols, float *H,
@@ -236,7 +252,7 @@ int qg_rmsnorm(const float *X, int64_t ldx, int64_t cols, int32_t ncols, const f
 static int gateup_common(int qtype, const void *g_qs, const void *g_d, const void *u_qs, const void *u_d,
                          int64_t rows, int64_t cols, const float *X, int64_t ldx, int32_t ncols,
                          const float *gamma, float eps, float *H, int64_t ldh, void *ws, size_t ws_bytes,
-                         void *stream, bool tune, int32_t *plan) {
+                         void *stream, bool tune, int32_t flags, int32_t *plan) {
   if (!qtype_ok(qtype)) return QG_EINVAL;
   int st = check_matrix(g_qs, g_d, rows, cols);
   if (st) return st;
@@ -245,7 +261,7 @@ static int gateup_common(int qtype, const void *g_qs, const void *g_d, const voi
   if ((st = check_act(X, ldx, cols, ncols))) return st;
   if ((st = check_out(H, ldh, rows))) return st;
   if (overlap(span(X, ldx, cols, ncols), span(H, ldh, rows, ncols))) return QG_EINVAL;
-  if (!ws || ws_bytes < qg_gateup_ws_bytes(rows, cols)) return QG_EWORKSPACE;
+  if (!ws || ws_bytes < gateup_ws_min(rows, cols)) return QG_EWORKSPACE;
   if (!aligned(ws, 256)) return QG_EALIGN;
   QmvCall c;
   memset(&c, 0, sizeof(c));
@@ -269,12 +285,12 @@ static int gateup_common(int qtype, const void *g_qs, const void *g_d, const voi
   c.ws = ws;
   c.ws_bytes = ws_bytes;
   c.stream = (hipStream_t)stream;
-  return tune ? tune_call(c, plan) : launch_qmv(c);
+  return tune ? tune_call(c, flags, plan) : launch_qmv(c);
 }
 
 static int lmhead_argmax_common(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols,
                                 int64_t n_rows, const float *x, int32_t *out_idx, float *out_val, void *ws,
-                                size_t ws_bytes, void *stream, bool tune, int32_t *plan) {
+                                size_t ws_bytes, void *stream, bool tune, int32_t flags, int32_t *plan) {
   if (!qtype_ok(qtype)) return QG_EINVAL;
   int st = check_matrix(qs, d, rows, cols);
   if (st) return st;
@@ -282,7 +298,7 @@ static int lmhead_argmax_common(int qtype, const void *qs, const void *d, int64_
   if ((st = check_act(x, cols, cols, 1))) return st;
   if (!out_idx) return QG_EINVAL;
   if (!aligned(out_idx, 4) || (out_val && !aligned(out_val, 4))) return QG_EALIGN;
-  if (!ws || ws_bytes < qg_lmhead_ws_bytes(rows, cols)) return QG_EWORKSPACE;
+  if (!ws || ws_bytes < lmhead_ws_min(rows, cols, 0)) return QG_EWORKSPACE;
   if (!aligned(ws, 256)) return QG_EALIGN;
   QmvCall c;
   memset(&c, 0, sizeof(c));
@@ -304,35 +320,35 @@ static int lmhead_argmax_common(int qtype, const void *qs, const void *d, int64_
   c.ws = ws;
   c.ws_bytes = ws_bytes;
   c.stream = (hipStream_t)stream;
-  return tune ? tune_call(c, plan) : launch_qmv(c);
+  return tune ? tune_call(c, flags, plan) : launch_qmv(c);
 }
 
 int lmhead_argmax(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols, int64_t n_rows,
                   const float *x, int32_t *out_idx, float *out_val, void *ws, size_t ws_bytes,
                   void *stream) {
   return lmhead_argmax_common(qtype, qs, d, rows, cols, n_rows, x, out_idx, out_val, ws, ws_bytes, stream,
-                              false, nullptr);
+                              false, 0, nullptr);
 }
 
 int qg_tune_lmhead(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols, int64_t n_rows,
                    const float *x, int32_t *out_idx, float *out_val, void *ws, size_t ws_bytes, void *stream,
-                   int32_t *plan) {
+                   int32_t flags, int32_t *plan) {
   return lmhead_argmax_common(qtype, qs, d, rows, cols, n_rows, x, out_idx, out_val, ws, ws_bytes, stream,
-                              true, plan);
+                              true, flags, plan);
 }
 
 int qg_tune_gemv(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols, const float *X,
                  int64_t ldx, int32_t ncols, float *Y, int64_t ldy, void *ws, size_t ws_bytes, void *stream,
-                 int32_t *plan) {
+                 int32_t flags, int32_t *plan) {
   return qmv_common(qtype, qs, d, rows, cols, X, ldx, ncols, Y, ldy, 0, ws, ws_bytes, stream, ncols == 16,
-                    true, plan);
+                    true, flags, plan);
 }
 
 int qg_tune_gateup(int qtype, const void *g_qs, const void *g_d, const void *u_qs, const void *u_d,
                    int64_t rows, int64_t cols, const float *X, int64_t ldx, int32_t ncols, float *H,
-                   int64_t ldh, void *ws, size_t ws_bytes, void *stream, int32_t *plan) {
+                   int64_t ldh, void *ws, size_t ws_bytes, void *stream, int32_t flags, int32_t *plan) {
   return gateup_common(qtype, g_qs, g_d, u_qs, u_d, rows, cols, X, ldx, ncols, nullptr, 0.0f, H, ldh, ws,
-                       ws_bytes, stream, true, plan);
+                       ws_bytes, stream, true, flags, plan);
 }
 
 int lmhead_topk(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols, int64_t n_rows,
@@ -346,7 +362,7 @@ int lmhead_topk(int qtype, const void *qs, const void *d, int64_t rows, int64_t 
   if ((st = check_act(x, cols, cols, 1))) return st;
   if (!out_idx) return QG_EINVAL;
   if (!aligned(out_idx, 4) || (out_val && !aligned(out_val, 4))) return QG_EALIGN;
-  if (!ws || ws_bytes < qg_lmhead_topk_ws_bytes(rows, cols, k)) return QG_EWORKSPACE;
+  if (!ws || ws_bytes < lmhead_ws_min(rows, cols, k)) return QG_EWORKSPACE;
   if (!aligned(ws, 256)) return QG_EALIGN;
   QmvCall c;
   memset(&c, 0, sizeof(c));

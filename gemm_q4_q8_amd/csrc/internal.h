@@ -42,8 +42,10 @@ struct QmvCall {
 // segments and their order are a function of the shape).  PLAN_FORCED
 // marks a plan fixed by the caller (the tuner), bypassing the table.
 constexpr int PLAN_W_MASK = 0x1F, PLAN_FORCED = 1 << 30;
+constexpr int PLAN_S_SHIFT = 12, PLAN_S_MASK = 0xFF << PLAN_S_SHIFT;  // K segments (0: the shape's own)
 int plan_lookup(const QmvCall &c);                // tune.cpp
-int tune_call(QmvCall c, int32_t *plan_out);      // times the plans, stores the winner
+int builtin_split(const QmvCall &c);              // the shape's own K segments for this call
+int tune_call(QmvCall c, int32_t flags, int32_t *plan_out);  // times the plans, stores the winner
 
 // K segments of the dot path: a function of the matrix shape (and of the
 // widest batch the entry point takes) only, so that every column count gives

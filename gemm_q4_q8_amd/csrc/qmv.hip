@@ -428,7 +428,7 @@ static int launch_dot(const QmvCall &c, int S) {
   const int64_t NTu = cdiv(c.n_rows, 16);
   constexpr bool MF = DOT_MF;
   const int W = dot_waves(NTu, S);
-  const int plan = c.plan & ~PLAN_FORCED;
+  const int plan = c.plan & ~(PLAN_FORCED | PLAN_S_MASK);
   bool sw_ok = false, sw = false;
   int64_t R = 1;
   if (S > 1) {
@@ -513,7 +513,8 @@ static int dispatch_silu(const QmvCall &c, int S) {
 // per-chunk barrier, so the smallest size that keeps one per CU).
 template <int QT, int EPI>
 static int launch_gemm16(const QmvCall &c) {
-  const int S = gemm16_splits(c.rows, c.cols);
+  const int Sp = (c.plan & PLAN_S_MASK) >> PLAN_S_SHIFT;
+  const int S = Sp ? Sp : gemm16_splits(c.rows, c.cols);
   // at least 8 waves (the activation chunks are sized for them), else as
   // for the GEMV: one workgroup per CU when 8 to 16 waves allow it
   const int64_t NTu = cdiv(c.n_rows, 16), ncu = device_cus();
@@ -523,7 +524,7 @@ static int launch_gemm16(const QmvCall &c) {
       W = w;
       break;
     }
-  const int plan = c.plan & ~PLAN_FORCED;
+  const int plan = c.plan & ~(PLAN_FORCED | PLAN_S_MASK);
   if (plan) {
     if (plan < 8 || plan > 16) return QG_EUNSUPPORTED;  // 8 to 16 waves, no in-workgroup segments
     W = plan;
@@ -534,23 +535,35 @@ static int launch_gemm16(const QmvCall &c) {
 
 template <int QT>
 static int dispatch_qt(const QmvCall &c) {
+  // a plan's K segments replace the shape's own (a different summation
+  // order: the sums change by rounding only)
+  const int Sp = (c.plan & PLAN_S_MASK) >> PLAN_S_SHIFT;
+  if (Sp > cdiv(c.cols / 32, 4)) return QG_EUNSUPPORTED;
+  auto seg = [Sp](int S) { return Sp ? Sp : S; };
   if (c.ncols == 16) {
     if (c.epi == EPI_STORE) return launch_gemm16<QT, EPI_STORE>(c);
     if (c.epi == EPI_ACC) return launch_gemm16<QT, EPI_ACC>(c);
     return QG_EUNSUPPORTED;
   }
   switch (c.epi) {
-    case EPI_STORE: return dispatch_dot<QT, EPI_STORE>(c, gemv_segments(c.rows, c.cols, 1, 8));
-    case EPI_ACC: return dispatch_dot<QT, EPI_ACC>(c, gemv_segments(c.rows, c.cols, 1, 8));
-    case EPI_SILU: return dispatch_silu<QT>(c, gemv_segments(c.rows, c.cols, 2, 8));
+    case EPI_STORE: return dispatch_dot<QT, EPI_STORE>(c, seg(gemv_segments(c.rows, c.cols, 1, 8)));
+    case EPI_ACC: return dispatch_dot<QT, EPI_ACC>(c, seg(gemv_segments(c.rows, c.cols, 1, 8)));
+    case EPI_SILU: return dispatch_silu<QT>(c, seg(gemv_segments(c.rows, c.cols, 2, 8)));
     case EPI_ARGMAX:
       if (c.ncols != 1) return QG_ESHAPE;
-      return launch_dot<QT, 1, 1, EPI_ARGMAX>(c, gemv_segments(c.rows, c.cols, 1, 1));
+      return launch_dot<QT, 1, 1, EPI_ARGMAX>(c, seg(gemv_segments(c.rows, c.cols, 1, 1)));
     case EPI_TOPK:
       if (c.ncols != 1) return QG_ESHAPE;
-      return launch_dot<QT, 1, 1, EPI_TOPK>(c, gemv_segments(c.rows, c.cols, 1, 1));
+      return launch_dot<QT, 1, 1, EPI_TOPK>(c, seg(gemv_segments(c.rows, c.cols, 1, 1)));
   }
   return QG_EINVAL;
+}
+
+int builtin_split(const QmvCall &c) {
+  if (c.ncols == 16) return gemm16_splits(c.rows, c.cols);
+  if (c.epi == EPI_SILU) return gemv_segments(c.rows, c.cols, 2, 8);
+  if (c.epi == EPI_ARGMAX || c.epi == EPI_TOPK) return gemv_segments(c.rows, c.cols, 1, 1);
+  return gemv_segments(c.rows, c.cols, 1, 8);
 }
 
 static int dispatch_qmv(const QmvCall &c) {
@@ -561,7 +574,8 @@ static int dispatch_qmv(const QmvCall &c) {
 
 // The plan table's entry for this call, unless the caller fixed the plan;
 // an entry the call cannot use (refused before anything is launched) gives
-// way to the built-in choice, unless it is marked strict.
+// way to the built-in choice, unless it is marked strict (a split needing
+// more workspace than the call brings counts as unusable).
 int launch_qmv(const QmvCall &c0) {
   QmvCall c = c0;
   const bool forced = (c.plan & PLAN_FORCED) != 0;
@@ -569,7 +583,7 @@ int launch_qmv(const QmvCall &c0) {
   const bool strict = (c.plan & QG_PLAN_STRICT) != 0;
   c.plan &= ~QG_PLAN_STRICT;
   int st = dispatch_qmv(c);
-  if (st == QG_EUNSUPPORTED && !forced && !strict && c.plan) {
+  if ((st == QG_EUNSUPPORTED || st == QG_EWORKSPACE) && !forced && !strict && c.plan) {
     c.plan = 0;
     st = dispatch_qmv(c);
   }

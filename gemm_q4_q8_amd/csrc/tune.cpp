@@ -11,6 +11,7 @@
 #include <map>
 #include <mutex>
 #include <tuple>
+#include <vector>
 
 #include "internal.h"
 #include "qgemm.h"
@@ -52,8 +53,10 @@ bool plan_ok(int op, int ncols, int plan) {
     plan &= ~QG_PLAN_STRICT;
     if (plan == 0) return false;
   }
-  if (op == QG_OP_GEMV && ncols == 16) return plan >= 8 && plan <= 16;
-  return (plan >= 1 && plan <= 16) || plan == QG_PLAN_SW;
+  const int layout = plan & ~PLAN_S_MASK;  // what remains besides the K segments
+  if (layout == 0) return true;
+  if (op == QG_OP_GEMV && ncols == 16) return layout >= 8 && layout <= 16;
+  return (layout >= 1 && layout <= 16) || layout == QG_PLAN_SW;
 }
 
 void store_plan(const PlanKey &k, int plan) {
@@ -76,20 +79,28 @@ int plan_lookup(const QmvCall &c) {
 // winner.  The call must not accumulate into its output (the launches
 // repeat).  Every candidate is a layout the built-in choice itself takes
 // for some shape; one the call cannot use is refused before launching and
-// dropped.
-int tune_call(QmvCall c, int32_t *plan_out) {
+// dropped.  With QG_TUNE_SPLIT the K segments are candidates too: half and
+// twice the shape's own (within the K range and the workspace).
+int tune_call(QmvCall c, int32_t flags, int32_t *plan_out) {
   static const int kGemv[] = {0, 4, 8, 12, 16, QG_PLAN_SW};
   static const int kGemm16[] = {0, 8, 12, 16};
   const bool g16 = c.ncols == 16;
-  const int *cand = g16 ? kGemm16 : kGemv;
-  const int n = g16 ? 4 : 6;
-  constexpr int ROUNDS = 3, REPS = 10;
-  float best[6];
-  bool usable[6];
-  for (int i = 0; i < n; ++i) {
-    best[i] = 3.0e38f;
-    usable[i] = true;
+  const int *lay = g16 ? kGemm16 : kGemv;
+  const int nlay = g16 ? 4 : 6;
+  std::vector<int> splits{0};
+  if (flags & QG_TUNE_SPLIT) {
+    const int S = builtin_split(c);
+    const int64_t KT = (c.cols / 32 + 3) / 4;
+    if (S / 2 >= 1 && S / 2 < S) splits.push_back(S / 2);
+    if (2 * S <= KT && 2 * S <= 255) splits.push_back(2 * S);
   }
+  std::vector<int> cand;
+  for (int sp : splits)
+    for (int i = 0; i < nlay; ++i) cand.push_back(lay[i] | (sp << PLAN_S_SHIFT));
+  const int n = (int)cand.size();
+  constexpr int ROUNDS = 3, REPS = 10;
+  std::vector<float> best(n, 3.0e38f);
+  std::vector<char> usable(n, 1);
   hipEvent_t e0 = nullptr, e1 = nullptr;
   hipError_t he = hipEventCreate(&e0);
   if (he == hipSuccess) he = hipEventCreate(&e1);
@@ -103,7 +114,7 @@ int tune_call(QmvCall c, int32_t *plan_out) {
       if (!usable[i]) continue;
       c.plan = cand[i] | PLAN_FORCED;
       int s = launch_qmv(c);  // warm-up, and whether the plan fits
-      if (s == QG_EUNSUPPORTED && i > 0) {
+      if ((s == QG_EUNSUPPORTED || s == QG_EWORKSPACE) && i > 0) {
         usable[i] = false;
         continue;
       }

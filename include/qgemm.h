@@ -341,12 +341,19 @@ int moe_ffn(const qg_moe *m, const float *X, int64_t ldx, int32_t ntok, float *Y
  * workgroup, about a second at load, with a 3% noise margin; ARCH Engine,
  * its file table: an autotune module beside the kernels]
  *
- * A plan fixes how a product call is laid out on the GPU, never what it
- * sums: 0 = the built-in choice; 1..16 = that many waves (row tiles) per
- * workgroup, K segments reduced across workgroups; QG_PLAN_SW = the K
- * segments as waves of one workgroup.  The K segments and their summation
- * order are a function of the shape alone, so every plan gives the same
- * bits.  Plans live in a per-process table keyed by (current device, op,
+ * A plan fixes how a product call is laid out on the GPU: 0 = the built-in
+ * choice; 1..16 = that many waves (row tiles) per workgroup, K segments
+ * reduced across workgroups; QG_PLAN_SW = the K segments as waves of one
+ * workgroup.  These never change what is summed: the K segments and their
+ * order are a function of the shape, so every such plan gives the same
+ * bits.  A plan may add QG_PLAN_SPLIT(s), s = 1..255 K segments instead of
+ * the shape's own (the split-K of the pages' autotune): a different
+ * summation order, so results that differ by rounding (within the products'
+ * float tolerance), the same bits on every call while the entry stands
+ * (pin it with qg_plan_set for runs that must repeat); a split needing
+ * more workspace than the call brings is not usable by that call (the
+ * *_ws_bytes queries leave room for twice the shape's own split).  Plans
+ * live in a per-process table keyed by (current device, op,
  * qtype, rows, cols, ncols); every later call of that op on that shape and
  * column count uses the entry, or the built-in choice where the entry does
  * not fit the call (checked before anything is launched).  Ops:
@@ -357,18 +364,21 @@ int moe_ffn(const qg_moe *m, const float *X, int64_t ldx, int32_t ntok, float *Y
  *   QG_OP_LMHEAD  lmhead_argmax and lmhead_topk (ncols 1)
  * The fused FFN and the MoE layer keep their own plans.
  *
- * qg_tune_*: the arguments of the call they tune (same checks, same
- * errors); each candidate plan (built-in, 4, 8, 12, 16 waves, QG_PLAN_SW;
- * 8, 12, 16 for 16 columns) runs 1 + 10 times on the caller's stream in
- * three rounds, timed with HIP events (blocks the host until done); the
- * fastest stays only if more than 3% faster than the built-in choice, else
- * the entry is 0.  The outputs are overwritten (qg_tune_gemv stores W X,
- * it never accumulates) and end equal to the tuned call's.  *plan (may be
- * NULL) receives the entry.  Calls racing with a tuning call on another
- * thread see the old or the new entry.
+ * qg_tune_*: the arguments of the call they tune (same checks, same errors)
+ * and flags; each candidate plan (built-in, 4, 8, 12, 16 waves, QG_PLAN_SW;
+ * 8, 12, 16 for 16 columns; with flags & QG_TUNE_SPLIT each of these also at
+ * half and twice the shape's own K segments) runs 1 + 10 times on the
+ * caller's stream in three rounds, timed with HIP events (blocks the host
+ * until done); the fastest stays only if more than 3% faster than the
+ * built-in choice, else the entry is 0. Without QG_TUNE_SPLIT the tuned calls
+ * keep their bits. The outputs are overwritten (qg_tune_gemv stores W X, it
+ * never accumulates) and end equal to the tuned call's. *plan (may be NULL)
+ * receives the entry. Calls racing with a tuning call on another thread see
+ * the old or the new entry.
  * qg_plan_set pins an entry (QG_EINVAL for an op or plan outside the
  * above); a plan | QG_PLAN_STRICT makes the calls that cannot use it fail
- * with QG_EUNSUPPORTED instead of taking the built-in choice.  qg_plan_get
+ * (QG_EUNSUPPORTED; QG_EWORKSPACE for a split their workspace cannot hold)
+ * instead of taking the built-in choice.  qg_plan_get
  * reads an entry (0 when none), qg_plan_reset empties the table.
  * ------------------------------------------------------------------------ */
 #define QG_OP_GEMV 0
@@ -376,19 +386,21 @@ int moe_ffn(const qg_moe *m, const float *X, int64_t ldx, int32_t ntok, float *Y
 #define QG_OP_LMHEAD 2
 #define QG_PLAN_SW 0x100
 #define QG_PLAN_STRICT 0x200
+#define QG_PLAN_SPLIT(s) ((int32_t)(s) << 12)
+#define QG_TUNE_SPLIT 1
 
 int qg_tune_gemv(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols,
                  const float *X, int64_t ldx, int32_t ncols, float *Y, int64_t ldy,
-                 void *ws, size_t ws_bytes, void *stream, int32_t *plan);
+                 void *ws, size_t ws_bytes, void *stream, int32_t flags, int32_t *plan);
 
 int qg_tune_gateup(int qtype, const void *g_qs, const void *g_d, const void *u_qs,
                    const void *u_d, int64_t rows, int64_t cols, const float *X, int64_t ldx,
                    int32_t ncols, float *H, int64_t ldh, void *ws, size_t ws_bytes,
-                   void *stream, int32_t *plan);
+                   void *stream, int32_t flags, int32_t *plan);
 
 int qg_tune_lmhead(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols,
                    int64_t n_rows, const float *x, int32_t *out_idx, float *out_val,
-                   void *ws, size_t ws_bytes, void *stream, int32_t *plan);
+                   void *ws, size_t ws_bytes, void *stream, int32_t flags, int32_t *plan);
 
 int qg_plan_set(int op, int qtype, int64_t rows, int64_t cols, int32_t ncols, int32_t plan);
 

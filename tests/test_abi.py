@@ -276,7 +276,9 @@ def test_plan_table():
     L.qg_plan_reset()
     assert get(qg.OP_GEMV, 2, 64, 128, 1) == 0
     for op, nc, plan in [(qg.OP_GEMV, 1, 4), (qg.OP_GEMV, 8, qg.PLAN_SW), (qg.OP_GEMV, 16, 12),
-                         (qg.OP_GATEUP, 3, 16), (qg.OP_LMHEAD, 1, 8 | qg.PLAN_STRICT)]:
+                         (qg.OP_GATEUP, 3, 16), (qg.OP_LMHEAD, 1, 8 | qg.PLAN_STRICT),
+                         (qg.OP_GEMV, 2, qg.PLAN_SPLIT(3)), (qg.OP_GEMV, 16, qg.PLAN_SPLIT(5) | 8),
+                         (qg.OP_GATEUP, 1, qg.PLAN_SPLIT(255) | qg.PLAN_SW | qg.PLAN_STRICT)]:
         assert L.qg_plan_set(op, 2, 64, 128, nc, plan) == OK
         assert get(op, 2, 64, 128, nc) == plan
     assert get(qg.OP_GEMV, 8, 64, 128, 1) == 0           # other qtype: no entry
@@ -293,7 +295,10 @@ def test_plan_table():
            (qg.OP_GEMV, 2, 64, 128, 1, qg.PLAN_SW | 4),
            (qg.OP_GEMV, 2, 64, 128, 1, qg.PLAN_STRICT),
            (qg.OP_GEMV, 2, 64, 128, 16, 4),                # 16 columns: 8..16 waves
-           (qg.OP_GEMV, 2, 64, 128, 16, qg.PLAN_SW)]
+           (qg.OP_GEMV, 2, 64, 128, 16, qg.PLAN_SW),
+           (qg.OP_GEMV, 2, 64, 128, 16, qg.PLAN_SPLIT(2) | 4),
+           (qg.OP_GEMV, 2, 64, 128, 1, qg.PLAN_SPLIT(256)),  # 1..255 segments
+           (qg.OP_GEMV, 2, 64, 128, 1, qg.PLAN_SPLIT(3) | 17)]
     for a in bad:
         assert L.qg_plan_set(*a) == EINVAL, a
     assert L.qg_plan_get(qg.OP_GEMV, 2, 64, 128, 1, None) == EINVAL
@@ -307,14 +312,15 @@ def test_tune_argument_checks():
     any HIP call)."""
     ws, X, Y = FAKE + (3 << 20), FAKE + (1 << 20), FAKE + (2 << 20)
     tg = lambda **k: L.qg_tune_gemv(k.get("qt", 2), k.get("qs", FAKE), FAKE, 64, 128, X, 128, k.get("nc", 1),
-                                    k.get("Y", Y), 64, ws, 1 << 20, None, None)
+                                    k.get("Y", Y), 64, ws, 1 << 20, None, 0, None)
     assert tg(qs=None) == EINVAL
     assert tg(qt=3) == EINVAL
     assert tg(nc=9) == ESHAPE
     assert tg(Y=X + 64) == EINVAL
     assert L.qg_tune_gateup(2, FAKE, FAKE, None, FAKE, 64, 128, X, 128, 1, Y, 64, ws, 1 << 20, None,
-                            None) == EINVAL
+                            0, None) == EINVAL
     assert L.qg_tune_gateup(2, FAKE, FAKE, FAKE, FAKE, 64, 128, X, 128, 1, Y, 64, ws, 16, None,
-                            None) == EWS
-    assert L.qg_tune_lmhead(2, FAKE, FAKE, 64, 128, 65, X, Y, None, ws, 1 << 20, None, None) == ESHAPE
-    assert L.qg_tune_lmhead(2, FAKE, FAKE, 64, 128, 64, X, None, None, ws, 1 << 20, None, None) == EINVAL
+                            1, None) == EWS
+    assert L.qg_tune_lmhead(2, FAKE, FAKE, 64, 128, 65, X, Y, None, ws, 1 << 20, None, 0, None) == ESHAPE
+    assert L.qg_tune_lmhead(2, FAKE, FAKE, 64, 128, 64, X, None, None, ws, 1 << 20, None, 1, None) == EINVAL
+

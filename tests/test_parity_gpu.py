@@ -759,3 +759,98 @@ def test_tune_keeps_bits_and_fills_the_table(env):
         say(f"  tuned plans: gemv {p}, gemm16 {p16}, gateup {pg}, lmhead {pl}")
     finally:
         qg.plan_reset()
+
+
+def _split_runs(env, op, qtype, rows, cols, nc, call, splits, layouts=(0,)):
+    """call() twice under each pinned strict split: (split, layout, out) for
+    those applied; refusals must be for room (workspace) or layout."""
+    torch, qg, dev = env
+    done = []
+    qg.plan_reset()
+    try:
+        for sp in splits:
+            for lay in layouts:
+                qg.plan_set(op, qtype, rows, cols, nc, qg.PLAN_SPLIT(sp) | lay | qg.PLAN_STRICT)
+                try:
+                    a, b = call(), call()
+                except qg.QGError as e:
+                    assert e.status in (-4, -5), e
+                    continue
+                for u, v in zip(a, b):
+                    assert np.array_equal(u.view(np.uint32), v.view(np.uint32)), (sp, lay)
+                done.append((sp, lay, a))
+    finally:
+        qg.plan_reset()
+    say(f"  splits applied {[(s, l) for s, l, _ in done]}")
+    return done
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("rows,cols,ncols", [(2100, 2048, 1), (64, 8192, 3), (600, 11264, 1)])
+def test_split_plans_gemv(env, qtype, rows, cols, ncols):
+    """K splits pinned per shape: within the oracle's tolerance, the same bits
+    on repeat calls, storing and accumulating."""
+    torch, qg, dev = env
+    say(f"split gemv qtype={qtype} {rows}x{cols} ncols={ncols}")
+    raw, W = make(env, qtype, rows, cols, seed=rows + 3 * cols)
+    X = synth.gen_x(cols, ncols, cfg_id=rows + 11)
+    Xd = up(env, X.T)
+    y0 = synth.rng(6, rows).standard_normal((ncols, rows)).astype(np.float32)
+    done = _split_runs(env, qg.OP_GEMV, qtype, rows, cols, ncols,
+                       lambda: (qg.qgemv(W, Xd).cpu().numpy(),
+                                qg.qgemv(W, Xd, up(env, y0), accumulate=True).cpu().numpy()),
+                       [1, 2, 3, 4, 6, 8], (0, 8))
+    assert len(done) >= 4
+    ref, a = ops.gemv(qtype, raw, X)
+    for sp, lay, (Y, Ya) in done:
+        assert_tol(Y.astype(np.float64).T, ref, ops.tol_dot(a), f"split {sp} lay {lay}")
+        assert_tol(Ya.astype(np.float64).T, ref + y0.T.astype(np.float64), ops.tol_dot(a) + 1e-6 * np.abs(y0.T),
+                   f"split {sp} lay {lay} acc")
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+def test_split_plans_gemm16_and_gateup(env, qtype):
+    torch, qg, dev = env
+    rows, cols = 2100, 2048
+    raw, W = make(env, qtype, rows, cols, seed=71)
+    X = synth.gen_x(cols, 16, cfg_id=72)
+    Xd = up(env, X.T)
+    done = _split_runs(env, qg.OP_GEMV, qtype, rows, cols, 16, lambda: (qg.qgemm16(W, Xd).cpu().numpy(),),
+                       [1, 2, 4], (0, 12))
+    assert len(done) >= 3
+    ref, a = ops.gemv(qtype, raw, X)
+    for sp, lay, (Y,) in done:
+        assert_tol(Y.astype(np.float64).T, ref, ops.tol_dot(a), f"gemm16 split {sp}")
+    graw, G = make(env, qtype, 1000, 5120, seed=73)
+    uraw, U = make(env, qtype, 1000, 5120, seed=74)
+    x = synth.gen_x(5120, 1, cfg_id=75)
+    xd = up(env, x.T)
+    done = _split_runs(env, qg.OP_GATEUP, qtype, 1000, 5120, 1, lambda: (qg.gateup_silu(G, U, xd).cpu().numpy(),),
+                       [1, 2, 3, 6], (0, qg.PLAN_SW))
+    assert len(done) >= 3
+    h, th, _, _ = ops.gateup_silu(qtype, graw, uraw, x)
+    for sp, lay, (H,) in done:
+        assert_tol(H.astype(np.float64).T, h, th, f"gateup split {sp}")
+
+
+def test_tune_with_splits(env):
+    """Tuning over K splits too: the kept plan's results stay within the
+    oracle's tolerance and repeat bitwise."""
+    torch, qg, dev = env
+    qg.plan_reset()
+    try:
+        rows, cols = 1200, 8192
+        raw, W = make(env, Q4, rows, cols, seed=81)
+        X = synth.gen_x(cols, 1, cfg_id=82)
+        Xd = up(env, X.T)
+        p = qg.tune_gemv(W, Xd, split=True)
+        say(f"  tuned with splits: plan {p:#x}")
+        lay, sp = p & ~(0xFF << 12), (p >> 12) & 0xFF
+        assert lay in (0, 4, 8, 12, 16, qg.PLAN_SW) and sp >= 0
+        assert qg.plan_get(qg.OP_GEMV, Q4, rows, cols, 1) == p
+        Y1, Y2 = qg.qgemv(W, Xd).cpu().numpy(), qg.qgemv(W, Xd).cpu().numpy()
+        assert np.array_equal(Y1.view(np.uint32), Y2.view(np.uint32))
+        ref, a = ops.gemv(Q4, raw, X)
+        assert_tol(Y1.astype(np.float64).T, ref, ops.tol_dot(a), "tuned split gemv")
+    finally:
+        qg.plan_reset()
