@@ -270,19 +270,23 @@ def run_extras(B, kernels):
 def run_plans(B, kernels):
     """Each launch plan timed at the benchmarked decode shapes (the built-in
     choice, 4 / 8 / 12 / 16 waves per workgroup, K segments inside one
-    workgroup), and the plan the tuner keeps there."""
+    workgroup, and K splits of 1 to 12 segments with the built-in layout),
+    and the plans the tuner keeps there (without and with splits)."""
     torch, qg = B.torch, B.qg
     import synth
     Q4 = qg.Q4_0
     cands = [4, 8, 12, 16, qg.PLAN_SW]
 
+    splits = [qg.PLAN_SPLIT(s) for s in (1, 2, 3, 4, 6, 8, 12)]
+
     def sweep(op, w, ncols, mk_fns, iters, plans):
         us = {}
-        for pl in [0] + plans:
+        for pl in [0] + plans + splits:
             qg.plan_reset()
             if pl:
                 qg.plan_set(op, w.qtype, w.rows, w.cols, ncols, pl | qg.PLAN_STRICT)
-            key = "builtin" if pl == 0 else ("sw" if pl == qg.PLAN_SW else str(pl))
+            key = ("builtin" if pl == 0 else "sw" if pl == qg.PLAN_SW else
+                   f"split{pl >> 12}" if pl >= 1 << 12 else str(pl))
             try:
                 t, _ = B.graph_time(mk_fns(), iters)   # a refused plan raises in the eager warm-up
                 us[key] = round(t * 1e6, 2)
@@ -306,16 +310,22 @@ def run_plans(B, kernels):
             fns = lambda: [lambda i=i: qg.gateup_silu(p[2 * i], p[2 * i + 1], x, y) for i in range(len(p) // 2)]
             us = sweep(qg.OP_GATEUP, w, ncols, fns, len(p), cands)
             tuned = qg.tune_gateup(p[0], p[1], x, y)
+            qg.plan_reset()
+            tuned_s = qg.tune_gateup(p[0], p[1], x, y, split=True)
         elif ncols == 16:
             fns = lambda: [lambda m=m: qg.qgemm16(m, x, y) for m in p]
             us = sweep(qg.OP_GEMV, w, ncols, fns, 2 * len(p), [8, 12, 16])
             tuned = qg.tune_gemv(p[0], x, y)
+            qg.plan_reset()
+            tuned_s = qg.tune_gemv(p[0], x, y, split=True)
         else:
             fns = lambda: [lambda m=m: qg.qgemv(m, x, y) for m in p]
             us = sweep(qg.OP_GEMV, w, ncols, fns, 2 * len(p), cands)
             tuned = qg.tune_gemv(p[0], x, y)
+            qg.plan_reset()
+            tuned_s = qg.tune_gemv(p[0], x, y, split=True)
         qg.plan_reset()
-        kernels[f"plans_{nm}"] = {"us": us, "tuned_plan": tuned}
+        kernels[f"plans_{nm}"] = {"us": us, "tuned_plan": tuned, "tuned_plan_with_splits": tuned_s}
         del p
     log("  plans done")
 

@@ -79,8 +79,9 @@ int plan_lookup(const QmvCall &c) {
 // winner.  The call must not accumulate into its output (the launches
 // repeat).  Every candidate is a layout the built-in choice itself takes
 // for some shape; one the call cannot use is refused before launching and
-// dropped.  With QG_TUNE_SPLIT the K segments are candidates too: half and
-// twice the shape's own (within the K range and the workspace).
+// dropped.  With QG_TUNE_SPLIT the K segments are candidates too: half,
+// one less, one more and twice the shape's own (within the K range and the
+// workspace the size queries give).
 int tune_call(QmvCall c, int32_t flags, int32_t *plan_out) {
   static const int kGemv[] = {0, 4, 8, 12, 16, QG_PLAN_SW};
   static const int kGemm16[] = {0, 8, 12, 16};
@@ -91,8 +92,11 @@ int tune_call(QmvCall c, int32_t flags, int32_t *plan_out) {
   if (flags & QG_TUNE_SPLIT) {
     const int S = builtin_split(c);
     const int64_t KT = (c.cols / 32 + 3) / 4;
-    if (S / 2 >= 1 && S / 2 < S) splits.push_back(S / 2);
-    if (2 * S <= KT && 2 * S <= 255) splits.push_back(2 * S);
+    for (int sp : {S / 2, S - 1, S + 1, 2 * S}) {
+      bool seen = sp == S;
+      for (int q : splits) seen = seen || q == sp;
+      if (!seen && sp >= 1 && sp <= KT && sp <= 255) splits.push_back(sp);
+    }
   }
   std::vector<int> cand;
   for (int sp : splits)

@@ -367,7 +367,7 @@ int moe_ffn(const qg_moe *m, const float *X, int64_t ldx, int32_t ntok, float *Y
  * qg_tune_*: the arguments of the call they tune (same checks, same errors)
  * and flags; each candidate plan (built-in, 4, 8, 12, 16 waves, QG_PLAN_SW;
  * 8, 12, 16 for 16 columns; with flags & QG_TUNE_SPLIT each of these also at
- * half and twice the shape's own K segments) runs 1 + 10 times on the
+ * half, one less, one more and twice the shape's own K segments) runs 1 + 10 times on the
  * caller's stream in three rounds, timed with HIP events (blocks the host
  * until done); the fastest stays only if more than 3% faster than the
  * built-in choice, else the entry is 0. Without QG_TUNE_SPLIT the tuned calls
