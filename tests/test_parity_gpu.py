@@ -854,3 +854,56 @@ def test_tune_with_splits(env):
         assert_tol(Y1.astype(np.float64).T, ref, ops.tol_dot(a), "tuned split gemv")
     finally:
         qg.plan_reset()
+
+
+def test_graph_replay_decode_step(env):
+    """The decode step (residual reset by a copy, gate/up, down accumulating)
+    captured in a HIP graph: every replay, with eager calls on the same
+    workspace between replays, gives the eager result bitwise; also with a
+    plan pinned for the down projection (read when the graph is captured)."""
+    torch, qg, dev = env
+    F, Hd = 1024, 2048
+    _, G = make(env, Q4, F, Hd, seed=91)
+    _, U = make(env, Q4, F, Hd, seed=92)
+    _, D = make(env, Q4, Hd, F, seed=93)
+    x = up(env, synth.gen_x(Hd, 1, cfg_id=9).T)
+    y0 = up(env, synth.rng(94, Hd).standard_normal((1, Hd)).astype(np.float32))
+    h = torch.empty((1, F), device=dev)
+    y = torch.empty((1, Hd), device=dev)
+    spare = torch.empty((1, Hd), device=dev)
+
+    def step():
+        y.copy_(y0)
+        qg.gateup_silu(G, U, x, h)
+        qg.qgemv(D, h, y, accumulate=True)
+
+    try:
+        for pin in (None, 8):
+            qg.plan_reset()
+            if pin:
+                qg.plan_set(qg.OP_GEMV, Q4, Hd, F, 1, pin | qg.PLAN_STRICT)
+            step()
+            torch.cuda.synchronize()
+            want_h, want_y = h.cpu().numpy().copy(), y.cpu().numpy().copy()
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                with torch.cuda.graph(g, stream=s):
+                    step()
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            for r in range(3):
+                h.zero_()
+                y.zero_()
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                assert np.array_equal(h.cpu().numpy().view(np.uint32), want_h.view(np.uint32)), (pin, r)
+                assert np.array_equal(y.cpu().numpy().view(np.uint32), want_y.view(np.uint32)), (pin, r)
+                qg.qgemv(D, h, spare)          # eager work on the same workspace between replays
+                torch.cuda.synchronize()
+            say(f"  graph replays equal eager (plan {pin})")
+            del g
+    finally:
+        qg.plan_reset()
