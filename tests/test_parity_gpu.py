@@ -907,3 +907,45 @@ def test_graph_replay_decode_step(env):
             del g
     finally:
         qg.plan_reset()
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_graph_replay_moe(env, T):
+    """The MoE layer (router counters, work list, expert units) captured in a
+    HIP graph: every replay, with an eager layer call on the same workspace
+    between replays, gives the eager result bitwise."""
+    torch, qg, dev = env
+    m, _ = _moe_build(env, 16, 256, 128, 4, seed=95)
+    X = up(env, synth.gen_x(256, T, cfg_id=96).T)
+    y0 = up(env, synth.rng(97, 256).standard_normal((T, 256)).astype(np.float32))
+    Y = torch.empty((T, 256), device=dev)
+    Ys = torch.empty((T, 256), device=dev)
+    ti = torch.empty((T, 4), dtype=torch.int32, device=dev)
+
+    def layer():
+        Y.copy_(y0)
+        qg.moe_ffn(m, X, Y, ti)
+
+    layer()
+    torch.cuda.synchronize()
+    want_y, want_i = Y.cpu().numpy().copy(), ti.cpu().numpy().copy()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            layer()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for r in range(3):
+        Y.zero_()
+        ti.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(Y.cpu().numpy().view(np.uint32), want_y.view(np.uint32)), r
+        assert np.array_equal(ti.cpu().numpy(), want_i), r
+        Ys.copy_(y0)
+        qg.moe_ffn(m, X, Ys)                # eager layer on the same workspace between replays
+        torch.cuda.synchronize()
+    say(f"  moe graph replays equal eager (T={T})")
