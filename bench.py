@@ -64,13 +64,13 @@ class Bench:
         """Capture `iters` calls (cycling fns) in one HIP graph; return the
         mean time per call in seconds over one timed replay."""
         torch = self.torch
-        for f in fns[:2]:
-            f()                                   # eager warm-up (workspaces, code objects)
-        torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
+            for f in fns[:2]:
+                f()                               # eager warm-up on the capture stream (workspace, code objects)
+            torch.cuda.synchronize()
             with torch.cuda.graph(g, stream=s):
                 for i in range(iters):
                     fns[i % len(fns)]()
@@ -122,8 +122,6 @@ def run_ffn(B, steps, warmup):
     if warmup > 0:
         _, gw = B.graph_time(steps_fns, warmup)
     t_step, _ = B.graph_time(steps_fns, steps)
-    xv, yv, hv = x[0], y[0], h[0]
-    t_fused, _ = B.graph_time([lambda i=i: qg.ffn_fused(pg[i], pu[i], pd[i], xv, yv, hv) for i in range(n)], 4 * n)
     t_gu, _ = B.graph_time([lambda i=i: qg.gateup_silu(pg[i], pu[i], x, h) for i in range(n)], 4 * n)
     t_dn, _ = B.graph_time([lambda i=i: qg.qgemv(pd[i], h, y, accumulate=True) for i in range(n)], 4 * n)
     # RMSNorm ahead of gate/up: folded into the call, and as its own launch
@@ -142,7 +140,7 @@ def run_ffn(B, steps, warmup):
             "rmsnorm_then_gateup_q4_0_5120to2x17408": (gu_bytes + 4 * K, t_ngu)}
     raws = (graw, uraw, draw)
     del pg, pu, pd
-    return step_bytes, t_step, gu_bytes, t_gu, dn_bytes, t_dn, raws, t_fused, norm
+    return step_bytes, t_step, gu_bytes, t_gu, dn_bytes, t_dn, raws, norm
 
 
 def run_extras(B, kernels):
@@ -452,12 +450,11 @@ def main():
         return
 
     log("bench: decode FFN step")
-    step_bytes, t_step, gu_bytes, t_gu, dn_bytes, t_dn, raws, t_fused, norm = run_ffn(B, args.steps, args.warmup)
+    step_bytes, t_step, gu_bytes, t_gu, dn_bytes, t_dn, raws, norm = run_ffn(B, args.steps, args.warmup)
     value = step_bytes / t_step / 1e9
     kernels = {
         "gateup_silu_q4_0_5120to2x17408": kernel_entry(gu_bytes, t_gu),
         "qgemv_q4_0_17408to5120_acc": kernel_entry(dn_bytes, t_dn),
-        "ffn_fused_q4_0_5120x17408": kernel_entry(step_bytes, t_fused),
     }
     for nm, (nb, tt) in norm.items():
         kernels[nm] = kernel_entry(nb, tt)

@@ -64,9 +64,6 @@ _SIGS = {
     "qgemm16": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i32,
                                _vp, _sz, _vp]),
     "qg_gateup_ws_bytes": (_sz, [_i64, _i64]),
-    "qg_ffn_ws_bytes": (_sz, [_i64, _i64]),
-    "ffn_fused": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp,
-                                 _vp, _sz, _vp]),
     "gateup_silu": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _i32,
                                    _vp, _i64, _vp, _sz, _vp]),
     "gateup_silu_rmsnorm": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _i32,
@@ -129,20 +126,33 @@ def _stream(device) -> int:
 
 
 _WS = {}
+_WS_RETIRED = []
 
 
 def workspace(nbytes: int, device, key: str = "default"):
-    """A zero-filled device workspace (cached per device and key).  Its
-    leading counters are zero again after every completed call, so one
-    workspace serves any sequence of calls on one stream; a larger request
-    replaces it with a new zero-filled one."""
+    """A zero-filled device workspace, cached per (device, current stream,
+    key).  Its leading counters are zero again after every completed call,
+    so one workspace serves any sequence of calls on one stream; calls on
+    different streams, which may overlap, get different workspaces.  A
+    larger request replaces it with a new zero-filled one, and the old one
+    stays allocated for the life of the process: a HIP graph captured
+    earlier still holds its address.  Inside a graph capture the workspace
+    cannot be created or grown (its zero fill would only run at replay):
+    make one eager call of the largest shape on the capture stream first."""
     torch = _torch()
     dev = torch.device(device)
-    k = (dev.index, key)
+    k = (dev.index, torch.cuda.current_stream(dev).cuda_stream, key)
     ws = _WS.get(k)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
-        _WS[k] = ws
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("the library workspace of this stream would have to be created or grown "
+                               "during graph capture; make one eager call of the largest shape on the "
+                               "capture stream first")
+        new = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
+        if ws is not None:
+            _WS_RETIRED.append(ws)
+        _WS[k] = new
+        ws = new
     return ws
 
 
@@ -300,29 +310,6 @@ def rmsnorm(X, gamma, eps: float, Y=None):
     return Y
 
 
-def ffn_fused(wg: QMatrix, wu: QMatrix, wd: QMatrix, x, y, h=None):
-    """One token through a decode FFN: h = silu(Wg x) * (Wu x); y += Wd h.
-    Returns h.  Bitwise equal to gateup_silu + qgemv(accumulate=True)."""
-    torch = _torch()
-    _check_dev(x, y)
-    if not (wg.qtype == wu.qtype == wd.qtype):
-        raise ValueError("gate, up and down must share one quantisation type")
-    if h is None:
-        h = torch.empty(wg.rows, dtype=torch.float32, device=x.device)
-    ws = workspace(lib.qg_ffn_ws_bytes(wg.cols, wg.rows), x.device, "ffn")
-    _check(lib.ffn_fused(wg.qtype, wg.qs.data_ptr(), wg.d.data_ptr(), wu.qs.data_ptr(), wu.d.data_ptr(),
-                         wd.qs.data_ptr(), wd.d.data_ptr(), wg.cols, wg.rows, x.data_ptr(), h.data_ptr(),
-                         y.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x.device)), "ffn_fused")
-    return h
-
-
-def ffn_wait_error(device=None) -> int:
-    """The fused FFN's error word (nonzero: a wait gave up; see qgemm.h)."""
-    torch = _torch()
-    ws = _WS.get((torch.device(device or "cuda:0").index or 0, "ffn"))
-    return 0 if ws is None else int(ws[8:12].view(torch.int32).item())
-
-
 def read_probe(t, sink=None):
     """Measurement aid: read every byte of device tensor `t` once (the
     bench's streaming-read ceiling).  Returns the sink tensor."""
@@ -464,6 +451,10 @@ class MoE:
     normalize_topk: bool = True
     norm_weight: object = None  # f32 [hidden]: RMSNorm ahead of router and experts
     norm_eps: float = 0.0
+
+    @property
+    def qtype(self) -> int:
+        return self.gate.qtype
 
     def struct(self) -> qg_moe:
         s = qg_moe()

@@ -388,48 +388,6 @@ int lmhead_topk(int qtype, const void *qs, const void *d, int64_t rows, int64_t 
   return launch_qmv(c);
 }
 
-size_t qg_ffn_ws_bytes(int64_t hidden, int64_t ffn) {
-  if (hidden <= 0 || ffn <= 0 || hidden % 32 || ffn % 32) return 0;
-  return ffn_ws_bytes(hidden, ffn);
-}
-
-int ffn_fused(int qtype, const void *g_qs, const void *g_d, const void *u_qs, const void *u_d,
-              const void *d_qs, const void *d_d, int64_t hidden, int64_t ffn, const float *x, float *h,
-              float *y, void *ws, size_t ws_bytes, void *stream) {
-  if (!qtype_ok(qtype)) return QG_EINVAL;
-  int st = check_matrix(g_qs, g_d, ffn, hidden);
-  if (st) return st;
-  if ((st = check_matrix(u_qs, u_d, ffn, hidden))) return st;
-  if ((st = check_matrix(d_qs, d_d, hidden, ffn))) return st;
-  if ((st = check_act(x, hidden, hidden, 1))) return st;
-  if ((st = check_act(h, ffn, ffn, 1))) return st;  // h is also the down projection's input
-  if ((st = check_out(y, hidden, hidden))) return st;
-  if (overlap(span(x, hidden, hidden, 1), span(h, ffn, ffn, 1)) ||
-      overlap(span(x, hidden, hidden, 1), span(y, hidden, hidden, 1)) ||
-      overlap(span(h, ffn, ffn, 1), span(y, hidden, hidden, 1)))
-    return QG_EINVAL;
-  if (!ws || ws_bytes < qg_ffn_ws_bytes(hidden, ffn)) return QG_EWORKSPACE;
-  if (!aligned(ws, 256)) return QG_EALIGN;
-  FfnCall c;
-  memset(&c, 0, sizeof(c));
-  c.qtype = qtype;
-  c.g_qs = g_qs;
-  c.g_d = g_d;
-  c.u_qs = u_qs;
-  c.u_d = u_d;
-  c.d_qs = d_qs;
-  c.d_d = d_d;
-  c.hidden = hidden;
-  c.ffn = ffn;
-  c.x = x;
-  c.h = h;
-  c.y = y;
-  c.ws = ws;
-  c.ws_bytes = ws_bytes;
-  c.stream = (hipStream_t)stream;
-  return launch_ffn(c);
-}
-
 static int check_moe(const qg_moe *m, int32_t ntok) {
   if (!m) return QG_EINVAL;
   if (!qtype_ok(m->qtype)) return QG_EINVAL;

@@ -1,23 +1,34 @@
 // One work unit of the product kernels: W row tiles (one per wave, of one
 // matrix or of gate and up together) over one K segment, used by the GEMV
-// (1..8 columns), gate/up, LM head and 16-column GEMM kernels, the fused
-// FFN and the MoE expert kernels.
+// (1..8 columns), gate/up, LM head and 16-column GEMM kernels and the MoE
+// expert kernels.
 //
 // What is computed ("Engine and kernels", Kernel families): y = W x over
 // Q4_0 / Q8_0 blocks dequantised in registers with f32 sums, with the
 // epilogues of the kernel families (store, y += W x, SiLU(gate) * up, and
-// the per-row values an argmax needs).
+// the per-row values an argmax needs).  Activations are f32 ("Correctness
+// and portability": f16 only for block scales, the KV cache and the wire),
+// so products of 1..8 columns carry each activation at f32 range and
+// 22-bit precision into the matrix cores (below); only the 16-column
+// prefill tiles take plain f16 activation operands.
 //
 // How (MI355X):
-//  * The workgroup stages its activations once in LDS as f16,
-//    [block][column][32] (16 columns: in double-buffered chunks).
+//  * The workgroup stages its activations once in LDS.  1..8 columns: each
+//    value x of (block b, column c) as x = 2^e_bc (hi + lo), hi = f16(x
+//    2^-e_bc), lo = f16(x 2^-e_bc - hi), the power of two chosen per block
+//    and column so that the block's largest |x| lands in [2^14, 2^15):
+//    hi + lo holds x to 22 significant bits at any f32 magnitude.  16
+//    columns: f16 in double-buffered chunks.
 //  * One wave streams one row tile across its segment, PF tile columns
 //    ahead; each 16-byte load of a wave reads a contiguous 1 KiB stripe.
 //    The stream is a bounded buffer range, so loads past it return zeros
 //    without touching memory and the loop has no branch around its loads.
 //  * Weights become exact f16 values; per block, one matrix-core product
-//    (activation columns x the block's 16 rows) gives each lane its columns,
-//    scaled by the block's f16 scale into f32 accumulators.
+//    (activation rows x the block's 16 weight rows).  With 1..8 columns the
+//    hi parts sit in product rows 0..NC-1 and the lo parts in rows LO..,
+//    rows a narrow batch leaves idle, so the split costs no extra product;
+//    each lane scales its results by the block's f16 scale times 2^e_bc
+//    into f32 accumulators, and hi and lo sums meet once, after the stream.
 //  * Segments: S of them, contiguous K ranges or interleaved tile columns
 //    (segment q takes q, q + S, ...), chosen by the shape; summed in
 //    segment order, either by the last workgroup of the row group (from
@@ -25,12 +36,6 @@
 //    through LDS.  The order depends on the shape only, so each activation
 //    column of a batched call is bitwise equal to a 1-column call
 //    ("Architecture", Speculative decoding).
-//
-// Phases, for the fused FFN: a producer unit (gate/up) publishes the h rows
-// of its row group with coherent stores and then raises the ready flag of
-// each of its row tiles; a consumer unit (down) issues its first weight
-// loads, waits until the flags of the h row tiles its K segment reads are
-// raised, and reads h with coherent loads.
 #pragma once
 #include "common.h"
 #include "internal.h"
@@ -40,16 +45,9 @@ namespace qg {
 // Segment q of a K range of kt tile columns cut into n pieces.
 __host__ __device__ inline int seg_begin(int q, int kt, int n) { return (int)((int64_t)kt * q / n); }
 
-enum Phase { PH_PLAIN = 0, PH_PRODUCE = 1, PH_CONSUME = 2 };
-
-// Multiply form of the dot path: the matrix cores (true) or v_dot2 (false).
-#ifndef DOT_MF
-#define DOT_MF true
-#endif
-
-// Polls before a consumer gives up waiting (about 0.1 s); a correct launch
-// never gets near it, it only guarantees the kernel ends.
-constexpr int WAIT_POLLS = 1 << 20;
+// PH_PRODUCE: outputs are written with coherent (agent-scope) stores, for a
+// consumer in another workgroup of the same launch.
+enum Phase { PH_PLAIN = 0, PH_PRODUCE = 1 };
 
 struct DotArgs {
   const uint8_t *qs0, *qs1, *d0, *d1;
@@ -60,8 +58,7 @@ struct DotArgs {
   int SW;             // K segments inside one workgroup (<= 1: none): wave wk
                       // streams segment wk / R of row tile wk % R, R = waves / SW
   int IL;             // interleaved segments: segment q of n holds tile columns
-                      // q, q + n, q + 2n, ... (every unit stages all of K);
-                      // otherwise contiguous ranges
+                      // q, q + n, q + 2n, ...; otherwise contiguous ranges
   int G;              // row groups of R * RT row tiles
   int64_t units;      // G * S workgroups
   int64_t per_xcd;
@@ -79,21 +76,26 @@ struct DotArgs {
   int topk;
   int32_t *out_idx;
   float *out_val;
-  uint32_t *ready;    // fused FFN: one flag per h row tile, raised by its producer unit
-  int ready_n;        // fused FFN, consumer: h row tiles (flags) in all
-  uint32_t *err;      // fused FFN: set when a wait gave up
-  int NWU;            // waves of the unit (<= 0: every wave of the workgroup); the
-                      // other waves only take part in its barriers
   const float *gamma; // RMSNorm prologue: the weights (cols), and eps
   float norm_eps;
   const int32_t *xmap, *ymap;  // MoE: column c reads X column xmap[c], writes Y column ymap[c]
   int64_t xspan;      // bytes of X the columns may read (0: the ncols columns)
 };
 
-// The default `staged` hook of dot_unit: nothing.
-struct NoHook {
-  __device__ void operator()() const {}
-};
+// Floats of one row tile's segment partial: NI values per lane, 64 lanes
+// (NI: columns per lane, at most 4).
+__host__ __device__ constexpr int dot_part_floats(int nc) { return (nc < 4 ? nc : 4) * 64; }
+
+// LDS bytes of `ntiles` staged tile columns (4 blocks each) of `nc`
+// activation columns: 16 columns, f16 values; 1..8 columns, the hi and lo
+// halves of every value plus one f32 power of two per (block, column).
+__host__ __device__ constexpr size_t dot_stage_bytes(int64_t ntiles, int nc) {
+  return nc >= 16 ? (size_t)ntiles * TILE_BLOCKS * nc * 64 : (size_t)ntiles * TILE_BLOCKS * nc * (2 * 64 + 4);
+}
+
+// Smallest workgroup (waves) a streamed-staging unit of launch-time size
+// runs with: its per-thread chunk pieces are sized for it.
+constexpr int DOT_XS_WMIN = 8;
 
 // Register fence after a matrix-core product and the FMAs that read its
 // result.  The matrix core reads A and B and writes all four result
@@ -103,14 +105,6 @@ struct NoHook {
 // the FMAs produced, so it is ordered after those FMAs (which wait for the
 // product to complete) and all of A, B and D stay allocated until then, also
 // the result values no FMA reads (fewer than four columns).
-// Floats of one row tile's segment partial: NI values per lane, 64 lanes
-// (NI: columns per lane, at most 4 in the matrix-core form).
-__host__ __device__ constexpr int dot_part_floats(int nc) { return (DOT_MF ? (nc < 4 ? nc : 4) : nc) * 64; }
-
-// Smallest workgroup (waves) a streamed-staging unit of launch-time size
-// runs with: its per-thread chunk pieces are sized for it.
-constexpr int DOT_XS_WMIN = 8;
-
 template <int NI>
 __device__ __forceinline__ void mfma_fence(float (&acc)[NI], const h8 &A, const h8 &B, const f4 &D) {
   static_assert(NI >= 1 && NI <= 4, "columns per lane");
@@ -135,36 +129,66 @@ __device__ __forceinline__ void mfma_fence(float (&acc)[NI], const h8 (&A)[4], c
 }
 #undef QG_FENCE_IN
 
-// The unit (row group g, segment s) of the launch `a`.  RMSN (gate/up,
-// units that stage all of K): the activations are RMS-normalised first, as
-// x * gamma staged, times 1 / sqrt(mean(x^2) + eps) per column applied to
-// the two products (the same value, since the products are linear in x).
-// Returns true when
-// this workgroup emitted the outputs of row group g (its only segment, or
-// the last of its segments to finish).  For the argmax epilogue, (bv, bi)
-// then hold each lane's best (value, row).  `staged` runs once the
-// activations are in LDS and the first weight loads are in flight (the
-// fused FFN takes its next work unit there, so that round trip overlaps the
-// stream).
-template <int QT, int NC, int NMAT, int EPI, int RT, int PF, int WKT, int PH, bool MF = false,
-          class Hook = NoHook, bool RMSN = false>
+// The largest of a value over the four lanes of a DPP quad (all four active).
+__device__ __forceinline__ float quad_max(float m) {
+  const int b = __builtin_bit_cast(int, m);
+  m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0xB1, 0xF, 0xF, false)));
+  const int c = __builtin_bit_cast(int, m);
+  return fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(c, c, 0x4E, 0xF, 0xF, false)));
+}
+
+// The power of two of a block column whose largest magnitude is m: `up` =
+// 2^(14 - E) for m in [2^E, 2^(E+1)), so m * up lies in [2^14, 2^15) (below
+// the f16 maximum 65504 after rounding), and `down` = 1 / up.  Magnitudes
+// below 2^-112 (zero included) share the largest factor 2^126.
+__device__ __forceinline__ void block_pow2(float m, float &up, float &down) {
+  const uint32_t be = (__builtin_bit_cast(uint32_t, m) >> 23) & 0xFFu;
+  const uint32_t bc = be < 15u ? 15u : be;
+  up = __builtin_bit_cast(float, (268u - bc) << 23);
+  down = __builtin_bit_cast(float, (bc - 14u) << 23);
+}
+
+// x * up split into hi + lo, both f16 (round to nearest even): hi the
+// rounded value, lo the rounded remainder (the remainder itself is exact in
+// f32), so hi + lo agrees with x * up to 22 significant bits.
+__device__ __forceinline__ void split_hl(const float (&x)[8], float up, h8 &H, h8 &L) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float t = x[e] * up;
+    const _Float16 h = (_Float16)t;
+    H[e] = h;
+    L[e] = (_Float16)(t - (float)h);
+  }
+}
+
+// The unit (row group g, segment s) of the launch `a`.  RMSN (gate/up): the
+// activations are RMS-normalised first, as x * gamma staged, times
+// 1 / sqrt(mean(x^2) + eps) per column applied to the two products (the
+// same value, since the products are linear in x); every such unit reads
+// all of K for the column's squares.  Returns true when this workgroup
+// emitted the outputs of row group g (its only segment, or the last of its
+// segments to finish).  For the argmax epilogue, (bv, bi) then hold each
+// lane's best (value, row).
+template <int QT, int NC, int NMAT, int EPI, int RT, int PF, int WKT, int PH, bool RMSN = false>
 __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t *smem, uint32_t *flag,
-                                          float &bv, int32_t &bi, Hook staged = Hook()) {
+                                          float &bv, int32_t &bi) {
   // WKT == 0: one row tile per wave of the workgroup as launched (at least
   // XWMIN waves when the activations stream in chunks)
   const int NTHR = WKT > 0 ? WKT * 64 : (int)blockDim.x;
-  constexpr int XC = NC;  // activation columns in the LDS layout
-  // accumulators per lane: dot form, one per column; matrix-core form, the
-  // 4 D values of lane (r, sl) are columns 4 sl + i
-  constexpr int NI = MF ? (NC < 4 ? NC : 4) : NC;
-  constexpr int TB = QTraits<QT>::tile_bytes;
-  constexpr int QW = (QT == Q4) ? 1 : 2;  // 16-byte loads per lane per tile
-  constexpr int XAUX = PH == PH_CONSUME ? 16 : 0;  // sc1: h comes from other XCDs
   // Wide batches stream their activations in chunks of PF tile columns,
   // double-buffered in LDS and staged one chunk ahead of the products (the
   // whole segment would take several L2 round trips before the first
-  // product); narrow ones stage the whole segment up front.
+  // product); narrow ones stage the whole segment up front, as hi / lo
+  // pairs.
   constexpr bool XS = NC >= 16;
+  static_assert(XS ? NC == 16 : (NC >= 1 && NC <= 8), "column count");
+  constexpr int XC = XS ? NC : 2 * NC;  // activation rows of a block in LDS: hi, then lo
+  constexpr int LO = NC <= 4 ? 4 : 8;   // matrix-core row of the lo part of column 0
+  // accumulators per lane: the 4 D values of lane (r, sl) are product rows
+  // 4 sl + i
+  constexpr int NI = NC < 4 ? NC : 4;
+  constexpr int TB = QTraits<QT>::tile_bytes;
+  constexpr int QW = (QT == Q4) ? 1 : 2;  // 16-byte loads per lane per tile
   constexpr int CHV = PF * TILE_BLOCKS * NC * 4;   // 8-value pieces per chunk
   constexpr int CHH = PF * TILE_BLOCKS * NC * 32;  // halves per chunk buffer
   constexpr int XWMIN = WKT > 0 ? WKT : DOT_XS_WMIN;
@@ -172,16 +196,13 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wk = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // the workgroup's K range (staged in LDS), and inside it this wave's
-  // stream: all of it, or (SW > 1) in-workgroup segment wsg of SW.
-  // Interleaved segments: the workgroup stages all of K and the wave's
-  // segment q of nq takes tile columns q, q + nq, ... (wst = nq);
-  // contiguous ones: its range [wkt0, wkt0 + wnkt) of the staged columns.
+  // the workgroup's K range, and inside it this wave's stream: all of it,
+  // or (SW > 1) in-workgroup segment wsg of SW.  Interleaved segments: the
+  // wave's segment q of nq takes tile columns q, q + nq, ... (wst = nq);
+  // contiguous ones: its range [wkt0, wkt0 + wnkt) of the unit's columns.
   const int SW = (!XS && a.SW > 1) ? a.SW : 1;
-  const int NWA = a.NWU > 0 ? a.NWU : (NTHR >> 6);  // waves of the unit
-  const bool idle = wk >= NWA;                      // stages, waits at barriers, streams nothing
-  const int R = NWA / SW;
-  const int wrt = idle ? 0 : wk % R, wsg = idle ? 0 : wk / R;
+  const int R = (NTHR >> 6) / SW;
+  const int wrt = wk % R, wsg = wk / R;
   const bool IL = !XS && a.IL;
   const int kt0 = IL ? 0 : seg_begin(s, a.KT, a.S);
   const int nkt = IL ? a.KT : seg_begin(s + 1, a.KT, a.S) - kt0;
@@ -189,13 +210,27 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   const int wkt0 = IL ? wq_i : seg_begin(wsg, nkt, SW);        // first tile column, relative to kt0
   const int wst = IL ? wq_n : 1;                               // step between its tile columns
   const int wnkt = IL ? (nkt - wq_i + wq_n - 1) / wq_n : seg_begin(wsg + 1, nkt, SW) - wkt0;
-  const int64_t rt_base = idle ? (int64_t)a.NT : ((int64_t)g * R + wrt) * RT;
+  const int64_t rt_base = ((int64_t)g * R + wrt) * RT;
   const int r = lane & 15, sl = lane >> 4;
-  _Float16 *xs = (_Float16 *)smem;
 
-  // activations: a bounded range over the columns; a chunk outside the
-  // segment or the matrix reads zeros
-  const int nvec = nkt * TILE_BLOCKS * NC * 4;  // 8-value pieces of the segment
+  // Which activations the unit stages.  Interleaved segments across
+  // workgroups: only the unit's own tile columns (wq_i, wq_i + wq_n, ...),
+  // compacted; with the norm it still reads all of K (for the squares) and
+  // keeps its own columns.  Otherwise the unit's K range [kt0, kt0 + nkt).
+  const bool own = IL && SW == 1;
+  const int nlt = (own && !RMSN) ? wnkt : nkt;  // tile columns read
+  const int nst = own ? wnkt : nkt;             // tile columns staged
+  auto ld_tile = [&](int lt) -> int { return (own && !RMSN) ? wq_i + lt * wq_n : kt0 + lt; };
+  auto st_tile = [&](int lt) -> int {
+    if (own && RMSN) return lt % wq_n == wq_i ? lt / wq_n : -1;
+    return lt;
+  };
+  _Float16 *xs = (_Float16 *)smem;
+  float *scl = (float *)(smem + (size_t)nst * TILE_BLOCKS * XC * 64);  // [staged tile][column][block]
+
+  // activations: a bounded range over the columns; a piece outside the
+  // staged range or the matrix reads zeros
+  const int nvec = nlt * TILE_BLOCKS * NC * 4;  // 8-value pieces read by the unit (whole staging)
   const __amdgpu_buffer_rsrc_t rx =
       buf_range(a.X, (uint32_t)(a.xspan ? a.xspan : ((int64_t)(a.ncols - 1) * a.ldx + a.cols) * 4));
   // the X column piece v reads (through the column map, if any); a piece's
@@ -206,63 +241,89 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
     const int c = (v >> 2) % NC;
     return c < a.ncols && a.xmap ? a.xmap[c] : c;
   };
-  // piece v of the `span` pieces from tile column rel0 on: (block, column,
-  // 8 k) -> byte offset in X column xc, or past any range (reads zeros) when
-  // it lies outside the span, the segment or the matrix
-  auto x_off = [&](int v, int rel0, int span, int64_t xc) -> uint32_t {
+  // piece v = (block, column, 8 k) of the `span` pieces from tile column
+  // rel0 on (streamed chunks) or of the unit's read range (whole staging):
+  // its k, or -1 when it lies outside the span, the segment or the matrix
+  auto x_k = [&](int v, int rel0, int span) -> int64_t {
     const int qq = v & 3, c = (v >> 2) % NC, bl = (v >> 2) / NC;
-    const int64_t k = ((int64_t)(kt0 + rel0) * TILE_BLOCKS + bl) * 32 + qq * 8;
-    const bool ok = v < span && rel0 * TILE_BLOCKS + bl < nkt * TILE_BLOCKS && k < a.cols && c < a.ncols;
-    return ok ? (uint32_t)((xc * a.ldx + k) * 4) : 0xFFFFFFC0u;
+    const int64_t gb = XS ? (int64_t)(kt0 + rel0) * TILE_BLOCKS + bl
+                          : (int64_t)ld_tile(bl >> 2) * TILE_BLOCKS + (bl & 3);
+    const int64_t k = gb * 32 + qq * 8;
+    const bool ok = v < span && (!XS || rel0 * TILE_BLOCKS + bl < nkt * TILE_BLOCKS) && k < a.cols && c < a.ncols;
+    return ok ? k : -1;
   };
   // RMSNorm: gamma over the same 8 k of a piece (its range: cols floats;
-  // a piece outside reads zeros), and per staged piece the sum of its 8
+  // a piece outside reads zeros), and per piece read the sum of its 8
   // squares, [column][piece along K], past the staged activations and the
   // in-workgroup sums; then 1 / rms per column
   static_assert(!RMSN || (!XS && EPI == EPI_SILU), "RMSNorm prologue: gate/up, staged whole");
   const __amdgpu_buffer_rsrc_t rg = buf_range(a.gamma, RMSN ? (uint32_t)(a.cols * 4) : 0u);
-  const int npc = nkt * TILE_BLOCKS * 4;  // pieces of one column
-  float *ssq = (float *)(smem + (size_t)nkt * TILE_BLOCKS * NC * 64 +
+  const int npc = nlt * TILE_BLOCKS * 4;  // pieces of one column
+  float *ssq = (float *)(smem + dot_stage_bytes(nst, NC) +
                          (SW > 1 ? (size_t)(SW - 1) * R * NMAT * RT * NI * 64 * 4 : 0));
   float *inv_rms = ssq + (size_t)NC * npc;
   struct XPiece {
     u4 lo, hi, glo, ghi;
   };
   auto x_ld = [&](int v, int rel0, int span, int64_t xc, XPiece &pc) {
-    const uint32_t o = x_off(v, rel0, span, xc);
-    pc.lo = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, XAUX);
-    pc.hi = __builtin_amdgcn_raw_buffer_load_b128(rx, o + 16u, 0, XAUX);
+    const int64_t k = x_k(v, rel0, span);
+    const uint32_t o = k >= 0 ? (uint32_t)((xc * a.ldx + k) * 4) : 0xFFFFFFC0u;
+    pc.lo = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0);
+    pc.hi = __builtin_amdgcn_raw_buffer_load_b128(rx, o + 16u, 0, 0);
     if constexpr (RMSN) {
-      const int qq = v & 3, bl = (v >> 2) / NC;
-      const int64_t k = ((int64_t)(kt0 + rel0) * TILE_BLOCKS + bl) * 32 + qq * 8;
-      const uint32_t og = o != 0xFFFFFFC0u ? (uint32_t)(k * 4) : 0xFFFFFFC0u;
+      const uint32_t og = k >= 0 ? (uint32_t)(k * 4) : 0xFFFFFFC0u;
       pc.glo = __builtin_amdgcn_raw_buffer_load_b128(rg, og, 0, 0);
       pc.ghi = __builtin_amdgcn_raw_buffer_load_b128(rg, og + 16u, 0, 0);
     }
   };
+  // Every lane of a quad runs x_put together (a block column's four pieces
+  // are the four lanes of one quad: pieces are numbered (block, column,
+  // quarter) and the span is a multiple of 4), so the quad maximum below
+  // sees the whole block column.
   auto x_put = [&](int v, int span, _Float16 *dst, const XPiece &pc) {
-    if (v < span) {
-      const int qq = v & 3, c = (v >> 2) % NC, bl = (v >> 2) / NC;
-      float4 lo = __builtin_bit_cast(float4, pc.lo), hi = __builtin_bit_cast(float4, pc.hi);
-      if constexpr (RMSN) {
-        // the piece's squares in k order, then x * gamma
-        float q = lo[0] * lo[0];
-        q = __builtin_fmaf(lo[1], lo[1], q);
-        q = __builtin_fmaf(lo[2], lo[2], q);
-        q = __builtin_fmaf(lo[3], lo[3], q);
-        q = __builtin_fmaf(hi[0], hi[0], q);
-        q = __builtin_fmaf(hi[1], hi[1], q);
-        q = __builtin_fmaf(hi[2], hi[2], q);
-        q = __builtin_fmaf(hi[3], hi[3], q);
-        ssq[(size_t)c * npc + bl * 4 + qq] = q;
-        const float4 glo = __builtin_bit_cast(float4, pc.glo), ghi = __builtin_bit_cast(float4, pc.ghi);
+    const int qq = v & 3, c = (v >> 2) % NC, bl = (v >> 2) / NC;
+    float x[8];
+    {
+      const float4 lo = __builtin_bit_cast(float4, pc.lo), hi = __builtin_bit_cast(float4, pc.hi);
+      x[0] = lo[0]; x[1] = lo[1]; x[2] = lo[2]; x[3] = lo[3];
+      x[4] = hi[0]; x[5] = hi[1]; x[6] = hi[2]; x[7] = hi[3];
+    }
+    if constexpr (RMSN) {
+      // the piece's squares in k order, then x * gamma
+      float q = x[0] * x[0];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lo[e] *= glo[e];
-          hi[e] *= ghi[e];
-        }
+      for (int e = 1; e < 8; ++e) q = __builtin_fmaf(x[e], x[e], q);
+      if (v < span) ssq[(size_t)c * npc + bl * 4 + qq] = q;
+      const float4 glo = __builtin_bit_cast(float4, pc.glo), ghi = __builtin_bit_cast(float4, pc.ghi);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] *= glo[e];
+        x[4 + e] *= ghi[e];
       }
-      *(h8 *)(dst + ((size_t)bl * XC + c) * 32 + qq * 8) = cvt8(lo, hi);
+    }
+    if constexpr (XS) {
+      if (v < span) {
+        h8 hv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hv[e] = (_Float16)x[e];
+        *(h8 *)(dst + ((size_t)bl * XC + c) * 32 + qq * 8) = hv;
+      }
+    } else {
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, __builtin_fabsf(x[e]));
+      m = quad_max(m);
+      float up, down;
+      block_pow2(m, up, down);
+      h8 H, L;
+      split_hl(x, up, H, L);
+      const int st = st_tile(bl >> 2);
+      if (v < span && st >= 0) {
+        const int sb = st * TILE_BLOCKS + (bl & 3);
+        *(h8 *)(xs + ((size_t)sb * XC + c) * 32 + qq * 8) = H;
+        *(h8 *)(xs + ((size_t)sb * XC + NC + c) * 32 + qq * 8) = L;
+        if (qq == 0) scl[((size_t)st * NC + c) * TILE_BLOCKS + (bl & 3)] = down;
+      }
     }
   };
 
@@ -298,68 +359,43 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
       }
   };
 
-  // ---- 1. start the weight stream, and (first round) the activations
+  // ---- 1. start the activations (first round) and the weight stream
   constexpr int X0 = XS ? XR : 1;
   const int span0 = XS ? CHV : nvec;
   XPiece xp[X0];
   int64_t xcs[X0];
 #pragma unroll
   for (int i = 0; i < X0; ++i) xcs[i] = x_col(tid + i * NTHR);
-  if constexpr (PH != PH_CONSUME) {
 #pragma unroll
-    for (int i = 0; i < X0; ++i) x_ld(tid + i * NTHR, 0, span0, xcs[i], xp[i]);
-  }
+  for (int i = 0; i < X0; ++i) x_ld(tid + i * NTHR, 0, span0, xcs[i], xp[i]);
 #pragma unroll
   for (int p = 0; p < PF; ++p) load(p, p);
 
-  if constexpr (PH == PH_CONSUME) {
-    // the activations are h rows other workgroups produce: wait until the
-    // ready flags of the h row tiles of this segment's tile columns (8 row
-    // tiles of 16 to a column of 128) are raised
-    if (wk == 0) {
-      const int f0 = kt0 * 8, nf = (nkt * 8 < a.ready_n - f0) ? nkt * 8 : a.ready_n - f0;
-      for (int it = 0;; ++it) {
-        bool ok = true;
-        for (int j = lane; j < nf; j += 64) ok = ok && ld_agent_u32(a.ready + f0 + j) != 0u;
-        if (__all(ok)) break;
-        if (it >= WAIT_POLLS) {
-          if (lane == 0) st_agent_u32(a.err, 1u);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < X0; ++i) x_ld(tid + i * NTHR, 0, span0, xcs[i], xp[i]);
-  }
-
-  // ---- 2. staging: f16 in LDS, [block][column][32] (XS: chunk 0 into
-  // buffer 0).  Otherwise further pieces of the segment go in batches of XB
-  // whose loads are all issued before any is used.
+  // ---- 2. staging (XS: chunk 0 into buffer 0).  Otherwise further pieces
+  // of the read range go in batches of XB whose loads are all issued before
+  // any is used.
   //
-  // A piece past the segment is loaded (it reads zeros) but not stored, so
-  // no store waits for its load; left pending, that load would be waited
-  // for wherever its register is next written, which can be inside the
-  // weight stream, at every tile.  So each staging step ends with a wait of
-  // its own: after each batch, for everything (the weight tiles were issued
+  // A piece past the range is loaded (it reads zeros) but not stored, so no
+  // store waits for its load; left pending, that load would be waited for
+  // wherever its register is next written, which can be inside the weight
+  // stream, at every tile.  So each staging step ends with a wait of its
+  // own: after each batch, for everything (the weight tiles were issued
   // earlier and return first); after the first pieces, for everything with
-  // one matrix or when the activations came last, else for everything but
-  // the first weight tiles.  The wait at the loop's entry also shapes the
-  // waits the compiler places inside it: measured, one matrix streams best
-  // after the full wait (6-7 loads kept in flight per wave: decode down
-  // 14.0 -> 13.1 us), gate and up together after the partial one (the full
-  // wait keeps more in flight there and was 0.6 us slower).
+  // one matrix, else for everything but the first weight tiles.  The wait
+  // at the loop's entry also shapes the waits the compiler places inside
+  // it: measured, one matrix streams best after the full wait (6-7 loads
+  // kept in flight per wave: decode down 14.0 -> 13.1 us), gate and up
+  // together after the partial one (the full wait keeps more in flight
+  // there and was 0.6 us slower).
   constexpr int NWL = PF * NMAT * RT * (QW + 1);  // loads of the first PF tile columns
   static_assert(NWL <= 63, "wait count");
   constexpr int WAIT_ALL = 0x0F70;                // vmcnt(0), other counters untouched
-  constexpr int WAIT_X0 =
-      (PH == PH_CONSUME || NMAT == 1) ? WAIT_ALL : (WAIT_ALL | (NWL & 15) | ((NWL >> 4) << 14));
+  constexpr int WAIT_X0 = NMAT == 1 ? WAIT_ALL : (WAIT_ALL | (NWL & 15) | ((NWL >> 4) << 14));
 #pragma unroll
   for (int i = 0; i < X0; ++i) x_put(tid + i * NTHR, span0, xs, xp[i]);
   if constexpr (!XS) {
     __builtin_amdgcn_s_waitcnt(WAIT_X0);
-    constexpr int XB = 4;
+    constexpr int XB = RMSN && QT == Q8 && NMAT == 2 ? 2 : 4;  // fewer registers where gate, up and gamma crowd them
     for (int v0 = tid + NTHR; v0 < nvec; v0 += XB * NTHR) {
       XPiece pc[XB];
 #pragma unroll
@@ -382,7 +418,6 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
     }
     __syncthreads();
   }
-  staged();
 
   // ---- 3. stream the weight tiles of the segment
   float acc[NMAT][RT][NI];
@@ -394,53 +429,26 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
       for (int c = 0; c < NI; ++c) acc[m][t][c] = 0.0f;
 
   const Q4Magic mg = q4_magic();
-  // matrix-core A operands of a tile's four blocks: lane (r, sl) holds
-  // column r, k 8 sl .. 8 sl + 7.  Lanes of columns past NC keep zeros: they
-  // never load (exec-masked), so the registers set to zero here stay zero.
-  // 16 columns issue the four blocks' reads and products together (the
-  // products of a tile overlap the LDS reads); narrower batches, whose
-  // streams are bound by memory, keep one block at a time (fewer registers:
-  // the fused FFN keeps two workgroups per CU).
-#ifndef DOT_GA_MIN
-#define DOT_GA_MIN 16
-#endif
-  constexpr bool GA = NC >= DOT_GA_MIN;
+  // matrix-core A operands: lane (r, sl) holds product row r, k 8 sl ..
+  // 8 sl + 7.  16 columns: row r is column r.  1..8 columns: row c < NC is
+  // column c's hi part, row LO + c its lo part; lanes of the other rows
+  // never load (exec-masked), so the zeros set here stay.  16 columns issue
+  // the four blocks' reads and products together (the products of a tile
+  // overlap the LDS reads); narrower batches, whose streams are bound by
+  // memory, keep one block at a time.
   h8 A[TILE_BLOCKS];
 #pragma unroll
   for (int j = 0; j < TILE_BLOCKS; ++j) A[j] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+  const int arow = XS ? r : (r < NC ? r : (r >= LO && r < LO + NC ? NC + r - LO : -1));
+  // 1..8 columns: the column of this lane's result i is cb + i (its hi or
+  // its lo part); past NC it is unused, and reads a valid scale
+  const int cb = (4 * sl) & (LO - 1);
   auto compute = [&](int slot, int rel) {
-    // block index in LDS: the staged range's own (this wave's stream starts
-    // wkt0 tile columns in), or, streaming, the slot of tile column rel in
-    // its chunk's buffer
-    const int bl0 = XS ? ((((rel / PF) & 1) * PF) + rel % PF) * TILE_BLOCKS : (wkt0 + rel * wst) * TILE_BLOCKS;
-    if constexpr (MF) {
-      // per block: D (16 columns x 16 rows) = X_blk^T W_blk^T on the matrix
-      // cores from the exact f16 weights, then each lane's 4 D values get
-      // the block scale of its row, blocks in order
-      if constexpr (!GA) {
+    if constexpr (XS) {
+      // the slot of tile column rel in its chunk's buffer
+      const int bl0 = ((((rel / PF) & 1) * PF) + rel % PF) * TILE_BLOCKS;
 #pragma unroll
-        for (int j = 0; j < TILE_BLOCKS; ++j) {
-          if (NC == 16 || r < NC) A[0] = *(const h8 *)(xs + ((size_t)(bl0 + j) * XC + r) * 32 + sl * 8);
-#pragma unroll
-          for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-            for (int t = 0; t < RT; ++t) {
-              h2 w[4];
-              if constexpr (QT == Q4) unpack_q4(wq[slot][m][t][0][j], w, mg);
-              else unpack_q8(wq[slot][m][t][j >> 1][(j & 1) * 2], wq[slot][m][t][j >> 1][(j & 1) * 2 + 1], w);
-              const h8 B = {w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
-              const f4 D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], B, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-              const float dj = scale_of(wd[slot][m][t], j);
-#pragma unroll
-              for (int i = 0; i < NI; ++i) acc[m][t][i] = __builtin_fmaf(dj, D[i], acc[m][t][i]);
-              mfma_fence(acc[m][t], A[0], B, D);
-            }
-        }
-        return;
-      }
-#pragma unroll
-      for (int j = 0; j < TILE_BLOCKS; ++j)
-        if (NC == 16 || r < NC) A[j] = *(const h8 *)(xs + ((size_t)(bl0 + j) * XC + r) * 32 + sl * 8);
+      for (int j = 0; j < TILE_BLOCKS; ++j) A[j] = *(const h8 *)(xs + ((size_t)(bl0 + j) * XC + r) * 32 + sl * 8);
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -463,34 +471,34 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
           }
           mfma_fence(acc[m][t], A, B, D);
         }
-      return;
-    }
+    } else {
+      // staged tile of this tile column: compacted (own columns), else its
+      // place in the unit's range
+      const int st = own ? rel : wkt0 + rel * wst;
 #pragma unroll
-    for (int j = 0; j < TILE_BLOCKS; ++j) {
-      h2 xv[NC][4];
+      for (int j = 0; j < TILE_BLOCKS; ++j) {
+        if (arow >= 0) A[0] = *(const h8 *)(xs + ((size_t)(st * TILE_BLOCKS + j) * XC + arow) * 32 + sl * 8);
+        float sv[NI];  // the power of two of each of this lane's columns in block j
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const h8 xx = *(const h8 *)(xs + ((size_t)(bl0 + j) * XC + c) * 32 + sl * 8);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) xv[c][p] = lo_pair(xx, p);
-      }
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int t = 0; t < RT; ++t) {
-          h2 w[4];
-          if constexpr (QT == Q4) unpack_q4(wq[slot][m][t][0][j], w, mg);
-          else unpack_q8(wq[slot][m][t][j >> 1][(j & 1) * 2], wq[slot][m][t][j >> 1][(j & 1) * 2 + 1], w);
-          const float dj = scale_of(wd[slot][m][t], j);
-#pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            float p = dot2_first(w[0], xv[c][0]);
-            p = __builtin_amdgcn_fdot2(w[1], xv[c][1], p, false);
-            p = __builtin_amdgcn_fdot2(w[2], xv[c][2], p, false);
-            p = __builtin_amdgcn_fdot2(w[3], xv[c][3], p, false);
-            acc[m][t][c] = __builtin_fmaf(dj, p, acc[m][t][c]);
-          }
+        for (int i = 0; i < NI; ++i) {
+          const int cc = cb + i < NC ? cb + i : NC - 1;
+          sv[i] = scl[((size_t)st * NC + cc) * TILE_BLOCKS + j];
         }
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int t = 0; t < RT; ++t) {
+            h2 w[4];
+            if constexpr (QT == Q4) unpack_q4(wq[slot][m][t][0][j], w, mg);
+            else unpack_q8(wq[slot][m][t][j >> 1][(j & 1) * 2], wq[slot][m][t][j >> 1][(j & 1) * 2 + 1], w);
+            const h8 B = {w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
+            const f4 D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], B, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            const float dj = scale_of(wd[slot][m][t], j);
+#pragma unroll
+            for (int i = 0; i < NI; ++i) acc[m][t][i] = __builtin_fmaf(dj * sv[i], D[i], acc[m][t][i]);
+            mfma_fence(acc[m][t], A[0], B, D);
+          }
+      }
     }
   };
 
@@ -521,33 +529,23 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
         load(p, k + p + PF);
       }
     }
-  }
-
-  // ---- 4. per-row sums.  Dot form: after the butterfly every lane of row r
-  // holds the same (bitwise) sum of the wave's segment, and lane (r, sl)
-  // handles the outputs o = t * NC + c with o % 4 == sl.  Matrix-core form:
-  // lane (r, sl) holds column 4 sl + i of row r.
-  if constexpr (!MF) {
+    // hi and lo sums of each column meet: lane (r, sl) of a hi row adds
+    // lane (r, sl + LO / 4)
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
       for (int t = 0; t < RT; ++t)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          float v = acc[m][t][c];
-          v += __shfl_xor(v, 16);
-          v += __shfl_xor(v, 32);
-          acc[m][t][c] = v;
-        }
+        for (int i = 0; i < NI; ++i) acc[m][t][i] += __shfl_down(acc[m][t][i], LO * 4);
   }
+
+  // ---- 4. per-row sums: lane (r, sl) holds column 4 sl + i of row r (1..8
+  // columns: in its hi lanes, which now hold hi + lo)
   // (t, i) -> the column this lane handles, or -1
   auto col_of = [&](int t, int i) -> int {
-    if constexpr (MF) {
-      const int c = 4 * sl + i;
-      return c < NC ? c : -1;
-    } else {
-      return ((t * NC + i) & 3) == sl ? i : -1;
-    }
+    (void)t;
+    const int c = 4 * sl + i;
+    return c < NC ? c : -1;
   };
 
   auto emit = [&](int t, int c, const float (&v)[NMAT]) {
@@ -582,7 +580,7 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   // same order as the partials of segments across workgroups
   if (SW > 1) {
     constexpr int NV = NMAT * RT * NI;
-    float *red = (float *)(smem + (size_t)((a.KT + a.S - 1) / a.S) * TILE_BLOCKS * NC * 64);
+    float *red = (float *)(smem + dot_stage_bytes(nst, NC));
     if (wsg > 0) {
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
@@ -681,17 +679,6 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
           const int c = col_of(t, i);
           if (c >= 0 && rt_base + t < a.NT) emit(t, c, v[t][i]);
         }
-    }
-  }
-
-  if constexpr (PH == PH_PRODUCE) {
-    // h rows of row group g are out: raise the flags of its row tiles once
-    // every wave's stores are acknowledged
-    if (emitted && a.ready) {
-      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      const int64_t f = (int64_t)g * R * RT + tid;
-      if (tid < R * RT && f < a.NT) st_agent_u32(a.ready + f, 1u);
     }
   }
   return emitted;

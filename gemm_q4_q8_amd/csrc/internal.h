@@ -71,21 +71,8 @@ int launch_qmv(const QmvCall &c);  // returns 0 or a QG_ status
 int launch_repack(int qtype, int64_t n_mat, int64_t rows, int64_t cols, const void *blocks,
                   void *qs, void *d, hipStream_t stream);
 
-// One fused decode FFN: h = SiLU(Wg x) * (Wu x); y += Wd h (one token).
-struct FfnCall {
-  int qtype;
-  const void *g_qs, *g_d, *u_qs, *u_d, *d_qs, *d_d;
-  int64_t hidden, ffn;
-  const float *x;
-  float *h, *y;
-  void *ws;
-  size_t ws_bytes;
-  hipStream_t stream;
-};
-size_t ffn_ws_bytes(int64_t hidden, int64_t ffn);
-int launch_ffn(const FfnCall &c);
-
-// Streaming-read probe (the bench's measured read ceiling).
+// Requantisation to Q8_0, the stand-alone RMSNorm, and the streaming-read
+// probe (the bench's measured read ceiling).
 int launch_requant_q8_0(int src_type, int64_t nb, const void *src, void *dst, void *stream);
 int launch_rmsnorm(const float *X, int64_t ldx, int64_t cols, int ncols, const float *gamma, float eps, float *Y,
                    int64_t ldy, void *stream);

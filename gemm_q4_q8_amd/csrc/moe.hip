@@ -52,7 +52,7 @@ struct MoeArgs {
   int32_t *topk_idx;
   float *topk_w;
   uint32_t *rcnt, *dcnt, *gcnt, *nused;
-  float *logits, *pw, *hbuf, *zbuf, *gpart;
+  float *logits, *pw, *hbuf, *zbuf, *gpart, *dpart;
   int32_t *sel, *used_e, *used_cnt, *used_slot;
   int S_gu, G_gu, G_dn;   // gate/up K segments and row groups (at Fmax rows); down row groups
   int W_gu, W_dn;         // row tiles per gate/up and per down workgroup
@@ -64,9 +64,15 @@ struct MoeArgs {
   const float *rms_w;     // RMSNorm ahead of router and experts (NULL: none), and eps
   float rms_eps;
   int64_t gpart_per;      // gate/up partial floats per listed expert
+  int S_dn;               // entry-grouped down: K segments across workgroups
+  uint32_t *dscnt;        // ... their counters, per (listed expert, row group)
+  int64_t dpart_per;      // ... and partial floats per listed expert
 };
 
 static size_t a256(size_t v) { return (v + 255) & ~size_t(255); }
+// LDS of one wave of the token-major down projection: its h column as hi
+// and lo halves (f16 each) and one f32 power of two per block of 32
+__host__ __device__ constexpr size_t dn_tok_stage_bytes(int64_t fmax) { return (size_t)fmax * 4 + (size_t)fmax / 8; }
 __host__ __device__ static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Column capacity of the expert units: a work-list entry holds at most this
@@ -91,10 +97,11 @@ static void moe_waves(int T, int &w_gu, int &w_dn) {
 }
 
 struct MoeLayout {
-  size_t nused, logits, sel, pw, used_e, used_cnt, used_slot, hbuf, zbuf, gpart, total;
+  size_t nused, logits, sel, pw, used_e, used_cnt, used_slot, hbuf, zbuf, gpart, dpart, total;
   int64_t umax;  // work-list entries at most
-  size_t rcnt_w, dcnt_w, gcnt_w, sync_words;  // counter word offsets
-  int S_gu, G_gu, G_dn, nsh;
+  size_t rcnt_w, dcnt_w, gcnt_w, dscnt_w, sync_words;  // counter word offsets
+  int S_gu, G_gu, G_dn, nsh, S_dn;
+  int64_t dpart_per;
   int W_gu, W_dn, sw_gu, dn_tok, R_dt;
   int64_t gpart_per;
 };
@@ -114,22 +121,28 @@ static MoeLayout moe_layout(const qg_moe *m, int T) {
   // when the workgroup stays within 16 waves and its activations (all of
   // K, nc columns) plus the segment sums fit comfortably in LDS
   L.sw_gu = L.S_gu > 1 && L.W_gu * L.S_gu <= MOE_WMAX &&
-            (size_t)(m->hidden / 128) * TILE_BLOCKS * nc * 64 + (size_t)L.S_gu * L.W_gu * 2 * 4 * 64 * 4 <= 65536;
+            dot_stage_bytes(m->hidden / 128, nc) + (size_t)L.S_gu * L.W_gu * 2 * 4 * 64 * 4 <= 65536;
   // the token-major down projection (see moe_down_tok_kernel; measured
   // faster than the entry-grouped one at 1 to 16 tokens) while each wave's
   // h column fits in LDS; more row tiles per wave as tokens add workgroups
   L.R_dt = T <= 2 ? 1 : T <= 8 ? 2 : 4;
-  L.dn_tok = (size_t)(m->top_k + 1) * (Fmax * 2 + (size_t)L.R_dt * 64) <= 131072;
+  L.dn_tok = (size_t)(m->top_k + 1) * (dn_tok_stage_bytes(Fmax) + (size_t)L.R_dt * 64) <= 131072;
   L.G_gu = (int)cdiv(Fmax / 16, L.W_gu);
   L.G_dn = (int)cdiv(m->hidden / 16, L.W_dn);
   L.gpart_per = L.S_gu > 1 ? (int64_t)L.S_gu * 2 * (Fmax / 16) * dot_part_floats(nc) : 0;
+  // entry-grouped down (wide experts): contiguous K segments across
+  // workgroups so that each unit's h columns fit in 64 KiB of LDS
+  L.S_dn = L.dn_tok ? 1 : (int)cdiv((int64_t)dot_stage_bytes(Fmax / 128, nc), 65536);
+  if (L.S_dn > Fmax / 128) L.S_dn = (int)(Fmax / 128);
+  L.dpart_per = L.S_dn > 1 ? (int64_t)L.S_dn * (m->hidden / 16) * dot_part_floats(nc) : 0;
   // counters (in the shared counter words): the router's, one per down row
   // group, one per (listed expert, gate/up row group)
   L.rcnt_w = 0;
   L.dcnt_w = 4;
   L.gcnt_w = L.dcnt_w + (size_t)L.G_dn;
   L.nsh = m->sh_ffn > 0 ? (T + nc - 1) / nc : 0;  // shared-expert entries
-  L.sync_words = L.gcnt_w + (size_t)(umax + L.nsh) * L.G_gu;
+  L.dscnt_w = L.gcnt_w + (size_t)(umax + L.nsh) * L.G_gu;
+  L.sync_words = L.dscnt_w + (L.S_dn > 1 ? (size_t)(umax + L.nsh) * L.G_dn : 0);
   size_t o = QG_WS_SYNC_BYTES;
   L.nused = o; o += 256;
   L.logits = o; o += a256((size_t)T * m->n_expert * 4);
@@ -141,6 +154,7 @@ static MoeLayout moe_layout(const qg_moe *m, int T) {
   L.hbuf = o; o += a256((size_t)slots * Fmax * 4);
   L.zbuf = o; o += a256((size_t)slots * m->hidden * 4);
   L.gpart = o; o += a256((size_t)(umax + L.nsh) * L.gpart_per * 4);
+  L.dpart = o; o += a256((size_t)(umax + L.nsh) * L.dpart_per * 4);
   L.total = o;
   return L;
 }
@@ -463,7 +477,7 @@ __global__ void __launch_bounds__(MOE_WMAX * 64) moe_gateup_kernel(MoeArgs a) {
   __syncthreads();  // the column maps
   float bv = 0.0f;
   int32_t bi = 0;
-  dot_unit<QT, NC, 2, EPI_SILU, 1, PF, 0, PH_PLAIN, true, NoHook, RMSN>(d, g, s, smem, &flag, bv, bi);
+  dot_unit<QT, NC, 2, EPI_SILU, 1, PF, 0, PH_PLAIN, RMSN>(d, g, s, smem, &flag, bv, bi);
 }
 
 template <int QT, int NC, int PF>
@@ -473,11 +487,14 @@ __global__ void __launch_bounds__(MOE_WMAX * 64) moe_down_kernel(MoeArgs a) {
   __shared__ uint32_t flag;
   __shared__ int32_t s_x[TMAX], s_y[TMAX];
   const int tid = threadIdx.x;
-  const int u = blockIdx.x / a.G_dn, g = blockIdx.x % a.G_dn;
+  const int per = a.G_dn * a.S_dn;
+  const int u = blockIdx.x / per, g = (blockIdx.x % per) / a.S_dn, s = blockIdx.x % a.S_dn;
   DotArgs d = {};
   if (!moe_expert<false, NC>(a, u, d, s_x, s_y)) return;
-  d.S = 1;
+  d.S = a.S_dn;
   d.G = a.G_dn;
+  d.part = a.dpart + (int64_t)u * a.dpart_per;
+  d.cnt = a.dscnt + (int64_t)u * a.G_dn;
   d.X = a.hbuf;
   d.ldx = a.Fmax;
   d.xspan = (int64_t)(a.T * a.k + a.T) * a.Fmax * 4;  // every slot's h
@@ -486,8 +503,9 @@ __global__ void __launch_bounds__(MOE_WMAX * 64) moe_down_kernel(MoeArgs a) {
   __syncthreads();  // the column maps
   float bv = 0.0f;
   int32_t bi = 0;
-  // coherent stores of z (the combine below may run on another XCD)
-  dot_unit<QT, NC, 1, EPI_STORE, 1, PF, 0, PH_PRODUCE, true>(d, g, 0, smem, &flag, bv, bi);
+  // coherent stores of z (the combine below may run on another XCD); with
+  // K segments, only the workgroup that adds them up goes on
+  if (!dot_unit<QT, NC, 1, EPI_STORE, 1, PF, 0, PH_PRODUCE>(d, g, s, smem, &flag, bv, bi)) return;
 
   // ---- weighted combine of this row group, by the last expert to finish
   const uint32_t target = *a.nused + (a.SF > 0 ? (uint32_t)((a.T + NC - 1) / NC) : 0u);
@@ -525,7 +543,9 @@ __global__ void __launch_bounds__(MOE_WMAX * 64) moe_down_kernel(MoeArgs a) {
 // ------------------------------------- 3'. down, token-major (few tokens)
 // One workgroup per (token, group of R row tiles of the output), one wave
 // per routed slot of the token plus one for the shared expert.  Each wave
-// stages its slot's h column in LDS (f16) and streams its expert's R row
+// stages its slot's h column in LDS (as the dot unit stages activations:
+// hi and lo f16 halves under one power of two per block of 32, so h keeps
+// f32 range and 22 significant bits) and streams its expert's R row
 // tiles over all of K; the waves' row sums meet in LDS and are combined in
 // rank order, sum_k p_k z_k + shared, then added to Y once.  An expert is
 // read once per token that routed to it (not once for all of them, as in
@@ -570,12 +590,28 @@ __global__ void __launch_bounds__(576) moe_down_tok_kernel(MoeArgs a) {
 #pragma unroll
   for (int p = 0; p < PF; ++p) load(p, p);
 
-  // h column of this slot, f16 in LDS, [block][32]
-  _Float16 *xs = (_Float16 *)smem + (size_t)w * a.Fmax;
+  // h column of this slot in LDS: hi halves [K], lo halves [K], then the
+  // power of two of each block of 32.  A block is 4 pieces of 8 values,
+  // the 4 lanes of one quad (K / 8 is a multiple of 16, so every quad runs
+  // the loop together).
+  uint8_t *wbase = smem + (size_t)w * dn_tok_stage_bytes(a.Fmax);
+  _Float16 *xh = (_Float16 *)wbase, *xl = xh + a.Fmax;
+  float *xsc = (float *)(wbase + (size_t)a.Fmax * 4);
   const float *hcol = a.hbuf + (int64_t)slot * a.Fmax;
   for (int v = lane; v < (int)(K / 8); v += 64) {
     const float4 lo = *(const float4 *)(hcol + v * 8), hi = *(const float4 *)(hcol + v * 8 + 4);
-    *(h8 *)(xs + v * 8) = cvt8(lo, hi);
+    const float x[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, __builtin_fabsf(x[e]));
+    m = quad_max(m);
+    float up, down;
+    block_pow2(m, up, down);
+    h8 H, L;
+    split_hl(x, up, H, L);
+    *(h8 *)(xh + v * 8) = H;
+    *(h8 *)(xl + v * 8) = L;
+    if ((v & 3) == 0) xsc[v >> 2] = down;
   }
   __syncthreads();
 
@@ -589,18 +625,22 @@ __global__ void __launch_bounds__(576) moe_down_tok_kernel(MoeArgs a) {
       const int n = n0 + p;
       if (n < ntile) {
         const int i = n / KT, kt = n % KT;
+        const float4 s4 = *(const float4 *)(xsc + kt * TILE_BLOCKS);
         float part = 0.0f;
 #pragma unroll
         for (int j = 0; j < TILE_BLOCKS; ++j) {
           h2 wv[4];
           if constexpr (QT == Q4) unpack_q4(wq[p][0][j], wv, mg);
           else unpack_q8(wq[p][j >> 1][(j & 1) * 2], wq[p][j >> 1][(j & 1) * 2 + 1], wv);
-          const h8 xx = *(const h8 *)(xs + (kt * TILE_BLOCKS + j) * 32 + sl * 8);
-          float q = dot2_first(wv[0], lo_pair(xx, 0));
-          q = __builtin_amdgcn_fdot2(wv[1], lo_pair(xx, 1), q, false);
-          q = __builtin_amdgcn_fdot2(wv[2], lo_pair(xx, 2), q, false);
-          q = __builtin_amdgcn_fdot2(wv[3], lo_pair(xx, 3), q, false);
-          part = __builtin_fmaf(scale_of(wd[p], j), q, part);
+          const h8 hh = *(const h8 *)(xh + (kt * TILE_BLOCKS + j) * 32 + sl * 8);
+          const h8 hl = *(const h8 *)(xl + (kt * TILE_BLOCKS + j) * 32 + sl * 8);
+          // w . hi, then w . lo into the same f32 sum (exact f16 products)
+          float q = dot2_first(wv[0], lo_pair(hh, 0));
+#pragma unroll
+          for (int u = 1; u < 4; ++u) q = __builtin_amdgcn_fdot2(wv[u], lo_pair(hh, u), q, false);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) q = __builtin_amdgcn_fdot2(wv[u], lo_pair(hl, u), q, false);
+          part = __builtin_fmaf(scale_of(wd[p], j) * s4[j], q, part);
         }
 #pragma unroll
         for (int ii = 0; ii < RMAX; ++ii)
@@ -611,7 +651,7 @@ __global__ void __launch_bounds__(576) moe_down_tok_kernel(MoeArgs a) {
   }
 
   // row sums (the 4 slices of each row), then the combine through LDS
-  float *zs = (float *)(smem + (size_t)nw * a.Fmax * 2);  // [wave][R * 16]
+  float *zs = (float *)(smem + (size_t)nw * dn_tok_stage_bytes(a.Fmax));  // [wave][R * 16]
 #pragma unroll
   for (int i = 0; i < RMAX; ++i) {
     float v = acc[i];
@@ -644,11 +684,10 @@ static int grant(const void *kern, size_t lds, size_t &granted) {
   return QG_OK;
 }
 
-// LDS of a unit: the whole segment of activations, or (16 columns) two
-// chunks of PF tile columns
-template <int NC, int PF>
+// LDS of a unit's staged activations: at most ceil(KT / S) tile columns
+template <int NC>
 static size_t unit_lds(int64_t KT, int S) {
-  return NC >= 16 ? (size_t)2 * PF * TILE_BLOCKS * NC * 64 : (size_t)cdiv(KT, S) * TILE_BLOCKS * NC * 64;
+  return dot_stage_bytes(cdiv(KT, S), NC);
 }
 
 template <int QT, int NC>
@@ -668,12 +707,11 @@ static int launch_moe_t(const MoeCall &c, MoeArgs &a) {
   // with the RMSNorm, every unit stages all of K (interleaved segments)
   if (a.rms_w && !(a.il_gu || a.sw_gu)) return QG_EUNSUPPORTED;
   auto kg = a.rms_w ? moe_gateup_kernel<QT, NC, PFG, true> : moe_gateup_kernel<QT, NC, PFG, false>;
-  // in-workgroup or interleaved segments: all of K staged (plus, in the
-  // workgroup, the segment sums; with the norm, the squares per piece and
-  // 1 / rms per column)
-  size_t lds_g = (a.sw_gu || a.il_gu) ? unit_lds<NC, PFG>(a.H / 128, 1) + (a.sw_gu ? (size_t)(a.S_gu - 1) * a.W_gu * 2 *
-                                                                (NC < 4 ? NC : 4) * 64 * 4 : 0)
-                         : unit_lds<NC, PFG>(a.H / 128, a.S_gu);
+  // in-workgroup segments: all of K staged, plus the segment sums; across
+  // workgroups, the unit's tile columns (with the norm, also the squares
+  // per piece and 1 / rms per column)
+  size_t lds_g = a.sw_gu ? unit_lds<NC>(a.H / 128, 1) + (size_t)(a.S_gu - 1) * a.W_gu * 2 * (NC < 4 ? NC : 4) * 64 * 4
+                         : unit_lds<NC>(a.H / 128, a.S_gu);
   if (a.rms_w) lds_g += (size_t)NC * (a.H / 128) * TILE_BLOCKS * 4 * 4 + (size_t)NC * 4;
   const int sx = a.sw_gu ? 1 : a.S_gu;
   const int wg_threads = a.W_gu * (a.sw_gu ? a.S_gu : 1) * 64;
@@ -688,7 +726,7 @@ static int launch_moe_t(const MoeCall &c, MoeArgs &a) {
   if (a.dn_tok) {
     auto kt = moe_down_tok_kernel<QT, PFD>;
     const int nw = a.k + (a.SF > 0 ? 1 : 0);
-    const size_t lds_t = (size_t)nw * a.Fmax * 2 + (size_t)nw * a.R_dt * 16 * 4;
+    const size_t lds_t = (size_t)nw * dn_tok_stage_bytes(a.Fmax) + (size_t)nw * a.R_dt * 16 * 4;
     static size_t granted_t = 65536;
     if ((st = grant((const void *)kt, lds_t, granted_t))) return st;
     clear_hip_error();
@@ -696,11 +734,12 @@ static int launch_moe_t(const MoeCall &c, MoeArgs &a) {
     return launch_status();
   }
   auto kd = moe_down_kernel<QT, NC, PFD>;
-  const size_t lds_d = unit_lds<NC, PFD>(a.Fmax / 128, 1);
+  const size_t lds_d = unit_lds<NC>(a.Fmax / 128, a.S_dn);
   static size_t granted_d = 65536;
   if ((st = grant((const void *)kd, lds_d, granted_d))) return st;
   clear_hip_error();
-  hipLaunchKernelGGL(kd, dim3((unsigned)((int64_t)(a.Umax + a.nsh) * a.G_dn)), dim3(a.W_dn * 64), lds_d, c.stream, a);
+  hipLaunchKernelGGL(kd, dim3((unsigned)((int64_t)(a.Umax + a.nsh) * a.G_dn * a.S_dn)), dim3(a.W_dn * 64), lds_d,
+                     c.stream, a);
   return launch_status();
 }
 
@@ -769,6 +808,10 @@ int launch_moe(const MoeCall &c) {
   a.G_gu = L.G_gu;
   a.G_dn = L.G_dn;
   a.gpart_per = L.gpart_per;
+  a.S_dn = L.S_dn;
+  a.dpart = (float *)(ws + L.dpart);
+  a.dpart_per = L.dpart_per;
+  a.dscnt = w32 + L.dscnt_w;
   a.W_gu = L.W_gu;
   a.W_dn = L.W_dn;
   a.sw_gu = L.sw_gu;

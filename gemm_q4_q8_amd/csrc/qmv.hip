@@ -26,7 +26,7 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // --------------------------------------------------------------- dot path
 // WKT > 0: workgroups of WKT waves; WKT == 0: as many waves as launched, at
 // most WMAX (the launch planner picks the size per shape).
-template <int QT, int NC, int NMAT, int EPI, int RT, int PF, int WKT, bool MF, int WMAX, bool RMSN = false>
+template <int QT, int NC, int NMAT, int EPI, int RT, int PF, int WKT, int WMAX, bool RMSN = false>
 __global__ void __launch_bounds__(WMAX * 64) dot_kernel(DotArgs a) {
   static_assert(WKT <= WMAX, "workgroup size");
   const int NTHR = WKT > 0 ? WKT * 64 : (int)blockDim.x;
@@ -44,7 +44,7 @@ __global__ void __launch_bounds__(WMAX * 64) dot_kernel(DotArgs a) {
   float bv = __builtin_nanf("");  // argmax: this lane's best (value, row)
   int32_t bi = 0x7fffffff;
   const bool emitted =
-      dot_unit<QT, NC, NMAT, EPI, RT, PF, WKT, PH_PLAIN, MF, NoHook, RMSN>(a, g, s, smem, &flag, bv, bi);
+      dot_unit<QT, NC, NMAT, EPI, RT, PF, WKT, PH_PLAIN, RMSN>(a, g, s, smem, &flag, bv, bi);
 
   if constexpr (EPI == EPI_TOPK) {
     if (!emitted) return;
@@ -224,27 +224,24 @@ int device_cus() {
 }
 
 constexpr int DOT_STREAMS = 2048;     // (row tile, segment, matrix) weight streams
-constexpr size_t DOT_X_LDS = 65536;   // staged activations per workgroup
+constexpr size_t DOT_X_LDS = 131072;  // staged activations of a contiguous segment, 8 columns
 constexpr size_t LDS_HARD = 163840;   // gfx950 LDS per workgroup
 constexpr size_t DOT_SW_LDS = 131072;  // in-workgroup segments: activations + sums
-constexpr size_t DOT_IL_LDS = 81920;   // interleaved segments: all of K for 8 columns
+constexpr int64_t DOT_IL_TILES = 40;   // interleaved segments up to K = 5120
 
-// Interleaved K segments (segment q of n: tile columns q, q + n, ...) when
-// every unit can stage all of K for up to 8 columns; a function of the
-// shape only, so every column count of a shape sums in the same order.
-// Measured (K = 5120 and 2048): the waves of a workgroup then stream
-// neighbouring tiles and finish together (gate/up 21.7 -> 20.3 us, verify
-// Q4_0 4 columns 15.5 -> 15.1 us).
-bool dot_interleaved(int64_t cols) {
-  const int64_t KT = cdiv(cols / 32, 4);
-  return (size_t)KT * TILE_BLOCKS * 8 * 64 <= DOT_IL_LDS;
-}
+// Interleaved K segments (segment q of n: tile columns q, q + n, ...) up to
+// K = 5120 (both model widths of the pages); a function of the shape only,
+// so every column count of a shape sums in the same order.  Measured
+// (K = 5120 and 2048): the waves of a workgroup then stream neighbouring
+// tiles and finish together (gate/up 21.7 -> 20.3 us, verify Q4_0 4
+// columns 15.5 -> 15.1 us).
+bool dot_interleaved(int64_t cols) { return cdiv(cols / 32, 4) <= DOT_IL_TILES; }
 
 // K segments of the dot path: about DOT_STREAMS weight streams of one row
 // tile and one segment each (measured on the decode shapes: more streams,
 // or more bytes in flight per stream, only lengthen the queues and the
 // tail), at least 4 tile columns per segment, and few enough tile columns
-// per segment that `ncols_max` columns of f16 activations fit in DOT_X_LDS.
+// per segment that `ncols_max` columns of staged activations fit in DOT_X_LDS.
 int gemv_segments(int64_t rows, int64_t cols, int nmat, int ncols_max) {
   const int64_t NT = cdiv(rows, 16), KT = cdiv(cols / 32, 4);
   int64_t s;
@@ -265,7 +262,7 @@ int gemv_segments(int64_t rows, int64_t cols, int nmat, int ncols_max) {
     if (s < 2 && 2 * want >= 3 * NT) s = 2;
   }
   if (s > KT / 4) s = KT / 4;
-  const int64_t lds_min = cdiv(KT * TILE_BLOCKS * ncols_max * 64, (int64_t)DOT_X_LDS);
+  const int64_t lds_min = cdiv((int64_t)dot_stage_bytes(KT, ncols_max), (int64_t)DOT_X_LDS);
   if (s < lds_min) s = lds_min;
   if (s < 1) s = 1;
   if (s > KT) s = KT;
@@ -319,7 +316,7 @@ static int grant_lds(const void *kern, size_t lds, size_t &granted) {
 
 // S segments across workgroups; SW > 1: segments inside each workgroup
 // instead (S must then be 1), W = R * SW waves for R row tiles.
-template <int QT, int NC, int NMAT, int EPI, int RT, int PF, int WKT, bool MF, int WMAX = WKT, bool RMSN = false>
+template <int QT, int NC, int NMAT, int EPI, int RT, int PF, int WKT, int WMAX = WKT, bool RMSN = false>
 static int launch_dot_t(const QmvCall &c, int S, int W = WKT, int SW = 1) {
   const int64_t NT = cdiv(c.rows, 16), KT = cdiv(c.cols / 32, 4);
   const int64_t NTu = cdiv(c.n_rows, 16);  // row tiles actually produced
@@ -370,10 +367,6 @@ static int launch_dot_t(const QmvCall &c, int S, int W = WKT, int SW = 1) {
   a.part = (float *)(ws + off);
   a.out_idx = c.out_idx;
   a.out_val = c.out_val;
-  a.ready = nullptr;
-  a.ready_n = 0;
-  a.err = nullptr;
-  a.NWU = 0;
   a.gamma = RMSN ? c.gamma : nullptr;
   a.norm_eps = c.norm_eps;
   // the RMSNorm prologue needs every unit to stage all of K
@@ -386,15 +379,14 @@ static int launch_dot_t(const QmvCall &c, int S, int W = WKT, int SW = 1) {
   const size_t need = off + pbytes;
   if (need > c.ws_bytes) return QG_EWORKSPACE;
 
-  // staged activations: the whole segment, or (16 columns) two chunks of
-  // PF tile columns
-  // PF tile columns (+ the in-workgroup segment sums)
-  size_t lds = NC >= 16 ? (size_t)2 * PF * TILE_BLOCKS * NC * 64
-                        : (size_t)(a.IL ? KT : cdiv(KT, S)) * TILE_BLOCKS * NC * 64;
-  lds += (size_t)(SW - 1) * (W / SW) * NMAT * RT * (MF ? (NC < 4 ? NC : 4) : NC) * 64 * 4;
+  // staged activations: the unit's tile columns (all of K with in-workgroup
+  // segments; at most ceil(KT / S) otherwise), or (16 columns) two chunks
+  // of PF tile columns; then the in-workgroup segment sums
+  size_t lds = NC >= 16 ? dot_stage_bytes(2 * PF, NC) : dot_stage_bytes(SW > 1 ? KT : cdiv(KT, S), NC);
+  lds += (size_t)(SW - 1) * (W / SW) * NMAT * RT * (NC < 4 ? NC : 4) * 64 * 4;
   if (RMSN) lds += (size_t)NC * KT * TILE_BLOCKS * 4 * 4 + (size_t)NC * 4;  // squares per piece, 1/rms
   if (lds > LDS_HARD - 1024) return QG_EUNSUPPORTED;
-  auto kern = dot_kernel<QT, NC, NMAT, EPI, RT, PF, WKT, MF, WMAX, RMSN>;
+  auto kern = dot_kernel<QT, NC, NMAT, EPI, RT, PF, WKT, WMAX, RMSN>;
   static size_t granted = 65536;  // per instantiation; only ever raised
   int st = grant_lds((const void *)kern, lds, granted);
   if (st) return st;
@@ -426,7 +418,6 @@ static int launch_dot(const QmvCall &c, int S) {
   constexpr int PF0 = 4 / (NMAT * QW);
   constexpr int PF = PF0 < 2 ? 2 : PF0;
   const int64_t NTu = cdiv(c.n_rows, 16);
-  constexpr bool MF = DOT_MF;
   const int W = dot_waves(NTu, S);
   const int plan = c.plan & ~(PLAN_FORCED | PLAN_S_MASK);
   bool sw_ok = false, sw = false;
@@ -446,8 +437,8 @@ static int launch_dot(const QmvCall &c, int S) {
     const int64_t ncu = device_cus();
     R = cdiv(NTu, ncu);
     const int64_t KT = cdiv(c.cols / 32, 4);
-    constexpr int NI = MF ? (NC < 4 ? NC : 4) : NC;
-    const size_t lds = (size_t)KT * TILE_BLOCKS * NC * 64 + (size_t)(S - 1) * R * NMAT * NI * 64 * 4;
+    constexpr int NI = NC < 4 ? NC : 4;
+    const size_t lds = dot_stage_bytes(KT, NC) + (size_t)(S - 1) * R * NMAT * NI * 64 * 4;
     const int64_t u_sw = cdiv(NTu, R), u_cross = cdiv(NTu, (int64_t)W) * S;
     const int64_t cu_bytes = (int64_t)NMAT * R * KT * (QTraits<QT>::tile_bytes + TILE_D_BYTES);
     sw_ok = R * S <= 16 && lds <= DOT_SW_LDS;
@@ -463,13 +454,13 @@ static int launch_dot(const QmvCall &c, int S) {
     } else {
       const int Wp = plan & PLAN_W_MASK;
       if (Wp > 16) return QG_EUNSUPPORTED;
-      if (Wp <= 8) return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 8, RMSN>(c, S, Wp);
-      return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 16, RMSN>(c, S, Wp);
+      if (Wp <= 8) return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, 8, RMSN>(c, S, Wp);
+      return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, 16, RMSN>(c, S, Wp);
     }
   }
-  if (sw) return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 16, RMSN>(c, 1, (int)(R * S), S);
-  if (W <= 8) return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 8, RMSN>(c, S, W);
-  return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, MF, 16, RMSN>(c, S, W);
+  if (sw) return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, 16, RMSN>(c, 1, (int)(R * S), S);
+  if (W <= 8) return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, 8, RMSN>(c, S, W);
+  return launch_dot_t<QT, NC, NMAT, EPI, 1, PF, 0, 16, RMSN>(c, S, W);
 }
 
 template <int QT, int EPI>
@@ -529,8 +520,8 @@ static int launch_gemm16(const QmvCall &c) {
     if (plan < 8 || plan > 16) return QG_EUNSUPPORTED;  // 8 to 16 waves, no in-workgroup segments
     W = plan;
   }
-  if (W == 8) return launch_dot_t<QT, 16, 1, EPI, 1, 2, 8, true>(c, S);
-  return launch_dot_t<QT, 16, 1, EPI, 1, 2, 0, true, 16>(c, S, W);
+  if (W == 8) return launch_dot_t<QT, 16, 1, EPI, 1, 2, 8>(c, S);
+  return launch_dot_t<QT, 16, 1, EPI, 1, 2, 0, 16>(c, S, W);
 }
 
 template <int QT>

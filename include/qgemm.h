@@ -227,31 +227,6 @@ int qg_rmsnorm(const float *X, int64_t ldx, int64_t cols, int32_t ncols, const f
                float eps, float *Y, int64_t ldy, void *stream);
 
 /* ------------------------------------------------------------------------
- * Fused decode FFN, one token  [ENG Kernel families: fused gate/up with SiLU
- * applied before writing, and the residual epilogue y += W x]
- *
- *   h = silu(Wg x) * (Wu x);   y += Wd h
- *   Wg, Wu: ffn x hidden; Wd: hidden x ffn; all of one qtype.  x (hidden),
- *   h (ffn, written) and y (hidden, read and written) are device vectors;
- *   x and h 16-byte aligned, y 4-byte aligned; none may overlap.
- * The results are bitwise equal to gateup_silu followed by a 1-column qgemv
- * with accumulate on the same inputs; the difference is one persistent
- * launch in which the down projection's weight stream starts
- * while the gate/up rows are still being finished.  Each down work unit
- * waits (on device flags) for the h rows it reads, so the call needs the
- * whole device: run nothing else on the GPU concurrently with it.  The
- * wait is bounded; word 2 of the workspace (a uint32) becomes nonzero if a
- * wait ever gave up, and the outputs of that call are then invalid (it
- * stays set until the caller clears it).
- * ------------------------------------------------------------------------ */
-size_t qg_ffn_ws_bytes(int64_t hidden, int64_t ffn);
-
-int ffn_fused(int qtype, const void *g_qs, const void *g_d, const void *u_qs,
-              const void *u_d, const void *d_qs, const void *d_d, int64_t hidden,
-              int64_t ffn, const float *x, float *h, float *y,
-              void *ws, size_t ws_bytes, void *stream);
-
-/* ------------------------------------------------------------------------
  * LM head + greedy argmax  [ARCH One token, end to end: head over the whole
  * vocabulary, greedy sampling on the GPU; ENG Fewer passes: GPU argmax,
  * lowest-index tie-breaking; ENG Speculation: drafts over a row prefix]

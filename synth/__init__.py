@@ -85,6 +85,25 @@ def gen_weights(qtype: int, rows: int, cols: int, sigma: float,
     raise ValueError(f"unsupported qtype {qtype}")
 
 
+def flip_scale_signs(raw: np.ndarray, g: np.random.Generator, p: float = 0.5) -> np.ndarray:
+    """A copy of GGUF Q4_0 / Q8_0 blocks (uint8 [..., bytes]) with the sign bit
+    of each block's f16 scale (bit 7 of byte 1) set with probability p.  The
+    block definition allows any f16 scale; real files carry both signs."""
+    out = np.array(raw, dtype=np.uint8, copy=True)
+    out[..., 1] |= (g.random(out.shape[:-1]) < p).astype(np.uint8) << 7
+    return out
+
+
+def plant_q8_min(raw: np.ndarray, g: np.random.Generator, p: float) -> np.ndarray:
+    """A copy of GGUF Q8_0 blocks (uint8 [..., 34]) with each weight byte set
+    to 0x80 (int8 -128, a valid weight the uniform draw never makes) with
+    probability p."""
+    out = np.array(raw, dtype=np.uint8, copy=True)
+    w = out[..., 2:34]
+    w[g.random(w.shape) < p] = 0x80
+    return out
+
+
 def gen_x(cols: int, ncols: int, cfg_id: int, col0: int = 0) -> np.ndarray:
     """Activations, f32 [cols, ncols]; column j comes from rng(cfg_id, 100 + col0 + j)."""
     x = np.empty((cols, ncols), dtype=np.float32)

@@ -187,29 +187,6 @@ def test_rmsnorm_checks():
     assert rn(X, 128, 128, 2, G, 1e-6, X, 256, None) == EINVAL           # in place with another ld
 
 
-def test_ffn_fused_checks():
-    x, h, y, ws = FAKE + (1 << 28), FAKE + (2 << 28), FAKE + (3 << 28), FAKE + (4 << 28)
-    H, F = 256, 384
-    wsb = L.qg_ffn_ws_bytes(H, F)
-    assert wsb > 0
-    assert L.qg_ffn_ws_bytes(H, 100) == 0
-
-    def call(qt=2, H=H, F=F, x=x, h=h, y=y, ws=ws, wsb=wsb, g=FAKE):
-        return L.ffn_fused(qt, g, FAKE, FAKE, FAKE, FAKE, FAKE, H, F, x, h, y, ws, wsb, None)
-
-    assert call(qt=4) == EINVAL
-    assert call(g=None) == EINVAL
-    assert call(F=100) == ESHAPE
-    assert call(H=0) == ESHAPE
-    assert call(x=x + 4) == EALIGN          # x and h are read as 16-byte vectors
-    assert call(h=h + 8) == EALIGN
-    assert call(y=y + 2) == EALIGN
-    assert call(h=x + 64) == EINVAL         # overlaps
-    assert call(y=h) == EINVAL
-    assert call(wsb=wsb - 1) == EWS
-    assert call(ws=ws + 16) == EALIGN
-
-
 def test_repack_checks():
     src, qs, d = FAKE, FAKE + (1 << 30), FAKE + (2 << 30)
     assert L.qg_repack(2, 1, 16, 128, None, qs, d, None) == EINVAL

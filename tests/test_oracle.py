@@ -41,7 +41,8 @@ def test_f16_decode_agrees_with_numpy_for_all_finite_patterns():
 
 
 # ---------------------------------------------------------- hand-worked blocks
-@pytest.mark.parametrize("name,qtype", [("q4_0_block.txt", Q4), ("q8_0_block.txt", Q8)])
+@pytest.mark.parametrize("name,qtype", [("q4_0_block.txt", Q4), ("q8_0_block.txt", Q8),
+                                        ("q4_0_block_neg_scale.txt", Q4), ("q8_0_block_min.txt", Q8)])
 def test_hand_worked_block(name, qtype):
     raw, g = _block(name)
     raw = raw.reshape(1, 1, -1)
