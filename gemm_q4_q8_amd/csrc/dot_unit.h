@@ -14,11 +14,11 @@
 //
 // How (MI355X):
 //  * The workgroup stages its activations once in LDS.  1..8 columns: each
-//    value x of (block b, column c) as x = 2^e_bc (hi + lo), hi = f16(x
-//    2^-e_bc), lo = f16(x 2^-e_bc - hi), the power of two chosen per block
-//    and column so that the block's largest |x| lands in [2^14, 2^15):
-//    hi + lo holds x to 22 significant bits at any f32 magnitude.  16
-//    columns: f16 in double-buffered chunks.
+//    value x of (tile column t, column c) as x = 2^e_tc (hi + lo), hi =
+//    f16(x 2^-e_tc), lo = f16(x 2^-e_tc - hi), the power of two chosen per
+//    128 values of a column so that their largest |x| lands in [2^14,
+//    2^15): hi + lo holds x to 22 significant bits at any f32 magnitude.
+//    16 columns: f16 in double-buffered chunks.
 //  * One wave streams one row tile across its segment, PF tile columns
 //    ahead; each 16-byte load of a wave reads a contiguous 1 KiB stripe.
 //    The stream is a bounded buffer range, so loads past it return zeros
@@ -27,8 +27,9 @@
 //    (activation rows x the block's 16 weight rows).  With 1..8 columns the
 //    hi parts sit in product rows 0..NC-1 and the lo parts in rows LO..,
 //    rows a narrow batch leaves idle, so the split costs no extra product;
-//    each lane scales its results by the block's f16 scale times 2^e_bc
-//    into f32 accumulators, and hi and lo sums meet once, after the stream.
+//    each lane sums its results over the tile's four blocks, each times the
+//    block's f16 scale, then adds that tile sum times 2^e_tc into its f32
+//    accumulators; hi and lo sums meet once, after the stream.
 //  * Segments: S of them, contiguous K ranges or interleaved tile columns
 //    (segment q takes q, q + S, ...), chosen by the shape; summed in
 //    segment order, either by the last workgroup of the row group (from
@@ -86,11 +87,16 @@ struct DotArgs {
 // (NI: columns per lane, at most 4).
 __host__ __device__ constexpr int dot_part_floats(int nc) { return (nc < 4 ? nc : 4) * 64; }
 
+// Columns of the per-tile powers of two in LDS (a multiple of 4, so a lane
+// reads its four columns as one 16-byte vector).
+__host__ __device__ constexpr int dot_scale_cols(int nc) { return (nc + 3) & ~3; }
+
 // LDS bytes of `ntiles` staged tile columns (4 blocks each) of `nc`
 // activation columns: 16 columns, f16 values; 1..8 columns, the hi and lo
-// halves of every value plus one f32 power of two per (block, column).
+// halves of every value plus one f32 power of two per (tile, column).
 __host__ __device__ constexpr size_t dot_stage_bytes(int64_t ntiles, int nc) {
-  return nc >= 16 ? (size_t)ntiles * TILE_BLOCKS * nc * 64 : (size_t)ntiles * TILE_BLOCKS * nc * (2 * 64 + 4);
+  return nc >= 16 ? (size_t)ntiles * TILE_BLOCKS * nc * 64
+                  : (size_t)ntiles * (TILE_BLOCKS * nc * 2 * 64 + dot_scale_cols(nc) * 4);
 }
 
 // Smallest workgroup (waves) a streamed-staging unit of launch-time size
@@ -129,19 +135,21 @@ __device__ __forceinline__ void mfma_fence(float (&acc)[NI], const h8 (&A)[4], c
 }
 #undef QG_FENCE_IN
 
-// The largest of a value over the four lanes of a DPP quad (all four active).
-__device__ __forceinline__ float quad_max(float m) {
-  const int b = __builtin_bit_cast(int, m);
-  m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0xB1, 0xF, 0xF, false)));
-  const int c = __builtin_bit_cast(int, m);
-  return fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(c, c, 0x4E, 0xF, 0xF, false)));
+// The largest of a value over the 16 lanes of a DPP row (all active): the
+// quad permutes [1,0,3,2] and [2,3,0,1], then the half-row mirror and the
+// row mirror (each step pairs lanes holding maxima of disjoint groups).
+__device__ __forceinline__ float row16_max(float m) {
+#pragma unroll
+  for (int step = 0; step < 4; ++step)
+    m = fmaxf(m, __builtin_bit_cast(float, dpp_partner(__builtin_bit_cast(int, m), step)));
+  return m;
 }
 
-// The power of two of a block column whose largest magnitude is m: `up` =
+// The power of two of a tile column whose largest magnitude is m: `up` =
 // 2^(14 - E) for m in [2^E, 2^(E+1)), so m * up lies in [2^14, 2^15) (below
 // the f16 maximum 65504 after rounding), and `down` = 1 / up.  Magnitudes
 // below 2^-112 (zero included) share the largest factor 2^126.
-__device__ __forceinline__ void block_pow2(float m, float &up, float &down) {
+__device__ __forceinline__ void tile_pow2(float m, float &up, float &down) {
   const uint32_t be = (__builtin_bit_cast(uint32_t, m) >> 23) & 0xFFu;
   const uint32_t bc = be < 15u ? 15u : be;
   up = __builtin_bit_cast(float, (268u - bc) << 23);
@@ -226,7 +234,8 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
     return lt;
   };
   _Float16 *xs = (_Float16 *)smem;
-  float *scl = (float *)(smem + (size_t)nst * TILE_BLOCKS * XC * 64);  // [staged tile][column][block]
+  constexpr int SCC = dot_scale_cols(NC);
+  float *scl = (float *)(smem + (size_t)nst * TILE_BLOCKS * XC * 64);  // [staged tile][SCC columns]
 
   // activations: a bounded range over the columns; a piece outside the
   // staged range or the matrix reads zeros
@@ -237,15 +246,21 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   // column does not change from chunk to chunk, so streamed staging looks
   // it up once, not inside the weight stream (a map load there would make
   // every chunk wait for all weight loads in flight)
+  // Pieces (8 values) are numbered (block, column, quarter) when
+  // streaming 16 columns, and (tile column, column, block, quarter) when
+  // staging 1..8 columns: the 16 pieces of one tile column of one column
+  // are then the 16 lanes of one DPP row (the span is a multiple of 16).
+  auto p_col = [&](int v) -> int { return XS ? (v >> 2) % NC : (v >> 4) % NC; };
   auto x_col = [&](int v) -> int64_t {
-    const int c = (v >> 2) % NC;
+    const int c = p_col(v);
     return c < a.ncols && a.xmap ? a.xmap[c] : c;
   };
   // piece v = (block, column, 8 k) of the `span` pieces from tile column
   // rel0 on (streamed chunks) or of the unit's read range (whole staging):
   // its k, or -1 when it lies outside the span, the segment or the matrix
   auto x_k = [&](int v, int rel0, int span) -> int64_t {
-    const int qq = v & 3, c = (v >> 2) % NC, bl = (v >> 2) / NC;
+    const int qq = v & 3, c = p_col(v);
+    const int bl = XS ? (v >> 2) / NC : ((v >> 4) / NC) * TILE_BLOCKS + ((v >> 2) & 3);  // block read
     const int64_t gb = XS ? (int64_t)(kt0 + rel0) * TILE_BLOCKS + bl
                           : (int64_t)ld_tile(bl >> 2) * TILE_BLOCKS + (bl & 3);
     const int64_t k = gb * 32 + qq * 8;
@@ -276,12 +291,11 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
       pc.ghi = __builtin_amdgcn_raw_buffer_load_b128(rg, og + 16u, 0, 0);
     }
   };
-  // Every lane of a quad runs x_put together (a block column's four pieces
-  // are the four lanes of one quad: pieces are numbered (block, column,
-  // quarter) and the span is a multiple of 4), so the quad maximum below
-  // sees the whole block column.
+  // Every lane of a DPP row runs x_put together, so the row maximum below
+  // sees the whole tile column of its column.
   auto x_put = [&](int v, int span, _Float16 *dst, const XPiece &pc) {
-    const int qq = v & 3, c = (v >> 2) % NC, bl = (v >> 2) / NC;
+    const int qq = v & 3, c = p_col(v);
+    const int bl = XS ? (v >> 2) / NC : ((v >> 4) / NC) * TILE_BLOCKS + ((v >> 2) & 3);
     float x[8];
     {
       const float4 lo = __builtin_bit_cast(float4, pc.lo), hi = __builtin_bit_cast(float4, pc.hi);
@@ -312,9 +326,9 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
       float m = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) m = fmaxf(m, __builtin_fabsf(x[e]));
-      m = quad_max(m);
+      m = row16_max(m);
       float up, down;
-      block_pow2(m, up, down);
+      tile_pow2(m, up, down);
       h8 H, L;
       split_hl(x, up, H, L);
       const int st = st_tile(bl >> 2);
@@ -322,7 +336,7 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
         const int sb = st * TILE_BLOCKS + (bl & 3);
         *(h8 *)(xs + ((size_t)sb * XC + c) * 32 + qq * 8) = H;
         *(h8 *)(xs + ((size_t)sb * XC + NC + c) * 32 + qq * 8) = L;
-        if (qq == 0) scl[((size_t)st * NC + c) * TILE_BLOCKS + (bl & 3)] = down;
+        if ((v & 15) == 0) scl[(size_t)st * SCC + c] = down;
       }
     }
   };
@@ -431,15 +445,15 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   const Q4Magic mg = q4_magic();
   // matrix-core A operands: lane (r, sl) holds product row r, k 8 sl ..
   // 8 sl + 7.  16 columns: row r is column r.  1..8 columns: row c < NC is
-  // column c's hi part, row LO + c its lo part; lanes of the other rows
-  // never load (exec-masked), so the zeros set here stay.  16 columns issue
-  // the four blocks' reads and products together (the products of a tile
-  // overlap the LDS reads); narrower batches, whose streams are bound by
-  // memory, keep one block at a time.
+  // column c's hi part, row LO + c its lo part.  Row r of A reaches only
+  // row r of the product, so the lanes of the other rows load any staged
+  // row (that of column 0): their results sit in accumulators nothing reads,
+  // and every lane loads without a branch.  16 columns issue the four
+  // blocks' reads and products together (the products of a tile overlap
+  // the LDS reads); narrower batches, whose streams are bound by memory,
+  // keep one block at a time.
   h8 A[TILE_BLOCKS];
-#pragma unroll
-  for (int j = 0; j < TILE_BLOCKS; ++j) A[j] = h8{0, 0, 0, 0, 0, 0, 0, 0};
-  const int arow = XS ? r : (r < NC ? r : (r >= LO && r < LO + NC ? NC + r - LO : -1));
+  const int arow = XS ? r : (r < NC ? r : (r >= LO && r < LO + NC ? NC + r - LO : 0));
   // 1..8 columns: the column of this lane's result i is cb + i (its hi or
   // its lo part); past NC it is unused, and reads a valid scale
   const int cb = (4 * sl) & (LO - 1);
@@ -475,15 +489,12 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
       // staged tile of this tile column: compacted (own columns), else its
       // place in the unit's range
       const int st = own ? rel : wkt0 + rel * wst;
+      // the powers of two of this lane's columns cb .. cb + 3 in this tile
+      const float4 sv = *(const float4 *)(scl + (size_t)st * SCC + cb);
+      float ts[NMAT][RT][NI];  // the tile's sums, block by block
 #pragma unroll
       for (int j = 0; j < TILE_BLOCKS; ++j) {
-        if (arow >= 0) A[0] = *(const h8 *)(xs + ((size_t)(st * TILE_BLOCKS + j) * XC + arow) * 32 + sl * 8);
-        float sv[NI];  // the power of two of each of this lane's columns in block j
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const int cc = cb + i < NC ? cb + i : NC - 1;
-          sv[i] = scl[((size_t)st * NC + cc) * TILE_BLOCKS + j];
-        }
+        A[0] = *(const h8 *)(xs + ((size_t)(st * TILE_BLOCKS + j) * XC + arow) * 32 + sl * 8);
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -495,10 +506,16 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
             const f4 D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], B, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
             const float dj = scale_of(wd[slot][m][t], j);
 #pragma unroll
-            for (int i = 0; i < NI; ++i) acc[m][t][i] = __builtin_fmaf(dj * sv[i], D[i], acc[m][t][i]);
-            mfma_fence(acc[m][t], A[0], B, D);
+            for (int i = 0; i < NI; ++i) ts[m][t][i] = j == 0 ? dj * D[i] : __builtin_fmaf(dj, D[i], ts[m][t][i]);
+            mfma_fence(ts[m][t], A[0], B, D);
           }
       }
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+          for (int i = 0; i < NI; ++i) acc[m][t][i] = __builtin_fmaf(sv[i], ts[m][t][i], acc[m][t][i]);
     }
   };
 

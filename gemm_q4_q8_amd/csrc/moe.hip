@@ -71,8 +71,8 @@ struct MoeArgs {
 
 static size_t a256(size_t v) { return (v + 255) & ~size_t(255); }
 // LDS of one wave of the token-major down projection: its h column as hi
-// and lo halves (f16 each) and one f32 power of two per block of 32
-__host__ __device__ constexpr size_t dn_tok_stage_bytes(int64_t fmax) { return (size_t)fmax * 4 + (size_t)fmax / 8; }
+// and lo halves (f16 each) and one f32 power of two per tile column of 128
+__host__ __device__ constexpr size_t dn_tok_stage_bytes(int64_t fmax) { return (size_t)fmax * 4 + (size_t)fmax / 32; }
 __host__ __device__ static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Column capacity of the expert units: a work-list entry holds at most this
@@ -544,7 +544,7 @@ __global__ void __launch_bounds__(MOE_WMAX * 64) moe_down_kernel(MoeArgs a) {
 // One workgroup per (token, group of R row tiles of the output), one wave
 // per routed slot of the token plus one for the shared expert.  Each wave
 // stages its slot's h column in LDS (as the dot unit stages activations:
-// hi and lo f16 halves under one power of two per block of 32, so h keeps
+// hi and lo f16 halves under one power of two per 128 values, so h keeps
 // f32 range and 22 significant bits) and streams its expert's R row
 // tiles over all of K; the waves' row sums meet in LDS and are combined in
 // rank order, sum_k p_k z_k + shared, then added to Y once.  An expert is
@@ -591,9 +591,9 @@ __global__ void __launch_bounds__(576) moe_down_tok_kernel(MoeArgs a) {
   for (int p = 0; p < PF; ++p) load(p, p);
 
   // h column of this slot in LDS: hi halves [K], lo halves [K], then the
-  // power of two of each block of 32.  A block is 4 pieces of 8 values,
-  // the 4 lanes of one quad (K / 8 is a multiple of 16, so every quad runs
-  // the loop together).
+  // power of two of each tile column of 128.  A tile column is 16 pieces of
+  // 8 values, the 16 lanes of one DPP row (K / 8 is a multiple of 16, so
+  // every row runs the loop together).
   uint8_t *wbase = smem + (size_t)w * dn_tok_stage_bytes(a.Fmax);
   _Float16 *xh = (_Float16 *)wbase, *xl = xh + a.Fmax;
   float *xsc = (float *)(wbase + (size_t)a.Fmax * 4);
@@ -604,14 +604,14 @@ __global__ void __launch_bounds__(576) moe_down_tok_kernel(MoeArgs a) {
     float m = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) m = fmaxf(m, __builtin_fabsf(x[e]));
-    m = quad_max(m);
+    m = row16_max(m);
     float up, down;
-    block_pow2(m, up, down);
+    tile_pow2(m, up, down);
     h8 H, L;
     split_hl(x, up, H, L);
     *(h8 *)(xh + v * 8) = H;
     *(h8 *)(xl + v * 8) = L;
-    if ((v & 3) == 0) xsc[v >> 2] = down;
+    if ((v & 15) == 0) xsc[v >> 4] = down;
   }
   __syncthreads();
 
@@ -625,7 +625,6 @@ __global__ void __launch_bounds__(576) moe_down_tok_kernel(MoeArgs a) {
       const int n = n0 + p;
       if (n < ntile) {
         const int i = n / KT, kt = n % KT;
-        const float4 s4 = *(const float4 *)(xsc + kt * TILE_BLOCKS);
         float part = 0.0f;
 #pragma unroll
         for (int j = 0; j < TILE_BLOCKS; ++j) {
@@ -640,11 +639,12 @@ __global__ void __launch_bounds__(576) moe_down_tok_kernel(MoeArgs a) {
           for (int u = 1; u < 4; ++u) q = __builtin_amdgcn_fdot2(wv[u], lo_pair(hh, u), q, false);
 #pragma unroll
           for (int u = 0; u < 4; ++u) q = __builtin_amdgcn_fdot2(wv[u], lo_pair(hl, u), q, false);
-          part = __builtin_fmaf(scale_of(wd[p], j) * s4[j], q, part);
+          part = __builtin_fmaf(scale_of(wd[p], j), q, part);
         }
+        const float sc = xsc[kt];
 #pragma unroll
         for (int ii = 0; ii < RMAX; ++ii)
-          if (ii == i) acc[ii] += part;
+          if (ii == i) acc[ii] = __builtin_fmaf(sc, part, acc[ii]);
       }
       load(p, n + PF);
     }
