@@ -49,6 +49,18 @@ class qg_moe(ctypes.Structure):
     ]
 
 
+class qg_gemm16_problem(ctypes.Structure):
+    _fields_ = [
+        ("qtype", _i32), ("accumulate", _i32),
+        ("qs", _vp), ("d", _vp),
+        ("rows", _i64), ("cols", _i64),
+        ("X", _vp), ("ldx", _i64),
+        ("Y", _vp), ("ldy", _i64),
+    ]
+
+
+BATCH_MAX = 8
+
 _SIGS = {
     "qg_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "qg_last_hip_error": (ctypes.c_char_p, []),
@@ -63,6 +75,8 @@ _SIGS = {
     "qg_gemm16_ws_bytes": (_sz, [ctypes.c_int, _i64, _i64]),
     "qgemm16": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i32,
                                _vp, _sz, _vp]),
+    "qg_gemm16_batch_ws_bytes": (_sz, [ctypes.POINTER(qg_gemm16_problem), _i32]),
+    "qgemm16_batch": (ctypes.c_int, [ctypes.POINTER(qg_gemm16_problem), _i32, _vp, _sz, _vp]),
     "qg_gateup_ws_bytes": (_sz, [_i64, _i64]),
     "gateup_silu": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _i32,
                                    _vp, _i64, _vp, _sz, _vp]),
@@ -80,6 +94,7 @@ _SIGS = {
     "moe_ffn": (ctypes.c_int, [ctypes.POINTER(qg_moe), _vp, _i64, _i32, _vp, _i64, _vp, _vp,
                                _vp, _sz, _vp]),
     "qg_read_probe": (ctypes.c_int, [_vp, _sz, _vp, _vp]),
+    "qg_device_memory": (ctypes.c_int, [_i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     "qg_tune_gemv": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _i64, _i64, _vp, _i64, _i32, _vp, _i64,
                                     _vp, _sz, _vp, _i32, _vp]),
     "qg_tune_gateup": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _i32,
@@ -247,6 +262,29 @@ def qgemm16(w: QMatrix, X, Y=None, accumulate: bool = False):
     return Y
 
 
+def qgemm16_batch(items):
+    """One launch over several 16-column problems: items is a list of
+    (w: QMatrix, X [16, cols], Y [16, rows] or None, accumulate).  Each Y is
+    bitwise equal to qgemm16 on that problem.  Returns the list of Y."""
+    torch = _torch()
+    n = len(items)
+    arr = (qg_gemm16_problem * max(n, 1))()
+    outs = []
+    for i, (w, X, Y, acc) in enumerate(items):
+        _check_dev(X)
+        if X.shape[0] != 16:
+            raise ValueError("qgemm16_batch takes exactly 16 columns per problem")
+        if Y is None:
+            Y = torch.empty((16, w.rows), dtype=torch.float32, device=X.device)
+        outs.append(Y)
+        arr[i] = qg_gemm16_problem(w.qtype, int(acc), w.qs.data_ptr(), w.d.data_ptr(), w.rows, w.cols,
+                                   X.data_ptr(), _ld(X), Y.data_ptr(), _ld(Y))
+    dev = items[0][1].device if n else torch.device("cuda:0")
+    ws = workspace(lib.qg_gemm16_batch_ws_bytes(arr, n), dev)
+    _check(lib.qgemm16_batch(arr, n, ws.data_ptr(), ws.numel(), _stream(dev)), "qgemm16_batch")
+    return outs
+
+
 def gateup_silu(wg: QMatrix, wu: QMatrix, X, H=None):
     """H[j] = silu(Wg X[j]) * (Wu X[j]); X: [ncols, cols] (ncols 1..8)."""
     torch = _torch()
@@ -320,6 +358,12 @@ def read_probe(t, sink=None):
     _check(lib.qg_read_probe(t.data_ptr(), t.numel() * t.element_size(), sink.data_ptr(),
                              _stream(t.device)), "qg_read_probe")
     return sink
+
+def device_memory(device: int = 0):
+    """(memory clock in kHz, bus width in bits) as the HIP runtime reports them."""
+    c, w = _i32(), _i32()
+    _check(lib.qg_device_memory(device, ctypes.byref(c), ctypes.byref(w)), "qg_device_memory")
+    return c.value, w.value
 
 
 def lmhead_argmax(w: QMatrix, x, n_rows: Optional[int] = None, out_idx=None, out_val=None):

@@ -214,6 +214,43 @@ int qgemm16(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols
   return qmv_common(qtype, qs, d, rows, cols, X, ldx, 16, Y, ldy, accumulate, ws, ws_bytes, stream, true);
 }
 
+static int check_batch(const qg_gemm16_problem *p, int32_t n) {
+  if (!p) return QG_EINVAL;
+  if (n < 1 || n > QG_BATCH_MAX) return QG_ESHAPE;
+  for (int i = 0; i < n; ++i) {
+    if (!qtype_ok(p[i].qtype)) return QG_EINVAL;
+    int st = check_matrix(p[i].qs, p[i].d, p[i].rows, p[i].cols);
+    if (st) return st;
+    if ((st = check_act(p[i].X, p[i].ldx, p[i].cols, 16))) return st;
+    if ((st = check_out(p[i].Y, p[i].ldy, p[i].rows))) return st;
+  }
+  // the problems run concurrently: no output may overlap any input or
+  // another output
+  for (int i = 0; i < n; ++i) {
+    const Range yi = span(p[i].Y, p[i].ldy, p[i].rows, 16);
+    for (int j = 0; j < n; ++j) {
+      if (overlap(yi, span(p[j].X, p[j].ldx, p[j].cols, 16))) return QG_EINVAL;
+      if (j != i && overlap(yi, span(p[j].Y, p[j].ldy, p[j].rows, 16))) return QG_EINVAL;
+    }
+  }
+  return QG_OK;
+}
+
+size_t qg_gemm16_batch_ws_bytes(const qg_gemm16_problem *p, int32_t n) {
+  if (check_batch(p, n)) return 0;
+  return gemm16_batch_ws_bytes(p, n);
+}
+
+int qgemm16_batch(const qg_gemm16_problem *p, int32_t n, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_batch(p, n);
+  if (st) return st;
+  const size_t need = gemm16_batch_ws_bytes(p, n);
+  if (need == 0) return QG_EUNSUPPORTED;
+  if (!ws || ws_bytes < need) return QG_EWORKSPACE;
+  if (!aligned(ws, 256)) return QG_EALIGN;
+  return launch_gemm16_batch(p, n, ws, ws_bytes, (hipStream_t)stream);
+}
+
 static int gateup_common(int qtype, const void *g_qs, const void *g_d, const void *u_qs, const void *u_d,
                          int64_t rows, int64_t cols, const float *X, int64_t ldx, int32_t ncols,
                          const float *gamma, float eps, float *H, int64_t ldh, void *ws, size_t ws_bytes,
@@ -423,6 +460,20 @@ static int check_moe(const qg_moe *m, int32_t ntok) {
 size_t qg_moe_ws_bytes(const qg_moe *m, int32_t ntok) {
   if (check_moe(m, ntok) != QG_OK) return 0;
   return moe_ws_bytes(m, ntok);
+}
+
+int qg_device_memory(int32_t device, int32_t *clock_khz, int32_t *bus_bits) {
+  if (!clock_khz || !bus_bits) return QG_EINVAL;
+  int c = 0, w = 0;
+  hipError_t e = hipDeviceGetAttribute(&c, hipDeviceAttributeMemoryClockRate, device);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&w, hipDeviceAttributeMemoryBusWidth, device);
+  if (e != hipSuccess) {
+    record_hip_error(e);
+    return QG_EHIP;
+  }
+  *clock_khz = c;
+  *bus_bits = w;
+  return QG_OK;
 }
 
 int qg_read_probe(const void *p, size_t bytes, uint32_t *sink, void *stream) {

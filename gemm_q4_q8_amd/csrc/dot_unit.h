@@ -135,6 +135,13 @@ __device__ __forceinline__ void mfma_fence(float (&acc)[NI], const h8 (&A)[4], c
 }
 #undef QG_FENCE_IN
 
+// Half offset of 16-byte chunk q (0..3) of activation row g in LDS.  A row
+// is 32 halves (64 bytes); its chunks are stored in the order q ^ ((g >> 1)
+// & 3), so that the rows g .. g + 7 a group of 8 lanes reads at once (one
+// chunk each) cover all 128 bytes of banks instead of two 16-byte columns
+// of them (measured: 3.5 bank-conflict cycles per LDS instruction without).
+__device__ __forceinline__ size_t xrow(size_t g, int q) { return g * 32 + (size_t)((q ^ ((int)(g >> 1) & 3)) * 8); }
+
 // The largest of a value over the 16 lanes of a DPP row (all active): the
 // quad permutes [1,0,3,2] and [2,3,0,1], then the half-row mirror and the
 // row mirror (each step pairs lanes holding maxima of disjoint groups).
@@ -188,9 +195,10 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   // whole segment would take several L2 round trips before the first
   // product); narrow ones stage the whole segment up front, as hi / lo
   // pairs.
-  constexpr bool XS = NC >= 16;
-  static_assert(XS ? NC == 16 : (NC >= 1 && NC <= 8), "column count");
-  constexpr int XC = XS ? NC : 2 * NC;  // activation rows of a block in LDS: hi, then lo
+  constexpr bool F16 = NC >= 16;  // f16 operands (16 columns), else hi / lo pairs
+  constexpr bool XS = F16;         // activations streamed in chunks
+  static_assert(F16 ? NC == 16 : (NC >= 1 && NC <= 8), "column count");
+  constexpr int XC = F16 ? NC : 2 * NC;  // activation rows of a block in LDS: hi, then lo
   constexpr int LO = NC <= 4 ? 4 : 8;   // matrix-core row of the lo part of column 0
   // accumulators per lane: the 4 D values of lane (r, sl) are product rows
   // 4 sl + i
@@ -208,10 +216,10 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   // or (SW > 1) in-workgroup segment wsg of SW.  Interleaved segments: the
   // wave's segment q of nq takes tile columns q, q + nq, ... (wst = nq);
   // contiguous ones: its range [wkt0, wkt0 + wnkt) of the unit's columns.
-  const int SW = (!XS && a.SW > 1) ? a.SW : 1;
+  const int SW = (!F16 && a.SW > 1) ? a.SW : 1;
   const int R = (NTHR >> 6) / SW;
   const int wrt = wk % R, wsg = wk / R;
-  const bool IL = !XS && a.IL;
+  const bool IL = !F16 && a.IL;
   const int kt0 = IL ? 0 : seg_begin(s, a.KT, a.S);
   const int nkt = IL ? a.KT : seg_begin(s + 1, a.KT, a.S) - kt0;
   const int wq_i = SW > 1 ? wsg : s, wq_n = SW > 1 ? SW : a.S;  // this wave's segment of how many
@@ -246,11 +254,11 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   // column does not change from chunk to chunk, so streamed staging looks
   // it up once, not inside the weight stream (a map load there would make
   // every chunk wait for all weight loads in flight)
-  // Pieces (8 values) are numbered (block, column, quarter) when
-  // streaming 16 columns, and (tile column, column, block, quarter) when
-  // staging 1..8 columns: the 16 pieces of one tile column of one column
-  // are then the 16 lanes of one DPP row (the span is a multiple of 16).
-  auto p_col = [&](int v) -> int { return XS ? (v >> 2) % NC : (v >> 4) % NC; };
+  // Pieces (8 values) are numbered (block, column, quarter) for 16 columns,
+  // and (tile column, column, block, quarter) for 1..8 columns: the 16
+  // pieces of one tile column of one column are then the 16 lanes of one
+  // DPP row (the span is a multiple of 16).
+  auto p_col = [&](int v) -> int { return F16 ? (v >> 2) % NC : (v >> 4) % NC; };
   auto x_col = [&](int v) -> int64_t {
     const int c = p_col(v);
     return c < a.ncols && a.xmap ? a.xmap[c] : c;
@@ -260,9 +268,9 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   // its k, or -1 when it lies outside the span, the segment or the matrix
   auto x_k = [&](int v, int rel0, int span) -> int64_t {
     const int qq = v & 3, c = p_col(v);
-    const int bl = XS ? (v >> 2) / NC : ((v >> 4) / NC) * TILE_BLOCKS + ((v >> 2) & 3);  // block read
-    const int64_t gb = XS ? (int64_t)(kt0 + rel0) * TILE_BLOCKS + bl
-                          : (int64_t)ld_tile(bl >> 2) * TILE_BLOCKS + (bl & 3);
+    const int bl = F16 ? (v >> 2) / NC : ((v >> 4) / NC) * TILE_BLOCKS + ((v >> 2) & 3);  // block read
+    const int64_t gb = F16 ? (int64_t)(kt0 + rel0) * TILE_BLOCKS + bl
+                           : (int64_t)ld_tile(bl >> 2) * TILE_BLOCKS + (bl & 3);
     const int64_t k = gb * 32 + qq * 8;
     const bool ok = v < span && (!XS || rel0 * TILE_BLOCKS + bl < nkt * TILE_BLOCKS) && k < a.cols && c < a.ncols;
     return ok ? k : -1;
@@ -271,7 +279,7 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   // a piece outside reads zeros), and per piece read the sum of its 8
   // squares, [column][piece along K], past the staged activations and the
   // in-workgroup sums; then 1 / rms per column
-  static_assert(!RMSN || (!XS && EPI == EPI_SILU), "RMSNorm prologue: gate/up, staged whole");
+  static_assert(!RMSN || (!F16 && EPI == EPI_SILU), "RMSNorm prologue: gate/up, 1..8 columns");
   const __amdgpu_buffer_rsrc_t rg = buf_range(a.gamma, RMSN ? (uint32_t)(a.cols * 4) : 0u);
   const int npc = nlt * TILE_BLOCKS * 4;  // pieces of one column
   float *ssq = (float *)(smem + dot_stage_bytes(nst, NC) +
@@ -295,7 +303,7 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   // sees the whole tile column of its column.
   auto x_put = [&](int v, int span, _Float16 *dst, const XPiece &pc) {
     const int qq = v & 3, c = p_col(v);
-    const int bl = XS ? (v >> 2) / NC : ((v >> 4) / NC) * TILE_BLOCKS + ((v >> 2) & 3);
+    const int bl = F16 ? (v >> 2) / NC : ((v >> 4) / NC) * TILE_BLOCKS + ((v >> 2) & 3);
     float x[8];
     {
       const float4 lo = __builtin_bit_cast(float4, pc.lo), hi = __builtin_bit_cast(float4, pc.hi);
@@ -315,12 +323,12 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
         x[4 + e] *= ghi[e];
       }
     }
-    if constexpr (XS) {
+    if constexpr (F16) {
       if (v < span) {
         h8 hv;
 #pragma unroll
         for (int e = 0; e < 8; ++e) hv[e] = (_Float16)x[e];
-        *(h8 *)(dst + ((size_t)bl * XC + c) * 32 + qq * 8) = hv;
+        *(h8 *)(dst + xrow((size_t)bl * XC + c, qq)) = hv;
       }
     } else {
       float m = 0.0f;
@@ -334,8 +342,8 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
       const int st = st_tile(bl >> 2);
       if (v < span && st >= 0) {
         const int sb = st * TILE_BLOCKS + (bl & 3);
-        *(h8 *)(xs + ((size_t)sb * XC + c) * 32 + qq * 8) = H;
-        *(h8 *)(xs + ((size_t)sb * XC + NC + c) * 32 + qq * 8) = L;
+        *(h8 *)(xs + xrow((size_t)sb * XC + c, qq)) = H;
+        *(h8 *)(xs + xrow((size_t)sb * XC + NC + c, qq)) = L;
         if ((v & 15) == 0) scl[(size_t)st * SCC + c] = down;
       }
     }
@@ -409,8 +417,9 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   for (int i = 0; i < X0; ++i) x_put(tid + i * NTHR, span0, xs, xp[i]);
   if constexpr (!XS) {
     __builtin_amdgcn_s_waitcnt(WAIT_X0);
-    constexpr int XB = RMSN && QT == Q8 && NMAT == 2 ? 2 : 4;  // fewer registers where gate, up and gamma crowd them
-    for (int v0 = tid + NTHR; v0 < nvec; v0 += XB * NTHR) {
+    // pieces per batch (fewer registers where gate, up and gamma crowd them)
+    constexpr int XB = RMSN && QT == Q8 && NMAT == 2 ? 2 : 4;
+    for (int v0 = tid + X0 * NTHR; v0 < nvec; v0 += XB * NTHR) {
       XPiece pc[XB];
 #pragma unroll
       for (int b = 0; b < XB; ++b) x_ld(v0 + b * NTHR, 0, nvec, x_col(v0 + b * NTHR), pc[b]);
@@ -453,16 +462,16 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   // the LDS reads); narrower batches, whose streams are bound by memory,
   // keep one block at a time.
   h8 A[TILE_BLOCKS];
-  const int arow = XS ? r : (r < NC ? r : (r >= LO && r < LO + NC ? NC + r - LO : 0));
+  const int arow = F16 ? r : (r < NC ? r : (r >= LO && r < LO + NC ? NC + r - LO : 0));
   // 1..8 columns: the column of this lane's result i is cb + i (its hi or
   // its lo part); past NC it is unused, and reads a valid scale
   const int cb = (4 * sl) & (LO - 1);
   auto compute = [&](int slot, int rel) {
-    if constexpr (XS) {
+    if constexpr (F16) {
       // the slot of tile column rel in its chunk's buffer
       const int bl0 = ((((rel / PF) & 1) * PF) + rel % PF) * TILE_BLOCKS;
 #pragma unroll
-      for (int j = 0; j < TILE_BLOCKS; ++j) A[j] = *(const h8 *)(xs + ((size_t)(bl0 + j) * XC + r) * 32 + sl * 8);
+      for (int j = 0; j < TILE_BLOCKS; ++j) A[j] = *(const h8 *)(xs + xrow((size_t)(bl0 + j) * XC + r, sl));
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -494,7 +503,7 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
       float ts[NMAT][RT][NI];  // the tile's sums, block by block
 #pragma unroll
       for (int j = 0; j < TILE_BLOCKS; ++j) {
-        A[0] = *(const h8 *)(xs + ((size_t)(st * TILE_BLOCKS + j) * XC + arow) * 32 + sl * 8);
+        A[0] = *(const h8 *)(xs + xrow((size_t)(st * TILE_BLOCKS + j) * XC + arow, sl));
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -548,12 +557,14 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
     }
     // hi and lo sums of each column meet: lane (r, sl) of a hi row adds
     // lane (r, sl + LO / 4)
+    if constexpr (!F16) {
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
+      for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-      for (int t = 0; t < RT; ++t)
+        for (int t = 0; t < RT; ++t)
 #pragma unroll
-        for (int i = 0; i < NI; ++i) acc[m][t][i] += __shfl_down(acc[m][t][i], LO * 4);
+          for (int i = 0; i < NI; ++i) acc[m][t][i] += __shfl_down(acc[m][t][i], LO * 4);
+    }
   }
 
   // ---- 4. per-row sums: lane (r, sl) holds column 4 sl + i of row r (1..8

@@ -13,6 +13,8 @@
 // products on the matrix cores, segment reduction, epilogue); the argmax
 // across row groups is added here.  K segments per shape: gemv_segments()
 // (1..8 columns, the same for every column count) and gemm16_splits().
+#include <string.h>
+
 #include "common.h"
 #include "dot_unit.h"
 #include "internal.h"
@@ -207,6 +209,96 @@ __global__ void __launch_bounds__(WMAX * 64) dot_kernel(DotArgs a) {
       *a.out_idx = bi;
       if (a.out_val) *a.out_val = bv;
     }
+  }
+}
+
+// ----------------------------------------------- grouped 16-column problems
+// One launch over several 16-column problems (a prefill pass through several
+// matrices).  Each workgroup takes one work unit (row group of G16_W row
+// tiles, K segment) of one problem, with the problem's own K segments and
+// order, so every output is bitwise equal to the single-problem call.  The
+// workgroups are small, so several reside on each CU: while one stages its
+// activations, publishes its partial sums or waits for its first weights,
+// the others stream, and the units of the next problem start as soon as
+// CUs free up, without a launch boundary between problems.  The units are
+// those of the single-problem call with 8 waves (its activations stream in
+// chunks of G16_PF tile columns).  Measured alternatives at the prefill
+// pass (Q4_0 and Q8_0, 5120 -> 17408 and back, 75-77 us as built): the
+// whole K segment staged first and 4 tile columns in flight, the same;
+// 4-wave workgroups, 84 us; reducer workgroups at the end of the launch
+// summing the segments (no unit waiting for a counter), 93 us: every
+// workgroup of a launch holds the same LDS, so reducers waiting at the tail
+// took the slots of units still to run.
+constexpr int G16_W = 8;   // waves (row tiles) per workgroup
+constexpr int G16_PF = 2;  // tile columns in flight per wave
+
+struct G16Prob {
+  const uint8_t *qs, *d;
+  const float *X;
+  float *Y;
+  int64_t rows, cols, ldx, ldy;
+  float *part;
+  uint32_t *cnt;
+  int64_t u0;  // the problem's first unit in the launch
+  int NT, KT, S, G;
+  int qt, acc;
+};
+struct G16Args {
+  // first unit of each problem (ascending; past the last problem:
+  // INT64_MAX), read together to find a workgroup's problem
+  int64_t ustart[QG_BATCH_MAX];
+  G16Prob p[QG_BATCH_MAX];
+  int n;
+  int64_t units;
+};
+
+template <int W>
+__global__ void __launch_bounds__(W * 64) gemm16_batch_kernel(G16Args b) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ uint32_t flag;
+  // units in launch order, dealt round-robin to the XCDs (workgroup b runs
+  // on XCD b % 8): every XCD gets the same mix of problems, so the XCDs
+  // finish together (a contiguous range per XCD gave some XCDs twice the
+  // bytes of others)
+  const int64_t u = blockIdx.x;
+  if (u >= b.units) return;
+  // the problem holding unit u: its index from the first-unit numbers (one
+  // scalar load), then that one descriptor, read in place through a uniform
+  // index (a select over every descriptor made a chain of dependent scalar
+  // loads ahead of the first weight load)
+  int pi = 0;
+#pragma unroll
+  for (int j = 1; j < QG_BATCH_MAX; ++j) pi += u >= b.ustart[j] ? 1 : 0;
+  pi = __builtin_amdgcn_readfirstlane(pi);
+  const G16Prob &P = b.p[pi];
+  DotArgs a = {};
+  a.qs0 = a.qs1 = P.qs;
+  a.d0 = a.d1 = P.d;
+  a.rows = P.rows;
+  a.cols = P.cols;
+  a.NT = P.NT;
+  a.KT = P.KT;
+  a.S = P.S;
+  a.SW = 1;
+  a.IL = 0;
+  a.G = P.G;
+  a.X = P.X;
+  a.ldx = P.ldx;
+  a.ncols = 16;
+  a.Y = P.Y;
+  a.ldy = P.ldy;
+  a.part = P.part;
+  a.cnt = P.cnt;
+  const int64_t lu = u - P.u0;
+  const int g = (int)(lu / P.S), s = (int)(lu % P.S);
+  float bv = 0.0f;
+  int32_t bi = 0;
+  if (P.qt == Q4) {
+    if (P.acc) dot_unit<Q4, 16, 1, EPI_ACC, 1, G16_PF, W, PH_PLAIN>(a, g, s, smem, &flag, bv, bi);
+    else dot_unit<Q4, 16, 1, EPI_STORE, 1, G16_PF, W, PH_PLAIN>(a, g, s, smem, &flag, bv, bi);
+  } else {
+    if (P.acc) dot_unit<Q8, 16, 1, EPI_ACC, 1, G16_PF, W, PH_PLAIN>(a, g, s, smem, &flag, bv, bi);
+    else dot_unit<Q8, 16, 1, EPI_STORE, 1, G16_PF, W, PH_PLAIN>(a, g, s, smem, &flag, bv, bi);
   }
 }
 
@@ -548,6 +640,68 @@ static int dispatch_qt(const QmvCall &c) {
       return launch_dot<QT, 1, 1, EPI_TOPK>(c, seg(gemv_segments(c.rows, c.cols, 1, 1)));
   }
   return QG_EINVAL;
+}
+
+// Workspace of a grouped launch: the counters of every problem's row groups
+// in the shared counter words, then each problem's segment partials.  Fills
+// `b` when given (the pointers inside `ws`).
+static size_t gemm16_batch_layout(const qg_gemm16_problem *p, int n, G16Args *b, uint8_t *ws) {
+  size_t off = QG_WS_SYNC_BYTES, words = 0;
+  int64_t u0 = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t NT = cdiv(p[i].rows, 16), KT = cdiv(p[i].cols / 32, 4);
+    const int S = gemm16_splits(p[i].rows, p[i].cols);
+    const int64_t G = cdiv(NT, G16_W);
+    if (b) {
+      G16Prob &q = b->p[i];
+      q.qs = (const uint8_t *)p[i].qs;
+      q.d = (const uint8_t *)p[i].d;
+      q.X = p[i].X;
+      q.Y = p[i].Y;
+      q.rows = p[i].rows;
+      q.cols = p[i].cols;
+      q.ldx = p[i].ldx;
+      q.ldy = p[i].ldy;
+      q.part = (float *)(ws + off);
+      q.cnt = (uint32_t *)ws + words;
+      q.u0 = u0;
+      q.NT = (int)NT;
+      q.KT = (int)KT;
+      q.S = S;
+      q.G = (int)G;
+      q.qt = p[i].qtype == QG_Q4_0 ? Q4 : Q8;
+      q.acc = p[i].accumulate ? 1 : 0;
+    }
+    words += (size_t)G;
+    if (S > 1) off += align256((size_t)S * NT * dot_part_floats(16) * 4);
+    u0 += G * S;
+  }
+  if (b) {
+    b->n = n;
+    b->units = u0;
+    for (int i = 0; i < QG_BATCH_MAX; ++i) b->ustart[i] = i < n ? b->p[i].u0 : INT64_MAX;
+  }
+  return words > WS_SYNC_WORDS ? 0 : off;
+}
+
+size_t gemm16_batch_ws_bytes(const qg_gemm16_problem *p, int n) { return gemm16_batch_layout(p, n, nullptr, nullptr); }
+
+int launch_gemm16_batch(const qg_gemm16_problem *p, int n, void *ws, size_t ws_bytes, hipStream_t stream) {
+  G16Args b;
+  memset(&b, 0, sizeof(b));
+  const size_t need = gemm16_batch_layout(p, n, &b, (uint8_t *)ws);
+  if (need == 0) return QG_EUNSUPPORTED;
+  if (need > ws_bytes) return QG_EWORKSPACE;
+  for (int i = 0; i < n; ++i) {
+    const G16Prob &q = b.p[i];
+    const int64_t xb = (15 * q.ldx + q.cols) * 4, tb = q.qt == Q4 ? 1024 : 2048;
+    if (xb >= ((int64_t)1 << 31) || (int64_t)q.KT * tb >= ((int64_t)1 << 31)) return QG_EUNSUPPORTED;
+    if ((size_t)q.S * q.NT * dot_part_floats(16) * 4 >= ((size_t)1 << 31)) return QG_EUNSUPPORTED;
+  }
+  const size_t lds = dot_stage_bytes(2 * G16_PF, 16);  // two chunks
+  clear_hip_error();
+  hipLaunchKernelGGL(gemm16_batch_kernel<G16_W>, dim3((unsigned)b.units), dim3(G16_W * 64), lds, stream, b);
+  return launch_status();
 }
 
 int builtin_split(const QmvCall &c) {

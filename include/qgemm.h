@@ -28,11 +28,17 @@
  *     X (and x) must be 16-byte aligned with ldx a multiple of 4 (columns are
  *     read as whole 16-byte vectors); Y and H need 4-byte alignment only;
  *     ldx >= cols, ldy >= rows.
- *   - Arithmetic: weights are dequantised exactly in registers; activations
- *     enter the products rounded to f16 (round to nearest even, relative
- *     error <= 2^-11); every sum and the scale multiply are f32.  Nothing is
- *     accumulated in f16.  Results are bitwise reproducible run to run: all
- *     reductions (split-K included) have a fixed order per shape.
+ *   - Arithmetic: weights are dequantised exactly in registers; every sum and
+ *     every scale multiply is f32, nothing is accumulated in f16 [ENG
+ *     Correctness and portability].  Activations are f32 and keep f32 range:
+ *     products of 1..8 columns (GEMV, gate/up, LM head, MoE experts) carry
+ *     each activation as an exact pair of f16 values under a power of two
+ *     chosen per 128 values of a column (relative error <= 2^-22, any finite
+ *     f32 magnitude).  Only the 16-column prefill GEMM rounds its activation
+ *     operands to f16 (round to nearest even, relative error <= 2^-11, so
+ *     |x| must stay below 65504 there).  Results are bitwise reproducible
+ *     run to run: all reductions (split-K included) have a fixed order per
+ *     shape.
  *   - Pointers named qs, d, X, Y, H, x, out_*, ws, blocks are DEVICE
  *     pointers; `stream` is a hipStream_t passed as void* (NULL = the null
  *     stream).  Calls are asynchronous on that stream; a device fault shows
@@ -97,6 +103,13 @@ const char *qg_last_hip_error(void);
  * device uint32 the kernel may write (almost never does).  Asynchronous on
  * `stream`.  Errors: QG_EINVAL (null), QG_EALIGN, QG_ESHAPE, QG_EHIP. */
 int qg_read_probe(const void *p, size_t bytes, uint32_t *sink, void *stream);
+
+/* Measurement aid: the memory clock (kHz) and bus width (bits) the HIP
+ * runtime reports for `device`, from which a peak HBM rate follows (two
+ * transfers per clock: 2 * clock * width / 8 bytes per second), to cross-
+ * check a published peak.  Host only.  Errors: QG_EINVAL (null pointer),
+ * QG_EHIP (no such device). */
+int qg_device_memory(int32_t device, int32_t *clock_khz, int32_t *bus_bits);
 
 /* ------------------------------------------------------------------------
  * Load-time repack  [ARCH Memory and caching; ENG Reading weights]
@@ -167,6 +180,38 @@ size_t qg_gemm16_ws_bytes(int qtype, int64_t rows, int64_t cols);
 int qgemm16(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols,
             const float *X, int64_t ldx, float *Y, int64_t ldy, int32_t accumulate,
             void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * A prefill pass over several matrices in one launch  [ARCH Prefill: the
+ * prompt runs 16 columns per pass through every weight matrix; ENG Batching
+ * and prefill: the 16-column GEMM; ENG Fewer passes: fewer launches]
+ *
+ *   for each problem i < n:  Y_i = (accumulate_i ? Y_i : 0) + W_i X_i,
+ *   X_i cols_i x 16, Y_i rows_i x 16, each as qgemm16 (same checks).
+ * Each Y_i is bitwise equal to qgemm16 on problem i (same K segments, same
+ * order).  The problems run concurrently in one launch, so no Y_i may
+ * overlap any X_j or any other Y_j (QG_EINVAL).  1 <= n <= QG_BATCH_MAX
+ * (else QG_ESHAPE); Q4_0 and Q8_0 problems may be mixed.  `p` is a HOST
+ * array of n descriptors; the library copies it into the launch.
+ * ------------------------------------------------------------------------ */
+#define QG_BATCH_MAX 8
+
+typedef struct {
+  int32_t qtype;       /* QG_Q4_0 or QG_Q8_0 */
+  int32_t accumulate;  /* 0: Y = W X;  1: Y += W X */
+  const void *qs;      /* packed weights of one matrix (qg_repack, n_mat = 1) */
+  const void *d;
+  int64_t rows, cols;
+  const float *X;      /* cols x 16, column-major, leading dimension ldx */
+  int64_t ldx;
+  float *Y;            /* rows x 16, column-major, leading dimension ldy */
+  int64_t ldy;
+} qg_gemm16_problem;
+
+size_t qg_gemm16_batch_ws_bytes(const qg_gemm16_problem *p, int32_t n);
+
+int qgemm16_batch(const qg_gemm16_problem *p, int32_t n, void *ws, size_t ws_bytes,
+                  void *stream);
 
 /* ------------------------------------------------------------------------
  * Fused gate/up + SiLU  [ENG Kernel families: fused gate/up, both FFN

@@ -107,6 +107,44 @@ def test_gemv_argument_checks():
     assert _gemv(Y=FAKE + (1 << 20) + 64) == EINVAL
 
 
+def test_gemm16_batch_checks():
+    P = qg.qg_gemm16_problem
+    X0, Y0, X1, Y1 = (FAKE + (k << 24) for k in (1, 2, 3, 4))
+
+    def arr(*probs):
+        a = (P * max(len(probs), 1))()
+        for i, p in enumerate(probs):
+            a[i] = p
+        return a
+
+    good = [P(2, 0, FAKE, FAKE, 64, 128, X0, 128, Y0, 64), P(8, 1, FAKE, FAKE, 100, 256, X1, 256, Y1, 100)]
+    a = arr(*good)
+    wsb = L.qg_gemm16_batch_ws_bytes(a, 2)
+    assert wsb >= 262144
+    ws = FAKE + (7 << 24)
+    # sizes grow with the problems, and one problem of the pair needs less
+    assert L.qg_gemm16_batch_ws_bytes(a, 1) <= wsb
+    assert L.qgemm16_batch(None, 2, ws, wsb, None) == EINVAL
+    assert L.qgemm16_batch(a, 0, ws, wsb, None) == ESHAPE
+    assert L.qgemm16_batch(arr(*(good * 5)), 9, ws, 1 << 30, None) == ESHAPE
+    assert L.qg_gemm16_batch_ws_bytes(a, 0) == 0
+    bad = list(good); bad[1] = P(5, 0, FAKE, FAKE, 100, 256, X1, 256, Y1, 100)
+    assert L.qgemm16_batch(arr(*bad), 2, ws, wsb, None) == EINVAL      # type id
+    bad[1] = P(8, 0, FAKE, FAKE, 100, 250, X1, 256, Y1, 100)
+    assert L.qgemm16_batch(arr(*bad), 2, ws, wsb, None) == ESHAPE      # cols % 32
+    bad[1] = P(8, 0, FAKE, FAKE, 100, 256, X1 + 4, 256, Y1, 100)
+    assert L.qgemm16_batch(arr(*bad), 2, ws, wsb, None) == EALIGN      # X not 16-byte aligned
+    bad[1] = P(8, 0, FAKE, FAKE, 100, 256, X1, 256, X0 + 64, 100)
+    assert L.qgemm16_batch(arr(*bad), 2, ws, wsb, None) == EINVAL      # Y_1 overlaps X_0
+    bad[1] = P(8, 0, FAKE, FAKE, 100, 256, X1, 256, Y0 + 400, 100)
+    assert L.qgemm16_batch(arr(*bad), 2, ws, wsb, None) == EINVAL      # Y_1 overlaps Y_0
+    bad[1] = P(8, 0, FAKE, FAKE, 100, 256, X1, 256, X1 + 64, 100)
+    assert L.qgemm16_batch(arr(*bad), 2, ws, wsb, None) == EINVAL      # Y_1 overlaps its own X
+    assert L.qgemm16_batch(a, 2, ws, wsb - 1, None) == EWS
+    assert L.qgemm16_batch(a, 2, None, wsb, None) == EWS
+    assert L.qgemm16_batch(a, 2, ws + 16, wsb, None) == EALIGN
+
+
 def test_gemm16_and_gateup_checks():
     ws = FAKE + (3 << 20)
     X, Y = FAKE + (1 << 20), FAKE + (2 << 20)

@@ -84,6 +84,30 @@ def test_prefill_gemm16(env, qtype, N, K):
     assert_tol(host(Y).T, ref, ops.tol_dot(a), "gemm16")
 
 
+def test_prefill_pass_batch(env):
+    """One prefill pass of the 16-column workload as one launch: Q4_0 and
+    Q8_0 at 5120 -> 17408 and 17408 -> 5120, each output bitwise equal to its
+    qgemm16 call, and rows sampled across every row tile group checked
+    against the oracle."""
+    torch, qg, dev = env
+    probs, raws = [], []
+    for i, (qt, N, K) in enumerate([(Q4, 17408, 5120), (Q4, 5120, 17408), (Q8, 17408, 5120), (Q8, 5120, 17408)]):
+        raw, W = matrix(env, qt, N, K, 45 + i)
+        X = synth.gen_x(K, 16, cfg_id=synth.CFG_PREFILL, col0=16 * i)
+        probs.append((W, up(env, X.T), None, 0))
+        raws.append((qt, raw, X))
+    say("prefill pass: 4 matrices in one launch")
+    outs = qg.qgemm16_batch(probs)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(46)
+    for i, (W, X, _, _) in enumerate(probs):
+        assert torch.equal(outs[i], qg.qgemm16(W, X)), i
+        qt, raw, Xh = raws[i]
+        rows = np.unique(np.concatenate([g.integers(0, W.rows, 600), [0, W.rows - 1]]))
+        ref, a = ops.gemv(qt, raw, Xh, rows=rows)
+        assert_tol(host(outs[i])[:, rows].T, ref, ops.tol_dot(a), f"pass problem {i}")
+
+
 def test_lmhead_argmax_full_vocabulary(env):
     torch, qg, dev = env
     N, K = 248320, 5120

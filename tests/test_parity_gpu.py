@@ -283,6 +283,37 @@ def test_gemm16_parity(env, qtype, rows, cols, acc):
     assert_tol(host(Yd).T, ref, ops.tol_dot(a, ref), "gemm16")
 
 
+# --------------------------------------------- 16 columns, several problems
+BATCH = [(Q4, 40, 416, 0), (Q8, 200, 2080, 1), (Q4, 600, 11264, 1), (Q8, 64, 4096, 0),
+         (Q4, 16, 128, 1), (Q8, 2100, 2048, 0), (Q4, 5120, 512, 0), (Q8, 40, 416, 1)]
+
+
+@pytest.mark.parametrize("n", [1, 3, 8])
+def test_gemm16_batch(env, n):
+    """Several 16-column problems (Q4_0 and Q8_0 mixed, storing and
+    accumulating, one to eight of them) in one launch: each output against
+    the oracle, bitwise equal to qgemm16 on that problem, and bitwise equal
+    again on a repeat launch."""
+    torch, qg, dev = env
+    say(f"gemm16 batch n={n}")
+    probs, refs = [], []
+    for i, (qt, rows, cols, acc) in enumerate(BATCH[:n]):
+        raw, W = make(env, qt, rows, cols, seed=700 + i)
+        X = synth.gen_x(cols, 16, cfg_id=701 + i)
+        y0 = synth.rng(702, i).standard_normal((rows, 16)).astype(np.float32)
+        probs.append((W, up(env, X.T), up(env, y0.T) if acc else None, acc))
+        refs.append((raw, X, y0))
+    single = [qg.qgemm16(W, X, None if Y is None else Y.clone(), accumulate=bool(acc)) for W, X, Y, acc in probs]
+    outs = qg.qgemm16_batch([(W, X, None if Y is None else Y.clone(), acc) for W, X, Y, acc in probs])
+    again = qg.qgemm16_batch([(W, X, None if Y is None else Y.clone(), acc) for W, X, Y, acc in probs])
+    torch.cuda.synchronize()
+    for i, ((qt, rows, cols, acc), (raw, X, y0)) in enumerate(zip(BATCH[:n], refs)):
+        ref, a = ops.gemv(qt, raw, X, y_in=y0 if acc else None)
+        assert_tol(host(outs[i]).T, ref, ops.tol_dot(a, ref), f"batch problem {i}")
+        assert torch.equal(outs[i], single[i]), i
+        assert torch.equal(again[i], outs[i]), i
+
+
 # ----------------------------------------------------------------- gate/up
 @pytest.mark.parametrize("qtype", [Q4, Q8])
 @pytest.mark.parametrize("rows,cols", [(40, 416), (64, 4096), (512, 2048)])
