@@ -88,6 +88,7 @@ _SIGS = {
     "qg_lmhead_topk_ws_bytes": (_sz, [_i64, _i64, _i32]),
     "lmhead_topk": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp,
                                    _vp, _sz, _vp]),
+    "lmhead_argmax_noalloc": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     "lmhead_argmax": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp,
                                      _vp, _sz, _vp]),
     "qg_moe_ws_bytes": (_sz, [ctypes.POINTER(qg_moe), _i32]),

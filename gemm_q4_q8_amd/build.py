@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libqgemm.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["repack.hip", "qmv.hip", "moe.hip", "probe.hip", "norm.hip", "requant.hip", "api.cpp", "tune.cpp"]
+SOURCES = ["repack.hip", "qmv.hip", "moe.hip", "noalloc.hip", "probe.hip", "norm.hip", "requant.hip", "api.cpp", "tune.cpp"]
 ARCH = "gfx950"
 
 

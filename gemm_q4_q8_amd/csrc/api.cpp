@@ -367,6 +367,29 @@ int lmhead_argmax(int qtype, const void *qs, const void *d, int64_t rows, int64_
                               false, 0, nullptr);
 }
 
+int lmhead_argmax_noalloc(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols, int64_t n_rows,
+                          const float *x, int32_t *out_idx, float *out_val, void *stream) {
+  // the checks lmhead_argmax makes before its workspace, so that a bad call
+  // touches nothing
+  if (!qtype_ok(qtype)) return QG_EINVAL;
+  int st = check_matrix(qs, d, rows, cols);
+  if (st) return st;
+  if (n_rows < 1 || n_rows > rows) return QG_ESHAPE;
+  if ((st = check_act(x, cols, cols, 1))) return st;
+  if (!out_idx) return QG_EINVAL;
+  if (!aligned(out_idx, 4) || (out_val && !aligned(out_val, 4))) return QG_EALIGN;
+  if (lmhead_ws_min(rows, cols, 0) > QG_NOALLOC_SCRATCH_BYTES) return QG_EUNSUPPORTED;
+  void *ws = nullptr;
+  if ((st = noalloc_scratch(&ws))) return st;
+  // the counters the head uses (word 0 and one per row group) start at zero
+  const int64_t words = (n_rows + 15) / 16 + 1;
+  if ((st = launch_clear_words(ws, (int)(words < (int64_t)WS_SYNC_WORDS ? words : (int64_t)WS_SYNC_WORDS),
+                               (hipStream_t)stream)))
+    return st;
+  return lmhead_argmax_common(qtype, qs, d, rows, cols, n_rows, x, out_idx, out_val, ws, QG_NOALLOC_SCRATCH_BYTES,
+                              stream, false, 0, nullptr);
+}
+
 int qg_tune_lmhead(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols, int64_t n_rows,
                    const float *x, int32_t *out_idx, float *out_val, void *ws, size_t ws_bytes, void *stream,
                    int32_t flags, int32_t *plan) {

@@ -82,6 +82,11 @@ int launch_rmsnorm(const float *X, int64_t ldx, int64_t cols, int ncols, const f
                    int64_t ldy, void *stream);
 int launch_read_probe(const void *p, size_t bytes, uint32_t *sink, void *stream);
 
+// The current device's library-owned scratch (its address, looked up once
+// per device), and a graph-safe zero fill of n words.
+int noalloc_scratch(void **out);
+int launch_clear_words(void *p, int n, hipStream_t stream);
+
 struct MoeCall {
   const qg_moe *m;
   const float *X;

@@ -69,6 +69,9 @@ extern "C" {
 /* Bytes of counters at the start of every workspace (see Conventions). */
 #define QG_WS_SYNC_BYTES 262144u
 
+/* Bytes of the library-owned scratch of lmhead_argmax_noalloc (per GPU). */
+#define QG_NOALLOC_SCRATCH_BYTES (2u << 20)
+
 /* Largest k of lmhead_topk. */
 #define QG_TOPK_MAX 16
 
@@ -286,6 +289,23 @@ size_t qg_lmhead_ws_bytes(int64_t rows, int64_t cols);
 int lmhead_argmax(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols,
                   int64_t n_rows, const float *x, int32_t *out_idx, float *out_val,
                   void *ws, size_t ws_bytes, void *stream);
+
+/* lmhead_argmax for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops or harnesses that forbid hipMalloc): the
+ * same computation and the same result bits, with the workspace replaced
+ * by a library-owned device array of QG_NOALLOC_SCRATCH_BYTES (2 MiB) per
+ * GPU, held until the process ends.  No allocation happens in the call.
+ * Each call first clears the array's counter words with a small kernel on
+ * `stream` (graph-safe), then runs the head.  Every call on one GPU uses
+ * that GPU's array: calls that may overlap in time on one GPU (different
+ * streams, or threads) race and must not be issued.  Shapes whose built-in
+ * launch needs more scratch than QG_NOALLOC_SCRATCH_BYTES (none up to
+ * about three million rows) return QG_EUNSUPPORTED before anything is
+ * launched; other errors as lmhead_argmax (QG_EHIP also if the array's
+ * address cannot be obtained). */
+int lmhead_argmax_noalloc(int qtype, const void *qs, const void *d, int64_t rows,
+                          int64_t cols, int64_t n_rows, const float *x, int32_t *out_idx,
+                          float *out_val, void *stream);
 
 /* ------------------------------------------------------------------------
  * LM head + top-k candidates  [ARCH One token, end to end: greedy and top-k

@@ -145,6 +145,19 @@ def test_gemm16_batch_checks():
     assert L.qgemm16_batch(a, 2, ws + 16, wsb, None) == EALIGN
 
 
+def test_lmhead_noalloc_checks():
+    x, oi = FAKE + (1 << 20), FAKE + (2 << 20)
+    f = L.lmhead_argmax_noalloc
+    assert f(5, FAKE, FAKE, 64, 128, 64, x, oi, None, None) == EINVAL
+    assert f(2, FAKE, FAKE, 64, 100, 64, x, oi, None, None) == ESHAPE
+    assert f(2, FAKE, FAKE, 64, 128, 65, x, oi, None, None) == ESHAPE
+    assert f(2, FAKE, FAKE, 64, 128, 64, x + 4, oi, None, None) == EALIGN
+    assert f(2, FAKE, FAKE, 64, 128, 64, x, None, None, None) == EINVAL
+    # a head whose launch needs more than the 2 MiB scratch is refused before
+    # anything runs (50,000,000 rows: 12.5 MB of row-group candidates)
+    assert f(2, FAKE, FAKE, 50_000_000, 128, 50_000_000, x, oi, None, None) == EUNSUP
+
+
 def test_gemm16_and_gateup_checks():
     ws = FAKE + (3 << 20)
     X, Y = FAKE + (1 << 20), FAKE + (2 << 20)
