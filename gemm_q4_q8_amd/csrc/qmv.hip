@@ -507,7 +507,10 @@ static int dot_waves(int64_t NTu, int S) {
 template <int QT, int NC, int NMAT, int EPI, bool RMSN = false>
 static int launch_dot(const QmvCall &c, int S) {
   constexpr int QW = QT == Q4 ? 1 : 2;
-  constexpr int PF0 = 4 / (NMAT * QW);
+  // the LM head (a gigabyte-scale stream) keeps 8 KiB of weights in flight
+  // per wave: a streaming read at this size gains from deeper queues
+  constexpr bool HEAD = EPI == EPI_ARGMAX || EPI == EPI_TOPK;
+  constexpr int PF0 = (HEAD ? 8 : 4) / (NMAT * QW);
   constexpr int PF = PF0 < 2 ? 2 : PF0;
   const int64_t NTu = cdiv(c.n_rows, 16);
   const int W = dot_waves(NTu, S);
