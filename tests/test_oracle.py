@@ -377,6 +377,108 @@ def test_requant_rounding_rules():
     assert np.array_equal(wn, -w) and np.array_equal(dn, d)
 
 
+@pytest.mark.parametrize("name,src", [("q4_k_block.txt", 12), ("q5_k_block.txt", 13), ("q6_k_block.txt", 14)])
+def test_kquant_decoding_golden(name, src):
+    """Hand-worked K-quant super-blocks (values worked out in the fixture
+    comments from the public GGUF layouts)."""
+    from oracle import requant as rq
+    raw, g = _block(name)
+    assert raw.size == rq.SRC_BLOCK_BYTES[src]
+    v = rq.decode_values_f32(src, raw[None, :])[0]
+    assert v.shape == (256,) and v.dtype == np.float32
+    keys = [k for k in g if k.startswith("v")]
+    assert len(keys) >= 10
+    for k in keys:
+        assert v[int(k[1:])] == float(g[k]), (name, k, v[int(k[1:])], g[k])
+    out = rq.requant_q8_0(src, np.stack([raw, raw]))
+    assert out.shape == (16, 34)
+
+
+def _pack_k_scales(sc, m):
+    """12 scale bytes from 6-bit scales and mins, the packing direction:
+    sub-blocks 0..3 fill the low 6 bits of bytes 0..3 (scales) and 4..7
+    (mins); sub-blocks 4..7 put scale | min << 4 (low nibbles) in bytes
+    8..11 and their top two bits in the top bits of bytes 0..3 (scales) and
+    4..7 (mins)."""
+    b = np.zeros(sc.shape[:-1] + (12,), np.int64)
+    for j in range(4):
+        b[..., j] = sc[..., j] | ((sc[..., j + 4] >> 4) << 6)
+        b[..., j + 4] = m[..., j] | ((m[..., j + 4] >> 4) << 6)
+        b[..., j + 8] = (sc[..., j + 4] & 15) | ((m[..., j + 4] & 15) << 4)
+    return b.astype(np.uint8)
+
+
+def test_kquant_scale_packing_round_trip():
+    from oracle import requant as rq
+    g = np.random.default_rng(41)
+    sc, m = g.integers(0, 64, (2000, 8)), g.integers(0, 64, (2000, 8))
+    got_sc, got_m = rq.k_scales_mins(_pack_k_scales(sc, m))
+    assert np.array_equal(got_sc, sc) and np.array_equal(got_m, m)
+    # every byte value is a legal packing: decoding covers 0..63 and re-packs
+    s12 = g.integers(0, 256, (2000, 12)).astype(np.uint8)
+    a, b = rq.k_scales_mins(s12)
+    assert a.min() >= 0 and a.max() <= 63 and b.min() >= 0 and b.max() <= 63
+    assert np.array_equal(_pack_k_scales(a, b), s12)
+
+
+def _f16b(x):
+    return np.asarray(x, np.float16).view(np.uint8).reshape(-1, 2)
+
+
+def test_kquant_sub_blocks_are_legacy_blocks():
+    """Special cases that reduce to the (separately pinned) 32-value
+    formats.  A Q4_K / Q5_K sub-block whose d * sc and dmin * m are exact in
+    f16 is the Q4_1 / Q5_1 block with scale d * sc, offset -dmin * m and the
+    same weights (both formats round the one difference of exact terms); a
+    Q6_K run of 32 whose two 16-value scales agree is the Q8_0 block with
+    scale d * sc and weights w - 32."""
+    from oracle import requant as rq
+    g = np.random.default_rng(43)
+    nb = 96
+    for src, legacy, wbits in ((rq.Q4_K, rq.Q4_1, 4), (rq.Q5_K, rq.Q5_1, 5)):
+        sc, m = g.integers(0, 64, (nb, 8)), g.integers(0, 64, (nb, 8))
+        d, dmin = 2.0 ** g.integers(-10, 2, nb), 2.0 ** g.integers(-10, 2, nb)
+        w = g.integers(0, 1 << wbits, (nb, 8, 32))
+        raw = np.zeros((nb, rq.SRC_BLOCK_BYTES[src]), np.uint8)
+        raw[:, 0:2], raw[:, 2:4], raw[:, 4:16] = _f16b(d), _f16b(dmin), _pack_k_scales(sc, m)
+        lo = w & 15
+        qs = (lo[:, 0::2, :] | (lo[:, 1::2, :] << 4)).reshape(nb, 128)   # byte 32 c + i
+        if src == rq.Q4_K:
+            raw[:, 16:144] = qs
+        else:
+            raw[:, 16:48] = sum(((w[:, j, :] >> 4) & 1) << j for j in range(8))
+            raw[:, 48:176] = qs
+        leg = np.zeros((nb, 8, rq.SRC_BLOCK_BYTES[legacy]), np.uint8)
+        leg[..., 0:2] = _f16b((d[:, None] * sc).reshape(-1)).reshape(nb, 8, 2)
+        leg[..., 2:4] = _f16b((-dmin[:, None] * m).reshape(-1)).reshape(nb, 8, 2)
+        nib = (w[..., :16] & 15) | ((w[..., 16:] & 15) << 4)
+        if legacy == rq.Q4_1:
+            leg[..., 4:20] = nib
+        else:
+            hb = sum(((w[..., i] >> 4) & 1) << i for i in range(32)).astype("<u4")
+            leg[..., 4:8] = hb[..., None].view(np.uint8)
+            leg[..., 8:24] = nib
+        want = rq.decode_values_f32(legacy, leg.reshape(nb * 8, -1))
+        got = rq.decode_values_f32(src, raw).reshape(nb * 8, 32)
+        assert np.array_equal(got, want), src
+    # Q6_K: scales equal in pairs
+    sc = np.repeat(g.integers(-128, 128, (nb, 8)), 2, axis=1)
+    d = 2.0 ** g.integers(-12, -2, nb)
+    w = g.integers(0, 64, (nb, 256))
+    raw = np.zeros((nb, 210), np.uint8)
+    h = w.reshape(nb, 2, 4, 32)                       # [half, quarter, lane]
+    raw[:, 0:128] = ((h[:, :, 0:2, :] & 15) | ((h[:, :, 2:4, :] & 15) << 4)).reshape(nb, 128)
+    raw[:, 128:192] = sum(((h[:, :, k, :] >> 4) & 3) << (2 * k) for k in range(4)).reshape(nb, 64)
+    raw[:, 192:208] = sc.astype(np.int8).view(np.uint8)
+    raw[:, 208:210] = _f16b(d)
+    q8 = np.zeros((nb, 8, 34), np.uint8)
+    q8[..., 0:2] = _f16b((d[:, None] * sc[:, 0::2]).reshape(-1)).reshape(nb, 8, 2)
+    q8[..., 2:34] = (w - 32).astype(np.int8).view(np.uint8).reshape(nb, 8, 32)
+    wq, dq = quant.decode_blocks(Q8, q8.reshape(-1, 34))
+    got = rq.decode_values_f32(rq.Q6_K, raw).reshape(nb * 8, 32).astype(np.float64)
+    assert np.array_equal(got, wq * dq[:, None])
+
+
 def test_softmax_properties():
     g = np.random.default_rng(14)
     v = g.standard_normal(8)
