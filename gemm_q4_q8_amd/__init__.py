@@ -304,15 +304,20 @@ def gateup_silu(wg: QMatrix, wu: QMatrix, X, H=None):
 
 
 Q4_1, Q5_0, Q5_1 = 3, 6, 7
+Q4_K, Q5_K, Q6_K = 12, 13, 14
+_REQUANT_RUNS = {Q4_1: 1, Q5_0: 1, Q5_1: 1, Q4_K: 8, Q5_K: 8, Q6_K: 8}
 
 
 def requant_q8_0(src_type: int, blocks, n_blocks: int, out=None):
-    """Q4_1 / Q5_0 / Q5_1 blocks (device uint8) -> canonical Q8_0 blocks
-    (device uint8, n_blocks * 34 bytes), on the GPU."""
+    """Q4_1 / Q5_0 / Q5_1 / Q4_K / Q5_K / Q6_K blocks (device uint8) ->
+    canonical Q8_0 blocks (device uint8, 34 bytes per 32 values: n_blocks *
+    34 bytes, or n_blocks * 8 * 34 for the 256-value K-quant blocks), on the
+    GPU."""
     torch = _torch()
     _check_dev(blocks)
     if out is None:
-        out = torch.empty(n_blocks * 34, dtype=torch.uint8, device=blocks.device)
+        n_out = n_blocks * _REQUANT_RUNS.get(src_type, 1)
+        out = torch.empty(n_out * 34, dtype=torch.uint8, device=blocks.device)
     _check(lib.qg_requant_q8_0(src_type, n_blocks, blocks.data_ptr(), out.data_ptr(), _stream(blocks.device)),
            "qg_requant_q8_0")
     return out

@@ -137,18 +137,21 @@ int qg_repack(int qtype, int64_t n_mat, int64_t rows, int64_t cols, const void *
 }
 
 int qg_requant_q8_0(int src_type, int64_t n_blocks, const void *src, void *dst, void *stream) {
-  int bs;
+  int bs, runs = 1;
   switch (src_type) {
     case QG_Q4_1: bs = 20; break;
     case QG_Q5_0: bs = 22; break;
     case QG_Q5_1: bs = 24; break;
+    case QG_Q4_K: bs = 144; runs = 8; break;
+    case QG_Q5_K: bs = 176; runs = 8; break;
+    case QG_Q6_K: bs = 210; runs = 8; break;
     default: return QG_EINVAL;
   }
-  if (n_blocks < 1 || n_blocks > ((int64_t)1 << 40)) return QG_ESHAPE;
+  if (n_blocks < 1 || n_blocks > ((int64_t)1 << 36) / runs) return QG_ESHAPE;
   if (!src || !dst) return QG_EINVAL;
   if (!aligned(src, 2) || !aligned(dst, 2)) return QG_EALIGN;
   const Range in{(uintptr_t)src, (uintptr_t)src + (uintptr_t)(n_blocks * bs)};
-  const Range out{(uintptr_t)dst, (uintptr_t)dst + (uintptr_t)(n_blocks * 34)};
+  const Range out{(uintptr_t)dst, (uintptr_t)dst + (uintptr_t)(n_blocks * runs * 34)};
   if (overlap(in, out)) return QG_EINVAL;
   return launch_requant_q8_0(src_type, n_blocks, src, dst, stream);
 }

@@ -78,7 +78,7 @@ extern "C" {
 /* GGUF tensor type ids, so a GGUF reader can pass them through. */
 enum { QG_Q4_0 = 2, QG_Q8_0 = 8 };
 /* Source block types qg_requant_q8_0 converts (GGUF type ids). */
-enum { QG_Q4_1 = 3, QG_Q5_0 = 6, QG_Q5_1 = 7 };
+enum { QG_Q4_1 = 3, QG_Q5_0 = 6, QG_Q5_1 = 7, QG_Q4_K = 12, QG_Q5_K = 13, QG_Q6_K = 14 };
 
 enum {
   QG_OK = 0,
@@ -235,15 +235,27 @@ int gateup_silu(int qtype, const void *g_qs, const void *g_d, const void *u_qs,
  * K-quant tensors of the public MoE file are requantized to Q8_0 on the way
  * to the GPU; ARCH where the weights live: converted once and kept]
  *
- *   dst[b] = Q8_0 block of the values of src[b] (b < n_blocks): d = max|v|
- *   / 127 and q = v / d rounded half away from zero, in float32 steps,
- *   d stored as binary16.  Source layouts: the public GGUF ones (Q4_1 20 B:
- *   f16 d, f16 m, 16 nibble bytes, v = w d + m; Q5_0 22 B: f16 d, 32 high
- *   bits, nibbles, v = (w - 16) d; Q5_1 24 B: d, m, high bits, nibbles,
- *   v = w d + m).  K-quants are not covered.  src and dst: device memory,
- *   2-byte aligned, not overlapping; dst receives n_blocks * 34 bytes of
- *   canonical Q8_0 blocks, ready for qg_repack(QG_Q8_0, ...).  Asynchronous
- *   on `stream`; the bytes are a function of the source bytes alone.
+ *   Each run of 32 values of src (in order) becomes one Q8_0 block of dst:
+ *   with v the run's float32 values, d = max|v| / 127 rounded to float32,
+ *   r = 1 / d rounded to float32 (0 when d is 0), q_j = v_j * r rounded to
+ *   float32 and then to the nearest integer, halves away from zero; d is
+ *   stored as binary16 (nearest even).
+ *   Source layouts, the public GGUF ones (values as float32, one rounding):
+ *     Q4_1  20 B / 32 values: f16 d, f16 m, 16 nibble bytes; v = w d + m.
+ *     Q5_0  22 B / 32: f16 d, 32 high bits, nibbles; v = (w - 16) d.
+ *     Q5_1  24 B / 32: d, m, high bits, nibbles; v = w d + m.
+ *     Q4_K 144 B / 256: f16 d, f16 dmin, 12 bytes of 6-bit scales and mins
+ *           of 8 sub-blocks, 128 nibble bytes; v = (d sc) w - dmin m.
+ *     Q5_K 176 B / 256: Q4_K plus 32 bytes of fifth bits.
+ *     Q6_K 210 B / 256: 128 bytes low nibbles, 64 bytes 2-bit tops, 16 int8
+ *           scales, f16 d; v = (d sc) (w - 32).
+ *   n_blocks counts source blocks; dst receives n_blocks * 34 bytes (Q4_1,
+ *   Q5_0, Q5_1) or n_blocks * 8 * 34 bytes (K-quants) of canonical Q8_0
+ *   blocks, ready for qg_repack(QG_Q8_0, ...).  src and dst: device memory,
+ *   2-byte aligned, not overlapping.  Errors: QG_EINVAL (source type, null
+ *   pointer, overlap), QG_ESHAPE (n_blocks < 1 or more than 2^36 output
+ *   blocks), QG_EALIGN, QG_EHIP.  Asynchronous on `stream`; the bytes are a
+ *   function of the source bytes alone.
  * ------------------------------------------------------------------------ */
 int qg_requant_q8_0(int src_type, int64_t n_blocks, const void *src, void *dst, void *stream);
 

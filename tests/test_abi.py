@@ -208,6 +208,12 @@ def test_requant_checks():
     assert rq(6, 10, src + 1, dst, None) == EALIGN
     assert rq(7, 10, src, dst + 1, None) == EALIGN
     assert rq(3, 10, src, src + 100, None) == EINVAL   # 200 source bytes overlap the output
+    assert rq(15, 10, src, dst, None) == EINVAL         # Q8_K is not a source type
+    assert rq(12, (1 << 33) + 1, src, dst, None) == ESHAPE   # more than 2^36 output blocks
+    assert rq(3, (1 << 36) + 1, src, dst, None) == ESHAPE
+    assert rq(14, 10, src + 1, dst, None) == EALIGN
+    assert rq(13, 10, src, src + 1000, None) == EINVAL  # 1760 source bytes overlap the output
+    assert rq(12, 10, src, src - 2000, None) == EINVAL  # 2720 output bytes overlap the source
 
 
 def test_rmsnorm_checks():

@@ -333,17 +333,45 @@ def test_gateup_parity(env, qtype, rows, cols, ncols):
 # --------------------------------------------------- requantisation to Q8_0
 def _src_blocks(src_type, nb, seed):
     """Random source blocks with finite scales of moderate size (the f16
-    exponent kept in 2^-14 .. 2^1) and random offsets for the types that
-    have one."""
+    exponent kept in 2^-14 .. 2^1) and random offsets (Q4_1, Q5_1) or
+    sub-block mins (Q4_K, Q5_K) for the types that have one; the rest of
+    the bytes (weights, K-quant scale bytes) uniformly random."""
     from oracle import requant as rq
     g = np.random.default_rng(seed)
     raw = g.integers(0, 256, (nb, rq.SRC_BLOCK_BYTES[src_type]), dtype=np.uint8)
     d = (g.uniform(-1.0, 1.0, nb) * 2.0 ** g.integers(-14, 2, nb)).astype(np.float16)
-    raw[:, 0:2] = d.view(np.uint8).reshape(-1, 2)
-    if src_type != rq.Q5_0:
+    d_off = 208 if src_type == rq.Q6_K else 0
+    raw[:, d_off:d_off + 2] = d.view(np.uint8).reshape(-1, 2)
+    if src_type not in (rq.Q5_0, rq.Q6_K):
         m = (g.standard_normal(nb) * 2.0 ** g.integers(-12, 3, nb)).astype(np.float16)
         raw[:, 2:4] = m.view(np.uint8).reshape(-1, 2)
     return raw
+
+
+def _ktie_block(src_type):
+    """A K-quant super-block whose first run has largest magnitude 127 and
+    values on exact halves (Q8_0 scale 1, reciprocal exact): Q4_K / Q5_K
+    with d = dmin = 0.5, sc_0 = 17, m_0 = 1 (8.5 w - 0.5, w = 0..15 twice);
+    Q6_K with d = 1/32, scales 0 and 1 = 127 ((127 / 32)(w - 32), w = 2 l
+    mod 64: w = 0 gives -127, w = 16 and 48 give -63.5 and 63.5).  The
+    other runs random."""
+    from oracle import requant as rq
+    b = np.random.default_rng(5).integers(0, 256, rq.SRC_BLOCK_BYTES[src_type]).astype(np.uint8)
+    if src_type == rq.Q6_K:
+        w = (2 * np.arange(32)) % 64
+        b[0:32] = (b[0:32] & 0xF0) | (w & 15)
+        b[128:160] = (b[128:160] & 0xFC) | (w >> 4)
+        b[192:194] = 127
+        b[208:210] = np.array([1.0 / 32], np.float16).view(np.uint8)
+        return b
+    b[0:4] = np.array([0.5, 0.5], np.float16).view(np.uint8)
+    b[4] = (b[4] & 0xC0) | 17
+    b[8] = (b[8] & 0xC0) | 1
+    q0 = 16 if src_type == rq.Q4_K else 48
+    b[q0:q0 + 32] = (b[q0:q0 + 32] & 0xF0) | (np.arange(32) % 16)
+    if src_type == rq.Q5_K:
+        b[16:48] &= 0xFE
+    return b
 
 
 def _tie_block(src_type):
@@ -371,60 +399,82 @@ def _tie_block(src_type):
 
 
 def test_tie_block_has_halves():
-    """The planted block does put quotients on exact halves (oracle)."""
+    """The planted blocks do put quotients on exact halves (oracle)."""
     from oracle import requant as rq
     for t in (3, 6, 7):
         v = rq.decode_values_f32(t, _tie_block(t)[None, :])[0]
         assert np.max(np.abs(v)) == 127.0
         assert np.any(np.abs(v - np.trunc(v)) == 0.5)
+    for t in (12, 13, 14):
+        v = rq.decode_values_f32(t, _ktie_block(t)[None, :])[0, :32]
+        assert np.max(np.abs(v)) == 127.0
+        assert np.any(np.abs(v - np.trunc(v)) == 0.5)
 
 
-@pytest.mark.parametrize("src_type", [3, 6, 7])
-@pytest.mark.parametrize("nb", [1, 255, 256, 257, 1024, 40000])
+_RQ_SIZES = {3: [1, 255, 256, 257, 1024, 40000], 6: [1, 255, 256, 257, 1024, 40000],
+             7: [1, 255, 256, 257, 1024, 40000], 12: [1, 31, 32, 33, 1000, 5000],
+             13: [1, 31, 32, 33, 1000, 5000], 14: [1, 31, 32, 33, 1000, 5000]}
+
+
+@pytest.mark.parametrize("src_type,nb", [(t, n) for t, ns in _RQ_SIZES.items() for n in ns])
 def test_requant_bytes_exact(env, src_type, nb):
-    """Every output byte equal to the oracle's, including all-zero and
-    single-value blocks and a tail past a multiple of 256 blocks."""
+    """Every output byte equal to the oracle's, including all-zero blocks,
+    blocks of one value (Q4_1 / Q5_0 / Q5_1 scale only) or all-zero runs
+    (K-quants with zero scales), a block with ties and a tail past a
+    workgroup's run (256 blocks; 32 K-quant super-blocks)."""
     torch, qg, dev = env
     from oracle import requant as rq
     raw = _src_blocks(src_type, nb, seed=nb + src_type)
+    kq = src_type in (rq.Q4_K, rq.Q5_K, rq.Q6_K)
     if nb > 3:
         raw[1, :] = 0                                  # all zero
-        raw[2, 4:] = 0                                 # scale only: every value the offset (or -16 d)
-        raw[3] = _tie_block(src_type)
+        if src_type == rq.Q6_K:
+            raw[2, 192:200] = 0                        # runs 0..3 zero
+        elif kq:
+            raw[2, 4:16] = 0                           # every scale and min zero
+        else:
+            raw[2, 4:] = 0                             # scale only: every value the offset (or -16 d)
+        raw[3] = _ktie_block(src_type) if kq else _tie_block(src_type)
     want = rq.requant_q8_0(src_type, raw)
-    got = host(qg.requant_q8_0(src_type, up(env, raw.reshape(-1)), nb)).reshape(nb, 34)
+    nout = want.shape[0]
+    got = host(qg.requant_q8_0(src_type, up(env, raw.reshape(-1)), nb)).reshape(nout, 34)
     bad = np.flatnonzero(np.any(got != want, axis=1))
     assert bad.size == 0, (bad[:5], got[bad[:1]], want[bad[:1]])
 
 
-@pytest.mark.parametrize("src_type", [3, 6, 7])
+@pytest.mark.parametrize("src_type", [3, 6, 7, 12, 13, 14])
 def test_requant_unaligned(env, src_type):
     """Source and destination 2 bytes past a 16-byte boundary (the 16-bit
     word path) give the same bytes, and nothing outside the output is
     written."""
     torch, qg, dev = env
     from oracle import requant as rq
-    nb = 1000
+    nb = 1000 if src_type < 12 else 130
     raw = _src_blocks(src_type, nb, seed=77 + src_type)
     bs = rq.SRC_BLOCK_BYTES[src_type]
+    want = rq.requant_q8_0(src_type, raw)
+    no = want.size
     sbuf = torch.zeros(nb * bs + 16, dtype=torch.uint8, device=dev)
     sbuf[2:2 + nb * bs] = up(env, raw.reshape(-1))
-    dbuf = torch.full((nb * 34 + 16,), 0xA5, dtype=torch.uint8, device=dev)
-    qg.requant_q8_0(src_type, sbuf[2:2 + nb * bs], nb, dbuf[2:2 + nb * 34])
+    dbuf = torch.full((no + 16,), 0xA5, dtype=torch.uint8, device=dev)
+    qg.requant_q8_0(src_type, sbuf[2:2 + nb * bs], nb, dbuf[2:2 + no])
     got = dbuf.cpu().numpy()
-    assert np.all(got[:2] == 0xA5) and np.all(got[2 + nb * 34:] == 0xA5)
-    assert np.array_equal(got[2:2 + nb * 34].reshape(nb, 34), rq.requant_q8_0(src_type, raw))
+    assert np.all(got[:2] == 0xA5) and np.all(got[2 + no:] == 0xA5)
+    assert np.array_equal(got[2:2 + no].reshape(-1, 34), want)
 
 
-def test_requant_then_product(env):
+@pytest.mark.parametrize("src_type", [3, 12, 13, 14])
+def test_requant_then_product(env, src_type):
     """The requantised blocks through repack and the GEMV: against the
-    oracle's product of the oracle's Q8_0 bytes."""
+    oracle's product of the oracle's Q8_0 bytes (the source blocks in row
+    order, so each row of 1024 values is 32 Q8_0 blocks)."""
     torch, qg, dev = env
     from oracle import requant as rq
     rows, cols = 300, 1024
-    raw = _src_blocks(3, rows * cols // 32, seed=9)
-    q8d = qg.requant_q8_0(3, up(env, raw.reshape(-1)), rows * cols // 32)
-    want = rq.requant_q8_0(3, raw)
+    nb = rows * cols // (256 if src_type >= 12 else 32)
+    raw = _src_blocks(src_type, nb, seed=9)
+    q8d = qg.requant_q8_0(src_type, up(env, raw.reshape(-1)), nb)
+    want = rq.requant_q8_0(src_type, raw)
     assert np.array_equal(q8d.cpu().numpy().reshape(-1, 34), want)
     W = qg.qg_repack(Q8, q8d, rows, cols)
     x = synth.gen_x(cols, 2, cfg_id=11)
