@@ -76,6 +76,7 @@ _SIGS = {
     "qgemm16": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i32,
                                _vp, _sz, _vp]),
     "qg_gemm16_batch_ws_bytes": (_sz, [ctypes.POINTER(qg_gemm16_problem), _i32]),
+    "qg_gemm16_batch_splits": (ctypes.c_int, [ctypes.POINTER(qg_gemm16_problem), _i32, ctypes.POINTER(ctypes.c_int32)]),
     "qgemm16_batch": (ctypes.c_int, [ctypes.POINTER(qg_gemm16_problem), _i32, _vp, _sz, _vp]),
     "qg_gateup_ws_bytes": (_sz, [_i64, _i64]),
     "gateup_silu": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _i32,
@@ -263,10 +264,7 @@ def qgemm16(w: QMatrix, X, Y=None, accumulate: bool = False):
     return Y
 
 
-def qgemm16_batch(items):
-    """One launch over several 16-column problems: items is a list of
-    (w: QMatrix, X [16, cols], Y [16, rows] or None, accumulate).  Each Y is
-    bitwise equal to qgemm16 on that problem.  Returns the list of Y."""
+def _batch_array(items):
     torch = _torch()
     n = len(items)
     arr = (qg_gemm16_problem * max(n, 1))()
@@ -281,9 +279,27 @@ def qgemm16_batch(items):
         arr[i] = qg_gemm16_problem(w.qtype, int(acc), w.qs.data_ptr(), w.d.data_ptr(), w.rows, w.cols,
                                    X.data_ptr(), _ld(X), Y.data_ptr(), _ld(Y))
     dev = items[0][1].device if n else torch.device("cuda:0")
+    return arr, n, outs, dev
+
+
+def qgemm16_batch(items):
+    """One launch over several 16-column problems: items is a list of
+    (w: QMatrix, X [16, cols], Y [16, rows] or None, accumulate).  Each Y is
+    bitwise equal to qgemm16 on that problem with the K split of
+    gemm16_batch_splits(items) pinned.  Returns the list of Y."""
+    arr, n, outs, dev = _batch_array(items)
     ws = workspace(lib.qg_gemm16_batch_ws_bytes(arr, n), dev)
     _check(lib.qgemm16_batch(arr, n, ws.data_ptr(), ws.numel(), _stream(dev)), "qgemm16_batch")
     return outs
+
+
+def gemm16_batch_splits(items):
+    """The K segments qgemm16_batch uses for each problem of `items` (same
+    form as qgemm16_batch's; a None output is allocated for the query)."""
+    arr, n, _, _ = _batch_array(items)
+    out = (ctypes.c_int32 * max(n, 1))()
+    _check(lib.qg_gemm16_batch_splits(arr, n, out), "qg_gemm16_batch_splits")
+    return [int(out[i]) for i in range(n)]
 
 
 def gateup_silu(wg: QMatrix, wu: QMatrix, X, H=None):

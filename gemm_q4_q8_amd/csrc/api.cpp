@@ -244,6 +244,16 @@ size_t qg_gemm16_batch_ws_bytes(const qg_gemm16_problem *p, int32_t n) {
   return gemm16_batch_ws_bytes(p, n);
 }
 
+int qg_gemm16_batch_splits(const qg_gemm16_problem *p, int32_t n, int32_t *splits) {
+  if (!splits) return QG_EINVAL;
+  int st = check_batch(p, n);
+  if (st) return st;
+  int S[QG_BATCH_MAX];
+  gemm16_batch_splits(p, n, S);
+  for (int i = 0; i < n; ++i) splits[i] = S[i];
+  return QG_OK;
+}
+
 int qgemm16_batch(const qg_gemm16_problem *p, int32_t n, void *ws, size_t ws_bytes, void *stream) {
   int st = check_batch(p, n);
   if (st) return st;

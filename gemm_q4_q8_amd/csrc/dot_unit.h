@@ -102,6 +102,8 @@ __host__ __device__ constexpr size_t dot_stage_bytes(int64_t ntiles, int nc) {
 // Smallest workgroup (waves) a streamed-staging unit of launch-time size
 // runs with: its per-thread chunk pieces are sized for it.
 constexpr int DOT_XS_WMIN = 8;
+// Tile columns of 16-column activations per LDS chunk (double-buffered).
+constexpr int X16_CHUNK = 2;
 
 // Register fence after a matrix-core product and the FMAs that read its
 // result.  The matrix core reads A and B and writes all four result
@@ -205,8 +207,12 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   constexpr int NI = NC < 4 ? NC : 4;
   constexpr int TB = QTraits<QT>::tile_bytes;
   constexpr int QW = (QT == Q4) ? 1 : 2;  // 16-byte loads per lane per tile
-  constexpr int CHV = PF * TILE_BLOCKS * NC * 4;   // 8-value pieces per chunk
-  constexpr int CHH = PF * TILE_BLOCKS * NC * 32;  // halves per chunk buffer
+  // tile columns per activation chunk (16 columns): the weight stream runs
+  // PF tile columns ahead, a whole number of chunks
+  constexpr int CT = XS ? X16_CHUNK : PF;
+  static_assert(PF % CT == 0, "weight prefetch: whole chunks");
+  constexpr int CHV = CT * TILE_BLOCKS * NC * 4;   // 8-value pieces per chunk
+  constexpr int CHH = CT * TILE_BLOCKS * NC * 32;  // halves per chunk buffer
   constexpr int XWMIN = WKT > 0 ? WKT : DOT_XS_WMIN;
   constexpr int XR = (CHV + XWMIN * 64 - 1) / (XWMIN * 64);  // pieces per thread per chunk (at most)
 
@@ -469,7 +475,7 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   auto compute = [&](int slot, int rel) {
     if constexpr (F16) {
       // the slot of tile column rel in its chunk's buffer
-      const int bl0 = ((((rel / PF) & 1) * PF) + rel % PF) * TILE_BLOCKS;
+      const int bl0 = ((((rel / CT) & 1) * CT) + rel % CT) * TILE_BLOCKS;
 #pragma unroll
       for (int j = 0; j < TILE_BLOCKS; ++j) A[j] = *(const h8 *)(xs + xrow((size_t)(bl0 + j) * XC + r, sl));
 #pragma unroll
@@ -531,20 +537,26 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   // PF tile columns in flight; loads past the segment read nothing
   if constexpr (XS) {
     // every wave runs the same trip count: the chunk hand-over is a barrier
+    // Chunk q (tile columns q CT ..) sits in buffer q % 2; the next chunk
+    // is loaded as chunk q starts and stored into the other buffer as it
+    // ends, where the barrier of chunk q - 1 has retired every read of it.
     const bool live = rt_base < a.NT;
     for (int k = 0; k < nkt; k += PF) {
-      XPiece np[XR];
 #pragma unroll
-      for (int i = 0; i < XR; ++i) x_ld(tid + i * NTHR, k + PF, CHV, xcs[i], np[i]);
+      for (int c0 = 0; c0 < PF; c0 += CT) {
+        XPiece np[XR];
 #pragma unroll
-      for (int p = 0; p < PF; ++p) {
-        if (live && k + p < nkt) compute(p, k + p);
-        load(p, k + p + PF);
+        for (int i = 0; i < XR; ++i) x_ld(tid + i * NTHR, k + c0 + CT, CHV, xcs[i], np[i]);
+#pragma unroll
+        for (int p = c0; p < c0 + CT; ++p) {
+          if (live && k + p < nkt) compute(p, k + p);
+          load(p, k + p + PF);
+        }
+        _Float16 *nb = xs + ((((k + c0) / CT) + 1) & 1) * CHH;
+#pragma unroll
+        for (int i = 0; i < XR; ++i) x_put(tid + i * NTHR, CHV, nb, np[i]);
+        __syncthreads();
       }
-      _Float16 *nb = xs + (((k / PF) + 1) & 1) * CHH;
-#pragma unroll
-      for (int i = 0; i < XR; ++i) x_put(tid + i * NTHR, CHV, nb, np[i]);
-      __syncthreads();
     }
   } else {
     const int nseg = rt_base < a.NT ? wnkt : 0;

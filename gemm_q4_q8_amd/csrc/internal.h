@@ -70,6 +70,7 @@ size_t qmv_ws_bytes(int64_t rows, int64_t cols, int slots, int nmat, int ncols_m
 int launch_qmv(const QmvCall &c);  // returns 0 or a QG_ status
 // Several 16-column problems in one launch (0 from the size query: too many
 // row groups for the counter words).
+void gemm16_batch_splits(const qg_gemm16_problem *p, int n, int *S);
 size_t gemm16_batch_ws_bytes(const qg_gemm16_problem *p, int n);
 int launch_gemm16_batch(const qg_gemm16_problem *p, int n, void *ws, size_t ws_bytes, hipStream_t stream);
 int launch_repack(int qtype, int64_t n_mat, int64_t rows, int64_t cols, const void *blocks,

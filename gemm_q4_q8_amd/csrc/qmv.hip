@@ -15,6 +15,8 @@
 // (1..8 columns, the same for every column count) and gemm16_splits().
 #include <string.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "dot_unit.h"
 #include "internal.h"
@@ -229,7 +231,8 @@ __global__ void __launch_bounds__(WMAX * 64) dot_kernel(DotArgs a) {
 // summing the segments (no unit waiting for a counter), 93 us: every
 // workgroup of a launch holds the same LDS, so reducers waiting at the tail
 // took the slots of units still to run.
-constexpr int G16_W = 8;   // waves (row tiles) per workgroup
+constexpr int G16_W = 8;   // waves per workgroup
+constexpr int G16_RT = 1;  // row tiles per wave
 constexpr int G16_PF = 2;  // tile columns in flight per wave
 
 struct G16Prob {
@@ -294,11 +297,11 @@ __global__ void __launch_bounds__(W * 64) gemm16_batch_kernel(G16Args b) {
   float bv = 0.0f;
   int32_t bi = 0;
   if (P.qt == Q4) {
-    if (P.acc) dot_unit<Q4, 16, 1, EPI_ACC, 1, G16_PF, W, PH_PLAIN>(a, g, s, smem, &flag, bv, bi);
-    else dot_unit<Q4, 16, 1, EPI_STORE, 1, G16_PF, W, PH_PLAIN>(a, g, s, smem, &flag, bv, bi);
+    if (P.acc) dot_unit<Q4, 16, 1, EPI_ACC, G16_RT, G16_PF, W, PH_PLAIN>(a, g, s, smem, &flag, bv, bi);
+    else dot_unit<Q4, 16, 1, EPI_STORE, G16_RT, G16_PF, W, PH_PLAIN>(a, g, s, smem, &flag, bv, bi);
   } else {
-    if (P.acc) dot_unit<Q8, 16, 1, EPI_ACC, 1, G16_PF, W, PH_PLAIN>(a, g, s, smem, &flag, bv, bi);
-    else dot_unit<Q8, 16, 1, EPI_STORE, 1, G16_PF, W, PH_PLAIN>(a, g, s, smem, &flag, bv, bi);
+    if (P.acc) dot_unit<Q8, 16, 1, EPI_ACC, G16_RT, G16_PF, W, PH_PLAIN>(a, g, s, smem, &flag, bv, bi);
+    else dot_unit<Q8, 16, 1, EPI_STORE, G16_RT, G16_PF, W, PH_PLAIN>(a, g, s, smem, &flag, bv, bi);
   }
 }
 
@@ -474,7 +477,7 @@ static int launch_dot_t(const QmvCall &c, int S, int W = WKT, int SW = 1) {
   // staged activations: the unit's tile columns (all of K with in-workgroup
   // segments; at most ceil(KT / S) otherwise), or (16 columns) two chunks
   // of PF tile columns; then the in-workgroup segment sums
-  size_t lds = NC >= 16 ? dot_stage_bytes(2 * PF, NC) : dot_stage_bytes(SW > 1 ? KT : cdiv(KT, S), NC);
+  size_t lds = NC >= 16 ? dot_stage_bytes(2 * X16_CHUNK, NC) : dot_stage_bytes(SW > 1 ? KT : cdiv(KT, S), NC);
   lds += (size_t)(SW - 1) * (W / SW) * NMAT * RT * (NC < 4 ? NC : 4) * 64 * 4;
   if (RMSN) lds += (size_t)NC * KT * TILE_BLOCKS * 4 * 4 + (size_t)NC * 4;  // squares per piece, 1/rms
   if (lds > LDS_HARD - 1024) return QG_EUNSUPPORTED;
@@ -645,18 +648,74 @@ static int dispatch_qt(const QmvCall &c) {
   return QG_EINVAL;
 }
 
+// K segments of each problem of a grouped launch.  Each problem's K is cut
+// into segments about as long as the shortest K of the launch (at least
+// one), so that the units of all problems stream about equally many tile
+// columns and only the longer problems pay a hand-off; these counts are
+// then multiplied by the smallest factor that gives at least two units per
+// CU (a launch whose units are all resident at once).  Segments stay at
+// least 4 tile columns long and at most 255.  Measured at the prefill pass
+// (5120 -> 17408 and back, Q4_0 and Q8_0, largest units first): the counts
+// this gives (1 and 3) took 56.9 us against 60.1-62.0 us for (2, 6), (1,
+// 4) and the single-problem splits (3, 9).
+void gemm16_batch_splits(const qg_gemm16_problem *p, int n, int *S) {
+  int64_t ktmin = INT64_MAX;
+  for (int i = 0; i < n; ++i) ktmin = std::min<int64_t>(ktmin, cdiv(p[i].cols / 32, 4));
+  int64_t base[QG_BATCH_MAX], cap[QG_BATCH_MAX], G[QG_BATCH_MAX];
+  for (int i = 0; i < n; ++i) {
+    const int64_t KT = cdiv(p[i].cols / 32, 4);
+    base[i] = std::max<int64_t>(1, (KT + ktmin / 2) / ktmin);
+    cap[i] = std::min<int64_t>(255, std::max<int64_t>(1, KT / 4));
+    G[i] = cdiv(cdiv(p[i].rows, 16), G16_W * G16_RT);
+  }
+  const int64_t want = 2 * (int64_t)device_cus();
+  for (int64_t m = 1;; ++m) {
+    int64_t units = 0;
+    bool grows = false;
+    for (int i = 0; i < n; ++i) {
+      S[i] = (int)std::min(base[i] * m, cap[i]);
+      units += G[i] * S[i];
+      grows |= base[i] * m < cap[i];
+    }
+    if (units >= want || !grows) break;
+  }
+}
+
 // Workspace of a grouped launch: the counters of every problem's row groups
 // in the shared counter words, then each problem's segment partials.  Fills
-// `b` when given (the pointers inside `ws`).
+// `b` when given (the pointers inside `ws`).  The problems take their units
+// in the launch in order of decreasing weight bytes per unit (ties: the
+// caller's order): the hardware hands out workgroups in launch order, so the
+// longest units start first and the short ones fill in at the end (measured
+// at the prefill pass with the single-problem splits: 71.6 us with the
+// caller's order Q4_0 before Q8_0, 66.1 us largest units first).  The order
+// changes no sum.
 static size_t gemm16_batch_layout(const qg_gemm16_problem *p, int n, G16Args *b, uint8_t *ws) {
   size_t off = QG_WS_SYNC_BYTES, words = 0;
-  int64_t u0 = 0;
+  int ord[QG_BATCH_MAX], Sp[QG_BATCH_MAX];
+  int64_t ubytes[QG_BATCH_MAX];
+  gemm16_batch_splits(p, n, Sp);
   for (int i = 0; i < n; ++i) {
+    const int64_t KT = cdiv(p[i].cols / 32, 4);
+    const int S = Sp[i];
+    const int64_t tb = p[i].qtype == QG_Q4_0 ? QTraits<Q4>::tile_bytes : QTraits<Q8>::tile_bytes;
+    ubytes[i] = (int64_t)G16_W * G16_RT * cdiv(KT, S) * tb;
+    ord[i] = i;
+  }
+  for (int i = 1; i < n; ++i)  // stable insertion sort, decreasing unit bytes
+    for (int j = i; j > 0 && ubytes[ord[j]] > ubytes[ord[j - 1]]; --j) {
+      const int t = ord[j];
+      ord[j] = ord[j - 1];
+      ord[j - 1] = t;
+    }
+  int64_t u0 = 0;
+  for (int k = 0; k < n; ++k) {
+    const int i = ord[k];
     const int64_t NT = cdiv(p[i].rows, 16), KT = cdiv(p[i].cols / 32, 4);
-    const int S = gemm16_splits(p[i].rows, p[i].cols);
-    const int64_t G = cdiv(NT, G16_W);
+    const int S = Sp[i];
+    const int64_t G = cdiv(NT, G16_W * G16_RT);
     if (b) {
-      G16Prob &q = b->p[i];
+      G16Prob &q = b->p[k];
       q.qs = (const uint8_t *)p[i].qs;
       q.d = (const uint8_t *)p[i].d;
       q.X = p[i].X;
@@ -701,7 +760,7 @@ int launch_gemm16_batch(const qg_gemm16_problem *p, int n, void *ws, size_t ws_b
     if (xb >= ((int64_t)1 << 31) || (int64_t)q.KT * tb >= ((int64_t)1 << 31)) return QG_EUNSUPPORTED;
     if ((size_t)q.S * q.NT * dot_part_floats(16) * 4 >= ((size_t)1 << 31)) return QG_EUNSUPPORTED;
   }
-  const size_t lds = dot_stage_bytes(2 * G16_PF, 16);  // two chunks
+  const size_t lds = dot_stage_bytes(2 * X16_CHUNK, 16);  // two chunks
   clear_hip_error();
   hipLaunchKernelGGL(gemm16_batch_kernel<G16_W>, dim3((unsigned)b.units), dim3(G16_W * 64), lds, stream, b);
   return launch_status();

@@ -191,11 +191,19 @@ int qgemm16(int qtype, const void *qs, const void *d, int64_t rows, int64_t cols
  *
  *   for each problem i < n:  Y_i = (accumulate_i ? Y_i : 0) + W_i X_i,
  *   X_i cols_i x 16, Y_i rows_i x 16, each as qgemm16 (same checks).
- * Each Y_i is bitwise equal to qgemm16 on problem i (same K segments, same
- * order).  The problems run concurrently in one launch, so no Y_i may
- * overlap any X_j or any other Y_j (QG_EINVAL).  1 <= n <= QG_BATCH_MAX
- * (else QG_ESHAPE); Q4_0 and Q8_0 problems may be mixed.  `p` is a HOST
- * array of n descriptors; the library copies it into the launch.
+ * The launch picks each problem's K split for the pass as a whole: K cut
+ * into segments about as long as the shortest K among the problems (at
+ * least one), all counts then multiplied by the smallest factor that gives
+ * at least two work units per CU of the current device; segments at least
+ * 4 tile columns long, at most 255 of them.  qg_gemm16_batch_splits reports
+ * these counts (host only); Y_i is bitwise equal to qgemm16 on problem i
+ * with that split pinned (qg_plan_set(QG_OP_GEMV, qtype, rows, cols, 16,
+ * QG_PLAN_SPLIT(splits[i]))), and the same on every call.  The problems run
+ * concurrently in one launch, so no Y_i may overlap any X_j or any other
+ * Y_j (QG_EINVAL).  1 <= n <= QG_BATCH_MAX (else QG_ESHAPE); Q4_0 and Q8_0
+ * problems may be mixed.  `p` is a HOST array of n descriptors; the library
+ * copies it into the launch.  Errors of the split query: those of the
+ * descriptors (as qgemm16_batch), QG_EINVAL for a null `splits`.
  * ------------------------------------------------------------------------ */
 #define QG_BATCH_MAX 8
 
@@ -212,6 +220,8 @@ typedef struct {
 } qg_gemm16_problem;
 
 size_t qg_gemm16_batch_ws_bytes(const qg_gemm16_problem *p, int32_t n);
+
+int qg_gemm16_batch_splits(const qg_gemm16_problem *p, int32_t n, int32_t *splits);
 
 int qgemm16_batch(const qg_gemm16_problem *p, int32_t n, void *ws, size_t ws_bytes,
                   void *stream);

@@ -145,6 +145,31 @@ def test_gemm16_batch_checks():
     assert L.qgemm16_batch(a, 2, ws + 16, wsb, None) == EALIGN
 
 
+def test_gemm16_batch_splits():
+    """The grouped launch's K splits (device without a GPU: 256 CUs): the
+    prefill pass's segments as long as its shortest K; a lone problem split
+    until it has two units per CU; short K never split."""
+    P = qg.qg_gemm16_problem
+    Xs = [FAKE + (k << 26) for k in range(1, 5)]
+    Ys = [FAKE + (k << 26) for k in range(5, 9)]
+
+    def splits(shapes):
+        a = (P * len(shapes))()
+        for i, (qt, r, c) in enumerate(shapes):
+            a[i] = P(qt, 0, FAKE, FAKE, r, c, Xs[i], c, Ys[i], r)
+        out = (ctypes.c_int32 * len(shapes))()
+        assert L.qg_gemm16_batch_splits(a, len(shapes), out) == 0
+        return list(out)
+
+    assert splits([(2, 17408, 5120), (2, 5120, 17408), (8, 17408, 5120), (8, 5120, 17408)]) == [1, 3, 1, 3]
+    assert splits([(2, 17408, 5120)]) == [4]          # 136 row groups x 4 >= 512 units
+    assert splits([(8, 5120, 17408)]) == [13]         # 40 row groups x 13
+    assert splits([(2, 64, 128), (8, 100, 256)]) == [1, 1]
+    a = (P * 1)(P(2, 0, FAKE, FAKE, 64, 128, Xs[0], 128, Ys[0], 64))
+    assert L.qg_gemm16_batch_splits(a, 1, None) == EINVAL
+    assert L.qg_gemm16_batch_splits(a, 0, (ctypes.c_int32 * 1)()) == ESHAPE
+
+
 def test_lmhead_noalloc_checks():
     x, oi = FAKE + (1 << 20), FAKE + (2 << 20)
     f = L.lmhead_argmax_noalloc

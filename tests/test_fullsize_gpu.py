@@ -87,8 +87,8 @@ def test_prefill_gemm16(env, qtype, N, K):
 def test_prefill_pass_batch(env):
     """One prefill pass of the 16-column workload as one launch: Q4_0 and
     Q8_0 at 5120 -> 17408 and 17408 -> 5120, each output bitwise equal to its
-    qgemm16 call, and rows sampled across every row tile group checked
-    against the oracle."""
+    qgemm16 call with the launch's K split pinned, and rows sampled across
+    every row tile group checked against the oracle."""
     torch, qg, dev = env
     probs, raws = [], []
     for i, (qt, N, K) in enumerate([(Q4, 17408, 5120), (Q4, 5120, 17408), (Q8, 17408, 5120), (Q8, 5120, 17408)]):
@@ -96,12 +96,20 @@ def test_prefill_pass_batch(env):
         X = synth.gen_x(K, 16, cfg_id=synth.CFG_PREFILL, col0=16 * i)
         probs.append((W, up(env, X.T), None, 0))
         raws.append((qt, raw, X))
-    say("prefill pass: 4 matrices in one launch")
+    splits = qg.gemm16_batch_splits(probs)
+    say(f"prefill pass: 4 matrices in one launch, K splits {splits}")
+    assert splits == [1, 3, 1, 3]   # segments as long as the shortest K; 512 units (2 per CU)
     outs = qg.qgemm16_batch(probs)
+    try:
+        for (W, _, _, _), sp in zip(probs, splits):
+            qg.plan_set(qg.OP_GEMV, W.qtype, W.rows, W.cols, 16, qg.PLAN_SPLIT(sp) | qg.PLAN_STRICT)
+        single = [qg.qgemm16(W, X) for W, X, _, _ in probs]
+    finally:
+        qg.plan_reset()
     torch.cuda.synchronize()
     g = np.random.default_rng(46)
     for i, (W, X, _, _) in enumerate(probs):
-        assert torch.equal(outs[i], qg.qgemm16(W, X)), i
+        assert torch.equal(outs[i], single[i]), i
         qt, raw, Xh = raws[i]
         rows = np.unique(np.concatenate([g.integers(0, W.rows, 600), [0, W.rows - 1]]))
         ref, a = ops.gemv(qt, raw, Xh, rows=rows)

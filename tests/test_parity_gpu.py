@@ -292,8 +292,8 @@ BATCH = [(Q4, 40, 416, 0), (Q8, 200, 2080, 1), (Q4, 600, 11264, 1), (Q8, 64, 409
 def test_gemm16_batch(env, n):
     """Several 16-column problems (Q4_0 and Q8_0 mixed, storing and
     accumulating, one to eight of them) in one launch: each output against
-    the oracle, bitwise equal to qgemm16 on that problem, and bitwise equal
-    again on a repeat launch."""
+    the oracle, bitwise equal to qgemm16 on that problem with the launch's
+    K split pinned, and bitwise equal again on a repeat launch."""
     torch, qg, dev = env
     say(f"gemm16 batch n={n}")
     probs, refs = [], []
@@ -303,7 +303,14 @@ def test_gemm16_batch(env, n):
         y0 = synth.rng(702, i).standard_normal((rows, 16)).astype(np.float32)
         probs.append((W, up(env, X.T), up(env, y0.T) if acc else None, acc))
         refs.append((raw, X, y0))
-    single = [qg.qgemm16(W, X, None if Y is None else Y.clone(), accumulate=bool(acc)) for W, X, Y, acc in probs]
+    splits = qg.gemm16_batch_splits(probs)
+    say(f"  splits {splits}")
+    try:
+        for (qt, rows, cols, _), sp in zip(BATCH[:n], splits):
+            qg.plan_set(qg.OP_GEMV, qt, rows, cols, 16, qg.PLAN_SPLIT(sp) | qg.PLAN_STRICT)
+        single = [qg.qgemm16(W, X, None if Y is None else Y.clone(), accumulate=bool(acc)) for W, X, Y, acc in probs]
+    finally:
+        qg.plan_reset()
     outs = qg.qgemm16_batch([(W, X, None if Y is None else Y.clone(), acc) for W, X, Y, acc in probs])
     again = qg.qgemm16_batch([(W, X, None if Y is None else Y.clone(), acc) for W, X, Y, acc in probs])
     torch.cuda.synchronize()
