@@ -313,22 +313,7 @@ def run_extras(B, kernels):
     log("  requant done")
 
     # MoE FFN, 256 experts (8 active) + shared, hidden 2048, ffn 512
-    E, H, F, k = 256, 2048, 512, 8
-    g = np.random.default_rng(61)
-    def stack(rows, cols):
-        raw = np.stack([synth.gen_weights(Q4, rows, cols, 0.02, g) for _ in range(E)])
-        return qg.qg_repack(Q4, B.up(raw.reshape(-1)), rows, cols, E)
-    gate, upm, down = stack(F, H), stack(F, H), stack(H, F)
-    sh = [B.matrix(Q4, r, c, seed=62 + i, sigma=0.02)[0] for i, (r, c) in enumerate(((F, H), (F, H), (H, F)))]
-    router = B.up(synth.gen_f32((E, H), 0.02, g))
-    layer_bytes = 3 * E * qbytes(Q4, F, H)
-    copies = max(2, -(-POOL_BYTES // layer_bytes))
-    cl = lambda m: qg.QMatrix(m.qtype, m.rows, m.cols, m.n_mat, m.qs.clone(), m.d.clone())
-    moes = []
-    for c in range(copies):
-        gg, uu, dd = (gate, upm, down) if c == 0 else (cl(gate), cl(upm), cl(down))
-        moes.append(qg.MoE(hidden=H, ffn=F, n_expert=E, top_k=k, router=router, gate=gg, up=uu,
-                           down=dd, sh_gate=sh[0], sh_up=sh[1], sh_down=sh[2]))
+    moes, (E, H, F, k), copies = moe_layers(B)
     eb = qbytes(Q4, F, H) * 3
     NX = 17  # distinct inputs per token count, cycled against the layer copies
     for T in (1, 16):
@@ -366,7 +351,7 @@ def run_extras(B, kernels):
         t_nu, _ = B.graph_time([lambda i=i: norm_then_moe(i) for i in range(calls)], calls)
         kernels[f"moe_ffn_rmsnorm_fused_{T}tok"] = kernel_entry(nbytes + 4 * H, t_nf, None, reps_nf)
         kernels[f"rmsnorm_then_moe_ffn_{T}tok"] = kernel_entry(nbytes + 4 * H, t_nu, None, B.last)
-    del moes, gate, upm, down
+    del moes
     log("  moe done")
 
 
@@ -510,14 +495,44 @@ def cpu_baseline(raws, min_seconds=12.0):
                       f"host cores available: {host_cores}"}
 
 
+def moe_layers(B, copies=None):
+    """The benchmarked MoE layer (256 Q4_0 experts, 8 active, plus a shared
+    expert; hidden 2048, expert FFN 512) in `copies` address-distinct copies
+    of its experts (default: enough for >= 1 GiB of expert weights)."""
+    import synth
+    torch, qg = B.torch, B.qg
+    Q4 = qg.Q4_0
+    E, H, F, k = 256, 2048, 512, 8
+    g = np.random.default_rng(61)
+
+    def stack(rows, cols):
+        raw = np.stack([synth.gen_weights(Q4, rows, cols, 0.02, g) for _ in range(E)])
+        return qg.qg_repack(Q4, B.up(raw.reshape(-1)), rows, cols, E)
+    gate, upm, down = stack(F, H), stack(F, H), stack(H, F)
+    sh = [B.matrix(Q4, r, c, seed=62 + i, sigma=0.02)[0] for i, (r, c) in enumerate(((F, H), (F, H), (H, F)))]
+    router = B.up(synth.gen_f32((E, H), 0.02, g))
+    layer_bytes = 3 * E * qbytes(Q4, F, H)
+    if copies is None:
+        copies = max(2, -(-POOL_BYTES // layer_bytes))
+    cl = lambda m: qg.QMatrix(m.qtype, m.rows, m.cols, m.n_mat, m.qs.clone(), m.d.clone())
+    moes = []
+    for c in range(copies):
+        gg, uu, dd = (gate, upm, down) if c == 0 else (cl(gate), cl(upm), cl(down))
+        moes.append(qg.MoE(hidden=H, ffn=F, n_expert=E, top_k=k, router=router, gate=gg, up=uu,
+                           down=dd, sh_gate=sh[0], sh_up=sh[1], sh_down=sh[2]))
+    return moes, (E, H, F, k), copies
+
+
 def traffic_run(B):
     """Fixed launches for hardware-counter runs (rocprofv3 --pmc FETCH_SIZE /
     WRITE_SIZE): 5 element-wise copies of exactly 1 GiB (read 1 GiB, write
     1 GiB) as the scale reference, then 8 prefill-pass launches over 4
     address-distinct weight sets, then 8 launches of each single 16-column
     GEMM, 4 of the LM head with argmax, 16 decode gate/up and 16 decode down
-    launches, over address-distinct weights."""
+    launches, 16 verify launches (Q8_0 5120 x 5120) at 4 and at 8 columns,
+    and 8 MoE layers at 16 tokens, over address-distinct weights."""
     torch, qg = B.torch, B.qg
+    Q4, Q8 = qg.Q4_0, qg.Q8_0
     import synth
     a = torch.empty(POOL_BYTES // 4, dtype=torch.float32, device=B.dev).normal_()
     b = torch.empty_like(a)
@@ -559,6 +574,35 @@ def traffic_run(B):
     for i in range(16):
         qg.qgemv(ws[i % 6][2], h, y, accumulate=True)
     torch.cuda.synchronize()
+    del ws
+    # verify Q8_0 5120 x 5120 at 4 and 8 columns, 8 address-distinct copies
+    w, _ = B.matrix(Q8, 5120, 5120, seed=31, sigma=0.005)
+    vp = [w] + [qg.QMatrix(w.qtype, w.rows, w.cols, 1, w.qs.clone(), w.d.clone()) for _ in range(7)]
+    for nc in (4, 8):
+        xv = B.up(synth.gen_x(5120, nc, cfg_id=3).T)
+        yv = torch.empty((nc, 5120), device=B.dev)
+        torch.cuda.synchronize()
+        for i in range(16):
+            qg.qgemv(vp[i % 8], xv, yv)
+        torch.cuda.synchronize()
+    del vp, w
+    # the MoE layer at 16 tokens: 8 calls, each on a fresh input and the next
+    # of 4 copies of the experts; the algorithmic bytes of each call (router,
+    # the experts its routing reads, the shared expert, activations in and
+    # out) printed for the summary
+    moes, (E, H, F, k), copies = moe_layers(B, 4)
+    eb = qbytes(Q4, F, H) * 3
+    T = 16
+    Y = torch.zeros((T, H), device=B.dev)
+    tidx = torch.empty((T, k), dtype=torch.int32, device=B.dev)
+    nb = []
+    for i in range(8):
+        X = B.up(synth.gen_x(H, T, cfg_id=5, col0=T * i).T)
+        torch.cuda.synchronize()
+        qg.moe_ffn(moes[i % copies], X, Y, tidx)
+        torch.cuda.synchronize()
+        nb.append(4 * E * H + eb * (len(np.unique(tidx.cpu().numpy())) + 1) + 12 * H * T)
+    print(f"moe_16tok_algorithmic_bytes_per_call {float(np.mean(nb)):.0f}", flush=True)
     print("traffic run done", flush=True)
 
 
