@@ -69,7 +69,7 @@ __global__ void __launch_bounds__(WMAX * 64) dot_kernel(DotArgs a) {
       }
       uint64_t mine = 0;  // lane kk: the key of rank kk
       for (int kk = 0; kk < k; ++kk) {
-        const uint64_t w = wave_max_u64(loc);
+        const uint64_t w = wave_max_key(loc);
         if (lane == kk) mine = w;
         if (w != 0 && loc == w) {  // the owner drops the winner
           loc = 0;
@@ -92,10 +92,7 @@ __global__ void __launch_bounds__(WMAX * 64) dot_kernel(DotArgs a) {
 #pragma unroll
     for (int j = 0; j < QG_TOPK_MAX; ++j) top[j] = 0;
     const __amdgpu_buffer_rsrc_t rk = buf_range(a.cand_k, (uint32_t)(nc * 8));
-#ifndef TOPK_BATCH
-#define TOPK_BATCH 16
-#endif
-    constexpr int TKB = TOPK_BATCH;
+    constexpr int TKB = 16;
     for (int64_t q0 = tid; q0 < nc; q0 += TKB * NTHR) {
       uint64_t v[TKB];
 #pragma unroll
@@ -118,7 +115,7 @@ __global__ void __launch_bounds__(WMAX * 64) dot_kernel(DotArgs a) {
     // ... each wave takes its k best heads (the owner of a head pops it) ...
     __syncthreads();  // s_key is reused
     for (int kk = 0; kk < k; ++kk) {
-      const uint64_t w = wave_max_u64(top[0]);
+      const uint64_t w = wave_max_key(top[0]);
       if (lane == 0) s_key[wk * QG_TOPK_MAX + kk] = w;
       if (w != 0 && top[0] == w) {
 #pragma unroll
@@ -140,7 +137,7 @@ __global__ void __launch_bounds__(WMAX * 64) dot_kernel(DotArgs a) {
       }
       uint64_t mine = 0;
       for (int kk = 0; kk < k; ++kk) {
-        const uint64_t w = wave_max_u64(loc);
+        const uint64_t w = wave_max_key(loc);
         if (lane == kk) mine = w;
         if (w != 0 && loc == w) {
           loc = 0;
