@@ -192,8 +192,9 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   // WKT == 0: one row tile per wave of the workgroup as launched (at least
   // XWMIN waves when the activations stream in chunks)
   const int NTHR = WKT > 0 ? WKT * 64 : (int)blockDim.x;
-  // Wide batches stream their activations in chunks of PF tile columns,
-  // double-buffered in LDS and staged one chunk ahead of the products (the
+  // Wide batches stream their activations in chunks of X16_CHUNK tile
+  // columns, double-buffered in LDS and staged one chunk ahead of the
+  // products (the
   // whole segment would take several L2 round trips before the first
   // product); narrow ones stage the whole segment up front, as hi / lo
   // pairs.
@@ -211,10 +212,8 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   // PF tile columns ahead, a whole number of chunks
   constexpr int CT = XS ? X16_CHUNK : PF;
   static_assert(PF % CT == 0, "weight prefetch: whole chunks");
-  constexpr int CHV = CT * TILE_BLOCKS * NC * 4;   // 8-value pieces per chunk
   constexpr int CHH = CT * TILE_BLOCKS * NC * 32;  // halves per chunk buffer
   constexpr int XWMIN = WKT > 0 ? WKT : DOT_XS_WMIN;
-  constexpr int XR = (CHV + XWMIN * 64 - 1) / (XWMIN * 64);  // pieces per thread per chunk (at most)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wk = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -355,6 +354,30 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
     }
   };
 
+  // 16 columns: wave w stages columns w, w + waves, ... of each chunk, lane
+  // l the 4 values at k 4 l .. 4 l + 3 of the chunk's 256, so that each load
+  // instruction reads one column's contiguous KiB (two 16-byte loads of 8
+  // consecutive values per lane touched every cache line twice).
+  static_assert(!XS || (CT * 128 == 256 && !RMSN), "16-column chunks: 256 values per column");
+  constexpr int XCW = XS ? (NC + XWMIN - 1) / XWMIN : 1;  // columns per wave at most
+  auto f16_ld = [&](int j, int rel0, u4 &pc) {
+    const int c = wk + j * (NTHR >> 6);
+    const int kr = 4 * lane, t = kr >> 7;
+    const int64_t k = (int64_t)(kt0 + rel0 + t) * 128 + (kr & 127);
+    const bool ok = c < NC && c < a.ncols && rel0 + t < nkt && k < a.cols;
+    const uint32_t o = ok ? (uint32_t)(((int64_t)c * a.ldx + k) * 4) : 0xFFFFFFC0u;
+    pc = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0);
+  };
+  auto f16_put = [&](int j, _Float16 *dst, const u4 &pc) {
+    const int c = wk + j * (NTHR >> 6);
+    if (c >= NC) return;
+    const int kr = 4 * lane;
+    const int blk = kr >> 5, qq = (kr >> 3) & 3, h = (kr >> 2) & 1;  // block of the chunk, 16-byte piece, half
+    const float4 f = __builtin_bit_cast(float4, pc);
+    const h4 hv = {(_Float16)f[0], (_Float16)f[1], (_Float16)f[2], (_Float16)f[3]};
+    *(h4 *)(dst + xrow((size_t)blk * XC + c, qq) + 4 * h) = hv;
+  };
+
   // one bounded range per (matrix, row tile) over this segment; row tiles
   // past the matrix get an empty range
   __amdgpu_buffer_rsrc_t rq[NMAT][RT], rd[NMAT][RT];
@@ -388,14 +411,16 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   };
 
   // ---- 1. start the activations (first round) and the weight stream
-  constexpr int X0 = XS ? XR : 1;
-  const int span0 = XS ? CHV : nvec;
+  constexpr int X0 = 1;
+  const int span0 = nvec;
   XPiece xp[X0];
-  int64_t xcs[X0];
+  u4 fp[XCW];
+  if constexpr (XS) {
 #pragma unroll
-  for (int i = 0; i < X0; ++i) xcs[i] = x_col(tid + i * NTHR);
-#pragma unroll
-  for (int i = 0; i < X0; ++i) x_ld(tid + i * NTHR, 0, span0, xcs[i], xp[i]);
+    for (int j = 0; j < XCW; ++j) f16_ld(j, 0, fp[j]);
+  } else {
+    x_ld(tid, 0, span0, x_col(tid), xp[0]);
+  }
 #pragma unroll
   for (int p = 0; p < PF; ++p) load(p, p);
 
@@ -419,8 +444,12 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
   static_assert(NWL <= 63, "wait count");
   constexpr int WAIT_ALL = 0x0F70;                // vmcnt(0), other counters untouched
   constexpr int WAIT_X0 = NMAT == 1 ? WAIT_ALL : (WAIT_ALL | (NWL & 15) | ((NWL >> 4) << 14));
+  if constexpr (XS) {
 #pragma unroll
-  for (int i = 0; i < X0; ++i) x_put(tid + i * NTHR, span0, xs, xp[i]);
+    for (int j = 0; j < XCW; ++j) f16_put(j, xs, fp[j]);
+  } else {
+    x_put(tid, span0, xs, xp[0]);
+  }
   if constexpr (!XS) {
     __builtin_amdgcn_s_waitcnt(WAIT_X0);
     // pieces per batch (fewer registers where gate, up and gamma crowd them)
@@ -544,9 +573,9 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
     for (int k = 0; k < nkt; k += PF) {
 #pragma unroll
       for (int c0 = 0; c0 < PF; c0 += CT) {
-        XPiece np[XR];
+        u4 np[XCW];
 #pragma unroll
-        for (int i = 0; i < XR; ++i) x_ld(tid + i * NTHR, k + c0 + CT, CHV, xcs[i], np[i]);
+        for (int j = 0; j < XCW; ++j) f16_ld(j, k + c0 + CT, np[j]);
 #pragma unroll
         for (int p = c0; p < c0 + CT; ++p) {
           if (live && k + p < nkt) compute(p, k + p);
@@ -554,7 +583,7 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
         }
         _Float16 *nb = xs + ((((k + c0) / CT) + 1) & 1) * CHH;
 #pragma unroll
-        for (int i = 0; i < XR; ++i) x_put(tid + i * NTHR, CHV, nb, np[i]);
+        for (int j = 0; j < XCW; ++j) f16_put(j, nb, np[j]);
         __syncthreads();
       }
     }
