@@ -410,8 +410,16 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
       }
   };
 
-  // ---- 1. start the activations (first round) and the weight stream
-  constexpr int X0 = 1;
+  // ---- 1. start the activations (first round) and the weight stream.
+  // Batches of 4 to 7 columns stage several pieces per thread: the first
+  // round then takes a whole batch, so that staging costs one memory round
+  // trip less (measured, verify at 4 columns: Q8_0 5120 x 5120 11.15 ->
+  // 10.4 us, Q4_0 5120 -> 17408 17.7 -> 17.2 us; the 16-token MoE layer,
+  // whose expert entries are 4-column units, 67.0 -> 66.4 us; at 8 columns,
+  // whose segments run across workgroups with few pieces per thread, no
+  // gain).  The norm forms keep one piece (theirs carry gamma too).
+  constexpr int XB = RMSN && QT == Q8 && NMAT == 2 ? 2 : 4;  // pieces per later batch
+  constexpr int X0 = (!XS && NC >= 4 && NC < 8 && !RMSN) ? XB : 1;
   const int span0 = nvec;
   XPiece xp[X0];
   u4 fp[XCW];
@@ -419,7 +427,8 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
 #pragma unroll
     for (int j = 0; j < XCW; ++j) f16_ld(j, 0, fp[j]);
   } else {
-    x_ld(tid, 0, span0, x_col(tid), xp[0]);
+#pragma unroll
+    for (int i = 0; i < X0; ++i) x_ld(tid + i * NTHR, 0, span0, x_col(tid + i * NTHR), xp[i]);
   }
 #pragma unroll
   for (int p = 0; p < PF; ++p) load(p, p);
@@ -448,12 +457,11 @@ __device__ __forceinline__ bool dot_unit(const DotArgs &a, int g, int s, uint8_t
 #pragma unroll
     for (int j = 0; j < XCW; ++j) f16_put(j, xs, fp[j]);
   } else {
-    x_put(tid, span0, xs, xp[0]);
+#pragma unroll
+    for (int i = 0; i < X0; ++i) x_put(tid + i * NTHR, span0, xs, xp[i]);
   }
   if constexpr (!XS) {
     __builtin_amdgcn_s_waitcnt(WAIT_X0);
-    // pieces per batch (fewer registers where gate, up and gamma crowd them)
-    constexpr int XB = RMSN && QT == Q8 && NMAT == 2 ? 2 : 4;
     for (int v0 = tid + X0 * NTHR; v0 < nvec; v0 += XB * NTHR) {
       XPiece pc[XB];
 #pragma unroll
