@@ -32,9 +32,9 @@
  *     every scale multiply is f32, nothing is accumulated in f16 [ENG
  *     Correctness and portability].  Activations are f32 and keep f32 range:
  *     products of 1..8 columns (GEMV, gate/up, LM head, MoE experts) carry
- *     each activation as an exact pair of f16 values under a power of two
- *     chosen per 128 values of a column (relative error <= 2^-22, any finite
- *     f32 magnitude).  Only the 16-column prefill GEMM rounds its activation
+ *     each activation as a pair of f16 values under a power of two chosen
+ *     per 128 values of a column (any finite f32 magnitude; error <= 2^-22
+ *     of the value plus 2^-39 of the largest magnitude among its 128).  Only the 16-column prefill GEMM rounds its activation
  *     operands to f16 (round to nearest even, relative error <= 2^-11, so
  *     |x| must stay below 65504 there).  Results are bitwise reproducible
  *     run to run: all reductions (split-K included) have a fixed order per
@@ -424,7 +424,7 @@ int moe_ffn(const qg_moe *m, const float *X, int64_t ldx, int32_t ntok, float *Y
  *                 plans 8..16 only)
  *   QG_OP_GATEUP  gateup_silu and gateup_silu_rmsnorm
  *   QG_OP_LMHEAD  lmhead_argmax and lmhead_topk (ncols 1)
- * The fused FFN and the MoE layer keep their own plans.
+ * The MoE layer and the grouped prefill pass keep their own launch shapes.
  *
  * qg_tune_*: the arguments of the call they tune (same checks, same errors)
  * and flags; each candidate plan (built-in, 4, 8, 12, 16 waves, QG_PLAN_SW;
