@@ -804,6 +804,15 @@ def test_moe_many_experts(env, T):
     _moe_check(env, m, hw, T, 8, cfg=121 + T)
 
 
+@pytest.mark.parametrize("T", [7, 16])
+def test_moe_few_experts(env, T):
+    """6 experts, top-2: each router workgroup (16 logits) holds logits of
+    up to three tokens and may complete, and select, several of them."""
+    say(f"moe 6 experts T={T}")
+    m, hw = _moe_build(env, E=6, H=256, F=128, k=2, seed=140 + T)
+    _moe_check(env, m, hw, T, 2, cfg=141 + T)
+
+
 def test_moe_rmsnorm_large_input(env):
     """The MoE norm path with |x * gamma| beyond the f16 range (the expert
     units stage the un-normalised product)."""
