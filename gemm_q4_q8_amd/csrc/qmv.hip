@@ -507,10 +507,13 @@ static int dot_waves(int64_t NTu, int S) {
 template <int QT, int NC, int NMAT, int EPI, bool RMSN = false>
 static int launch_dot(const QmvCall &c, int S) {
   constexpr int QW = QT == Q4 ? 1 : 2;
-  // the LM head (a gigabyte-scale stream) keeps 8 KiB of weights in flight
-  // per wave: a streaming read at this size gains from deeper queues
+  // the LM head (a gigabyte-scale stream) keeps about 12 KiB of weights in
+  // flight per wave (at most 8 tile columns): a streaming read at this size
+  // gains from deeper queues (Q8_0 248,320 x 5120: 219.5 us with 4 tile
+  // columns, 215.5 with 6, 228.5 with 8, where the registers leave 3 waves
+  // per SIMD)
   constexpr bool HEAD = EPI == EPI_ARGMAX || EPI == EPI_TOPK;
-  constexpr int PF0 = (HEAD ? 8 : 4) / (NMAT * QW);
+  constexpr int PF0 = HEAD ? (12 / (NMAT * QW) < 8 ? 12 / (NMAT * QW) : 8) : 4 / (NMAT * QW);
   constexpr int PF = PF0 < 2 ? 2 : PF0;
   const int64_t NTu = cdiv(c.n_rows, 16);
   const int W = dot_waves(NTu, S);
