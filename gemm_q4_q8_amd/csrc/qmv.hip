@@ -239,14 +239,18 @@ struct G16Prob {
   int64_t rows, cols, ldx, ldy;
   float *part;
   uint32_t *cnt;
-  int64_t u0;  // the problem's first unit in the launch
   int NT, KT, S, G;
   int qt, acc;
 };
+// Ranges of consecutive units of one problem, in launch order (a problem
+// holds at most two: one in each round of the launch).
+constexpr int G16_RANGES = 2 * QG_BATCH_MAX;
 struct G16Args {
-  // first unit of each problem (ascending; past the last problem:
-  // INT64_MAX), read together to find a workgroup's problem
-  int64_t ustart[QG_BATCH_MAX];
+  // range j covers launch units rstart[j] .. rstart[j + 1] - 1, which are
+  // units rlu0[j] .. of problem rprob[j]; past the last range: INT64_MAX
+  int64_t rstart[G16_RANGES];
+  int64_t rlu0[G16_RANGES];
+  int32_t rprob[G16_RANGES];
   G16Prob p[QG_BATCH_MAX];
   int n;
   int64_t units;
@@ -262,14 +266,15 @@ __global__ void __launch_bounds__(W * 64) gemm16_batch_kernel(G16Args b) {
   // bytes of others)
   const int64_t u = blockIdx.x;
   if (u >= b.units) return;
-  // the problem holding unit u: its index from the first-unit numbers (one
-  // scalar load), then that one descriptor, read in place through a uniform
-  // index (a select over every descriptor made a chain of dependent scalar
-  // loads ahead of the first weight load)
-  int pi = 0;
+  // the range holding unit u from the first-unit numbers (one scalar
+  // load), then its problem's one descriptor, read in place through a
+  // uniform index (a select over every descriptor made a chain of dependent
+  // scalar loads ahead of the first weight load)
+  int ri = 0;
 #pragma unroll
-  for (int j = 1; j < QG_BATCH_MAX; ++j) pi += u >= b.ustart[j] ? 1 : 0;
-  pi = __builtin_amdgcn_readfirstlane(pi);
+  for (int j = 1; j < G16_RANGES; ++j) ri += u >= b.rstart[j] ? 1 : 0;
+  ri = __builtin_amdgcn_readfirstlane(ri);
+  const int pi = __builtin_amdgcn_readfirstlane(b.rprob[ri]);
   const G16Prob &P = b.p[pi];
   DotArgs a = {};
   a.qs0 = a.qs1 = P.qs;
@@ -289,7 +294,7 @@ __global__ void __launch_bounds__(W * 64) gemm16_batch_kernel(G16Args b) {
   a.ldy = P.ldy;
   a.part = P.part;
   a.cnt = P.cnt;
-  const int64_t lu = u - P.u0;
+  const int64_t lu = u - b.rstart[ri] + b.rlu0[ri];
   const int g = (int)(lu / P.S), s = (int)(lu % P.S);
   float bv = 0.0f;
   int32_t bi = 0;
@@ -683,39 +688,36 @@ void gemm16_batch_splits(const qg_gemm16_problem *p, int n, int *S) {
 
 // Workspace of a grouped launch: the counters of every problem's row groups
 // in the shared counter words, then each problem's segment partials.  Fills
-// `b` when given (the pointers inside `ws`).  The problems take their units
-// in the launch in order of decreasing weight bytes per unit (ties: the
-// caller's order): the hardware hands out workgroups in launch order, so the
-// longest units start first and the short ones fill in at the end (measured
-// at the prefill pass with the single-problem splits: 71.6 us with the
-// caller's order Q4_0 before Q8_0, 66.1 us largest units first).  The order
-// changes no sum.
+// `b` when given (the pointers inside `ws`, the launch order of the units).
+//
+// Launch order.  The hardware hands out workgroups in launch order, so the
+// problems take their units in order of decreasing weight bytes per unit
+// (ties: the caller's order): long units start first, short ones fill in at
+// the end (measured at the prefill pass with the single-problem splits:
+// 71.6 us with the caller's order Q4_0 before Q8_0, 66.1 us largest units
+// first).  When the units make more than one and at most two rounds of one
+// unit per CU, the first round takes the largest units and the second the
+// rest in increasing size: the units CU c receives, c and c + CUs, then pair
+// a long unit with a short one (measured at the prefill pass, 512 units on
+// 256 CUs: 55.4-58.0 us largest first throughout, 53.2-54.0 us paired).
+// The order changes no sum.
 static size_t gemm16_batch_layout(const qg_gemm16_problem *p, int n, G16Args *b, uint8_t *ws) {
   size_t off = QG_WS_SYNC_BYTES, words = 0;
   int ord[QG_BATCH_MAX], Sp[QG_BATCH_MAX];
-  int64_t ubytes[QG_BATCH_MAX];
+  int64_t ubytes[QG_BATCH_MAX], nunits[QG_BATCH_MAX];
   gemm16_batch_splits(p, n, Sp);
+  int64_t U = 0;
   for (int i = 0; i < n; ++i) {
-    const int64_t KT = cdiv(p[i].cols / 32, 4);
-    const int S = Sp[i];
-    const int64_t tb = p[i].qtype == QG_Q4_0 ? QTraits<Q4>::tile_bytes : QTraits<Q8>::tile_bytes;
-    ubytes[i] = (int64_t)G16_W * G16_RT * cdiv(KT, S) * tb;
-    ord[i] = i;
-  }
-  for (int i = 1; i < n; ++i)  // stable insertion sort, decreasing unit bytes
-    for (int j = i; j > 0 && ubytes[ord[j]] > ubytes[ord[j - 1]]; --j) {
-      const int t = ord[j];
-      ord[j] = ord[j - 1];
-      ord[j - 1] = t;
-    }
-  int64_t u0 = 0;
-  for (int k = 0; k < n; ++k) {
-    const int i = ord[k];
     const int64_t NT = cdiv(p[i].rows, 16), KT = cdiv(p[i].cols / 32, 4);
     const int S = Sp[i];
     const int64_t G = cdiv(NT, G16_W * G16_RT);
+    const int64_t tb = p[i].qtype == QG_Q4_0 ? QTraits<Q4>::tile_bytes : QTraits<Q8>::tile_bytes;
+    ubytes[i] = (int64_t)G16_W * G16_RT * cdiv(KT, S) * tb;
+    nunits[i] = G * S;
+    U += G * S;
+    ord[i] = i;
     if (b) {
-      G16Prob &q = b->p[k];
+      G16Prob &q = b->p[i];
       q.qs = (const uint8_t *)p[i].qs;
       q.d = (const uint8_t *)p[i].d;
       q.X = p[i].X;
@@ -726,7 +728,6 @@ static size_t gemm16_batch_layout(const qg_gemm16_problem *p, int n, G16Args *b,
       q.ldy = p[i].ldy;
       q.part = (float *)(ws + off);
       q.cnt = (uint32_t *)ws + words;
-      q.u0 = u0;
       q.NT = (int)NT;
       q.KT = (int)KT;
       q.S = S;
@@ -736,12 +737,44 @@ static size_t gemm16_batch_layout(const qg_gemm16_problem *p, int n, G16Args *b,
     }
     words += (size_t)G;
     if (S > 1) off += align256((size_t)S * NT * dot_part_floats(16) * 4);
-    u0 += G * S;
   }
+  for (int i = 1; i < n; ++i)  // stable insertion sort, decreasing unit bytes
+    for (int j = i; j > 0 && ubytes[ord[j]] > ubytes[ord[j - 1]]; --j) {
+      const int t = ord[j];
+      ord[j] = ord[j - 1];
+      ord[j - 1] = t;
+    }
   if (b) {
+    int nr = 0;
+    int64_t next = 0;
+    auto add = [&](int prob, int64_t lu0, int64_t cnt) {
+      if (cnt <= 0) return;
+      b->rstart[nr] = next;
+      b->rlu0[nr] = lu0;
+      b->rprob[nr] = prob;
+      ++nr;
+      next += cnt;
+    };
+    const int64_t R = device_cus();
+    if (U > R && U <= 2 * R) {
+      int64_t first[QG_BATCH_MAX], left = R;
+      for (int k = 0; k < n; ++k) {
+        const int i = ord[k];
+        first[i] = nunits[i] < left ? nunits[i] : left;
+        left -= first[i];
+        add(i, 0, first[i]);
+      }
+      for (int k = n - 1; k >= 0; --k) add(ord[k], first[ord[k]], nunits[ord[k]] - first[ord[k]]);
+    } else {
+      for (int k = 0; k < n; ++k) add(ord[k], 0, nunits[ord[k]]);
+    }
+    for (int j = nr; j < G16_RANGES; ++j) {
+      b->rstart[j] = INT64_MAX;
+      b->rlu0[j] = 0;
+      b->rprob[j] = 0;
+    }
     b->n = n;
-    b->units = u0;
-    for (int i = 0; i < QG_BATCH_MAX; ++i) b->ustart[i] = i < n ? b->p[i].u0 : INT64_MAX;
+    b->units = U;
   }
   return words > WS_SYNC_WORDS ? 0 : off;
 }
