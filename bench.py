@@ -310,6 +310,19 @@ def run_extras(B, kernels):
     t, _ = B.graph_time([lambda sd=sd: qg.requant_q8_0(qg.Q4_1, sd[0], nbk, sd[1]) for sd in pairs], 32)
     kernels["requant_q4_1_to_q8_0_17408x5120"] = kernel_entry(nbk * (20 + 34), t, None, B.last)
     del src0, pairs
+    # the same matrix as Q4_K and Q6_K super-blocks (256 values each), random
+    # bytes with finite f16 scales near 1 (and mins near 1 for Q4_K)
+    for st, name, bs, doff in ((qg.Q4_K, "q4_k", 144, 0), (qg.Q6_K, "q6_k", 210, 208)):
+        nsb = 17408 * 5120 // 256
+        src0 = torch.randint(0, 256, (nsb * bs,), dtype=torch.uint8, device=B.dev)
+        src0.view(nsb, bs)[:, doff + 1] = 0x3C
+        if st == qg.Q4_K:
+            src0.view(nsb, bs)[:, 3] = 0x3C
+        pairs = [(src0 if i == 0 else src0.clone(), torch.empty(nsb * 8 * 34, dtype=torch.uint8, device=B.dev))
+                 for i in range(8)]
+        t, _ = B.graph_time([lambda sd=sd: qg.requant_q8_0(st, sd[0], nsb, sd[1]) for sd in pairs], 32)
+        kernels[f"requant_{name}_to_q8_0_17408x5120"] = kernel_entry(nsb * (bs + 8 * 34), t, None, B.last)
+        del src0, pairs
     log("  requant done")
 
     # MoE FFN, 256 experts (8 active) + shared, hidden 2048, ffn 512
