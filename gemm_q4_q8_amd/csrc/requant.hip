@@ -147,14 +147,17 @@ __device__ __forceinline__ void kquant_values(const In *w, int r, float (&v)[32]
     const In *ql = w + 32 * n + 16 * (k & 1);
     const In *qh = w + 64 + 16 * n;
     const int lsh = k >= 2 ? 4 : 0, hsh = 2 * k;
+    // four values per 32-bit word, one byte each (low 4 bits from ql, the
+    // top 2 from qh), then byte conversions; ds * (w - 32) as the fused ds *
+    // w - 32 ds (32 ds is exact), one rounding of the same exact value
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t a = ql[i], b = qh[i];
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t a = (uint32_t)ql[2 * i] | ((uint32_t)ql[2 * i + 1] << 16);
+      const uint32_t b = (uint32_t)qh[2 * i] | ((uint32_t)qh[2 * i + 1] << 16);
+      const uint32_t q4 = ((a >> lsh) & 0x0F0F0F0Fu) | (((b >> hsh) & 0x03030303u) << 4);
+      const float ds = i < 4 ? ds0 : ds1, m32 = -32.0f * ds;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int q = (int)(((a >> (8 * e + lsh)) & 15u) | (((b >> (8 * e + hsh)) & 3u) << 4)) - 32;
-        v[2 * i + e] = (i < 8 ? ds0 : ds1) * (float)q;
-      }
+      for (int e = 0; e < 4; ++e) v[4 * i + e] = __builtin_fmaf(ds, (float)((q4 >> (8 * e)) & 0xFFu), m32);
     }
   } else {
     // 6-bit scale and min of sub-block r from the 12 bytes at words 2..7:
@@ -177,16 +180,17 @@ __device__ __forceinline__ void kquant_values(const In *w, int r, float (&v)[32]
     constexpr int QS = SRC == SRC_Q4_K ? 8 : 24;  // first word of the nibbles
     const In *qs = w + QS + 16 * (r >> 1);
     const int sh = 4 * (r & 1);
+    // four values per 32-bit word, one byte each, then byte conversions
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t a = qs[i];
-      const uint32_t hb = SRC == SRC_Q5_K ? (uint32_t)w[8 + i] : 0u;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        uint32_t q = (a >> (8 * e + sh)) & 15u;
-        if (SRC == SRC_Q5_K) q |= ((hb >> (8 * e + r)) & 1u) << 4;
-        v[2 * i + e] = __builtin_fmaf(d1, (float)q, -m1);
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t a = (uint32_t)qs[2 * i] | ((uint32_t)qs[2 * i + 1] << 16);
+      uint32_t q4 = (a >> sh) & 0x0F0F0F0Fu;
+      if (SRC == SRC_Q5_K) {
+        const uint32_t hb = (uint32_t)w[8 + 2 * i] | ((uint32_t)w[8 + 2 * i + 1] << 16);
+        q4 |= ((hb >> r) & 0x01010101u) << 4;
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * i + e] = __builtin_fmaf(d1, (float)((q4 >> (8 * e)) & 0xFFu), -m1);
     }
   }
 }
