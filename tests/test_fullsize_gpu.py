@@ -10,6 +10,8 @@ times (the launch plan depends on the shape and the column count only).
 * LM head Q8_0 5120 -> 248,320 with argmax (and a 65,536-row draft prefix);
 * MoE FFN, 256 experts of 2048 -> 512 -> 2048 (top-8) + shared expert,
   1 and 16 tokens.
+* load-time requantisation to Q8_0 of a 17408 x 5120 matrix held as Q4_1
+  blocks and as Q4_K and Q6_K super-blocks (every output byte).
 
 Every output element is checked against the f64 oracle (these sizes run in
 seconds on the host); indices bit-exact where the oracle certifies them.
@@ -236,3 +238,30 @@ def test_moe_full_layer(env, moe_full, T):
     n_ord = check_routing(tidx.cpu().numpy(), tw.cpu().numpy(), res, k, H)
     say(f"  routing: {T} tokens, order certified for {n_ord}")
     assert_tol(host(Y).T, res["y"], res["tol"], f"moe T={T}")
+
+
+@pytest.mark.parametrize("src_type", [3, 12, 14])
+def test_requant_full_matrix(env, src_type):
+    """A 17408 x 5120 matrix (89,128,960 values) of Q4_1 blocks or Q4_K / Q6_K
+    super-blocks requantised to Q8_0 as the bench times it (one call over all
+    blocks), drawn by the bench's recipe: uniformly random bytes with each f16
+    scale's high byte set to 0x3C (scales near 1; Q4_1 offsets near -1, Q4_K
+    mins near 1).  Every one of the 2,785,280 output blocks equal, byte for
+    byte, to the oracle's."""
+    torch, qg, dev = env
+    from oracle import requant as rq
+    bs, nv = rq.SRC_BLOCK_BYTES[src_type], rq.SRC_BLOCK_VALUES[src_type]
+    nb = 17408 * 5120 // nv
+    raw = np.random.default_rng(90 + src_type).integers(0, 256, (nb, bs), dtype=np.uint8)
+    d_off = 208 if src_type == rq.Q6_K else 0
+    raw[:, d_off + 1] = 0x3C
+    if src_type == rq.Q4_1:
+        raw[:, 3] = 0xBC
+    elif src_type == rq.Q4_K:
+        raw[:, 3] = 0x3C
+    say(f"requant full matrix: type {src_type}, {nb} source blocks")
+    got = qg.requant_q8_0(src_type, up(env, raw.reshape(-1)), nb).cpu().numpy().reshape(-1, 34)
+    want = rq.requant_q8_0(src_type, raw)
+    assert got.shape == want.shape
+    bad = np.flatnonzero(np.any(got != want, axis=1))
+    assert bad.size == 0, (bad.size, bad[:5], got[bad[:1]], want[bad[:1]])
