@@ -2,8 +2,8 @@
 times (the launch plan depends on the shape and the column count only).
 
 * decode FFN layer, batch 1: gate/up Q4_0 5120 -> 2 x 17408 with SiLU, then
-  down Q4_0 17408 -> 5120 accumulated into the residual, end to end, as two
-  calls and as the fused single launch;
+  down Q4_0 17408 -> 5120 accumulated into the residual, end to end; the
+  gate/up with the RMSNorm of x folded in, and after the stand-alone norm;
 * speculative-verify GEMVs, 4 and 8 columns: Q8_0 5120 x 5120, Q4_0
   5120 -> 17408;
 * 16-column prefill GEMMs, Q4_0 and Q8_0, 5120 -> 17408 and 17408 -> 5120;
@@ -54,6 +54,28 @@ def test_decode_ffn_layer(env):
     y, _ = ops.gemv(Q4, draw, h, y_in=y_in)
     ty = ops.down_tol(Q4, draw, h, th) + 2 * ops.U32 * np.abs(y)
     assert_tol(host(Y).T, y, ty, "y += Wd h")
+
+
+def test_decode_gateup_rmsnorm(env):
+    """gate/up Q4_0 5120 -> 2 x 17408 of RMSNorm(x) at batch 1, as the bench
+    times it (gamma uniform in [0.5, 1.5], eps 1e-6): the folded call and the
+    stand-alone norm followed by gate/up, both against the oracle (the norm
+    in f64, then the products)."""
+    torch, qg, dev = env
+    N, K = 17408, 5120
+    say(f"decode gate/up with RMSNorm {K}->2x{N}, batch 1")
+    graw, G = matrix(env, Q4, N, K, 21)
+    uraw, U = matrix(env, Q4, N, K, 22)
+    x = synth.gen_x(K, 1, cfg_id=synth.CFG_FFN)
+    gam = synth.rng(3, K).uniform(0.5, 1.5, K).astype(np.float32)
+    n = ops.rmsnorm(x.astype(np.float64), gam.astype(np.float64), 1e-6)
+    h, th, _, _ = ops.gateup_silu(Q4, graw, uraw, n)
+    gd = up(env, gam)
+    H = qg.gateup_silu_rmsnorm(G, U, up(env, x.T), gd, 1e-6)
+    H2 = qg.gateup_silu(G, U, qg.rmsnorm(up(env, x.T), gd, 1e-6))
+    torch.cuda.synchronize()
+    assert_tol(host(H).T, h, th, "h = silu(Wg n) * (Wu n), norm folded")
+    assert_tol(host(H2).T, h, th, "h after the stand-alone norm")
 
 
 @pytest.mark.parametrize("qtype,N,K", [(Q8, 5120, 5120), (Q4, 17408, 5120)])
