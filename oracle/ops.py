@@ -249,6 +249,26 @@ def routing_certified(logits: np.ndarray, la: np.ndarray, top_k: int, hidden: in
                      for t in range(logits.shape[1])])
 
 
+def moe_router(x: np.ndarray, router: np.ndarray, norm_w: Optional[np.ndarray] = None,
+               norm_eps: float = 0.0):
+    """The input the router and the experts read (x [H, T], or RMSNorm(x)
+    with weights norm_w), the router's logits [E, T] and their rounding-error
+    scale, as moe_ffn takes them."""
+    x = np.asarray(x, dtype=np.float64)
+    if x.ndim == 1:
+        x = x[:, None]
+    H = x.shape[0]
+    if norm_w is not None:
+        x = rmsnorm(x, norm_w, norm_eps)
+    logits, la = router_logits(x, router)       # [E, T]
+    if norm_w is not None:
+        # the norm's 1 / rms in f32 (sum of H squares, square root, division)
+        # scales every logit of a token: relative error (H + 8) u32 more
+        gam = (H + 2) * U32 / (1 - (H + 2) * U32)
+        la = la + (H + 8) * U32 / gam * np.abs(logits)
+    return x, logits, la
+
+
 def moe_ffn(x: np.ndarray, router: np.ndarray, qtype: int,
             gate_raw: np.ndarray, up_raw: np.ndarray, down_raw: np.ndarray,
             top_k: int, normalize: bool = True,
@@ -264,18 +284,9 @@ def moe_ffn(x: np.ndarray, router: np.ndarray, qtype: int,
 
     Returns dict with y [H, T], tol [H, T], idx [T, k], p [T, k],
     logits [E, T], logit_a [E, T]."""
-    x = np.asarray(x, dtype=np.float64)
-    if x.ndim == 1:
-        x = x[:, None]
+    x, logits, la = moe_router(x, router, norm_w, norm_eps)
     H, T = x.shape
-    if norm_w is not None:
-        x = rmsnorm(x, norm_w, norm_eps)
-    logits, la = router_logits(x, router)       # [E, T]
     gam = (H + 2) * U32 / (1 - (H + 2) * U32)
-    if norm_w is not None:
-        # the norm's 1 / rms in f32 (sum of H squares, square root, division)
-        # scales every logit of a token: relative error (H + 8) u32 more
-        la = la + (H + 8) * U32 / gam * np.abs(logits)
     y = np.zeros((H, T)) if y_in is None else np.asarray(y_in, dtype=np.float64).reshape(H, T).copy()
     tol = np.full((H, T), ABS_TOL)
     idx = np.zeros((T, top_k), dtype=np.int64)
@@ -326,5 +337,5 @@ def gamma(k: int) -> float:
 __all__ = [
     "gemv", "tol_dot", "silu", "gateup_silu", "down_tol", "argmax_first",
     "argmax_certified", "topk_lowest_index", "softmax", "topk_certified",
-    "router_logits", "routing_certified", "moe_ffn", "moe_routing_certified", "gamma",
+    "router_logits", "routing_certified", "moe_router", "moe_ffn", "moe_routing_certified", "gamma",
 ]

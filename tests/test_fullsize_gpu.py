@@ -9,7 +9,7 @@ times (the launch plan depends on the shape and the column count only).
 * 16-column prefill GEMMs, Q4_0 and Q8_0, 5120 -> 17408 and 17408 -> 5120;
 * LM head Q8_0 5120 -> 248,320 with argmax (and a 65,536-row draft prefix);
 * MoE FFN, 256 experts of 2048 -> 512 -> 2048 (top-8) + shared expert,
-  1 and 16 tokens.
+  1 and 16 tokens, plain and with the RMSNorm of x folded in.
 * load-time requantisation to Q8_0 of a 17408 x 5120 matrix held as Q4_1
   blocks and as Q4_K and Q6_K super-blocks (every output byte).
 
@@ -260,6 +260,44 @@ def test_moe_full_layer(env, moe_full, T):
     n_ord = check_routing(tidx.cpu().numpy(), tw.cpu().numpy(), res, k, H)
     say(f"  routing: {T} tokens, order certified for {n_ord}")
     assert_tol(host(Y).T, res["y"], res["tol"], f"moe T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_moe_full_layer_rmsnorm(env, moe_full, T):
+    """The layer with the RMSNorm of x folded in ahead of router and experts,
+    as the bench times it (gamma uniform in [0.5, 1.5], eps 1e-6; the
+    residual not normalised): routing and output against the oracle, whose
+    norm is in f64."""
+    torch, qg, dev = env
+    m, (gate, upw, down, router, sh) = moe_full
+    H, k = m.hidden, m.top_k
+    say(f"MoE with RMSNorm, 256 experts top-8 + shared, T={T}")
+    gam = synth.rng(63, H).uniform(0.5, 1.5, H).astype(np.float32)
+    y_in = synth.rng(synth.CFG_MOE, 90).standard_normal((H, T)).astype(np.float32)
+    # the bench's tokens first, then later seeds until the oracle certifies
+    # every token's selected set
+    for c in range(0, 64 * T, T):
+        X = synth.gen_x(H, T, cfg_id=synth.CFG_MOE, col0=c)
+        _, lg, la = ops.moe_router(X, router, gam.astype(np.float64), 1e-6)
+        if np.all(ops.routing_certified(lg, la, k, H)):
+            break
+    else:
+        pytest.fail("no certified routing")
+    say(f"  tokens from column {c}")
+    res = ops.moe_ffn(X, router, Q4, gate, upw, down, top_k=k, sh_gate=sh[0], sh_up=sh[1],
+                      sh_down=sh[2], y_in=y_in, norm_w=gam.astype(np.float64), norm_eps=1e-6)
+    Y = up(env, y_in.T)
+    tidx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    m.norm_weight, m.norm_eps = up(env, gam), 1e-6
+    try:
+        qg.moe_ffn(m, up(env, X.T), Y, tidx, tw)
+        torch.cuda.synchronize()
+    finally:
+        m.norm_weight = None
+    n_ord = check_routing(tidx.cpu().numpy(), tw.cpu().numpy(), res, k, H)
+    say(f"  routing: {T} tokens, order certified for {n_ord}")
+    assert_tol(host(Y).T, res["y"], res["tol"], f"moe with norm T={T}")
 
 
 @pytest.mark.parametrize("src_type", [3, 12, 14])
