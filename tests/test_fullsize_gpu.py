@@ -266,8 +266,8 @@ def test_moe_full_layer(env, moe_full, T):
 def test_moe_full_layer_rmsnorm(env, moe_full, T):
     """The layer with the RMSNorm of x folded in ahead of router and experts,
     as the bench times it (gamma uniform in [0.5, 1.5], eps 1e-6; the
-    residual not normalised): routing and output against the oracle, whose
-    norm is in f64."""
+    residual not normalised), and the stand-alone norm followed by the plain
+    layer: routing and output against the oracle, whose norm is in f64."""
     torch, qg, dev = env
     m, (gate, upw, down, router, sh) = moe_full
     H, k = m.hidden, m.top_k
@@ -298,6 +298,12 @@ def test_moe_full_layer_rmsnorm(env, moe_full, T):
     n_ord = check_routing(tidx.cpu().numpy(), tw.cpu().numpy(), res, k, H)
     say(f"  routing: {T} tokens, order certified for {n_ord}")
     assert_tol(host(Y).T, res["y"], res["tol"], f"moe with norm T={T}")
+    # the stand-alone norm, then the plain layer
+    Y2 = up(env, y_in.T)
+    qg.moe_ffn(m, qg.rmsnorm(up(env, X.T), up(env, gam), 1e-6), Y2, tidx, tw)
+    torch.cuda.synchronize()
+    check_routing(tidx.cpu().numpy(), tw.cpu().numpy(), res, k, H)
+    assert_tol(host(Y2).T, res["y"], res["tol"], f"rmsnorm then moe T={T}")
 
 
 @pytest.mark.parametrize("src_type", [3, 12, 14])
